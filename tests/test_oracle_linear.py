@@ -1,0 +1,219 @@
+"""Pins of the oracle's W4A16 linear, grouped linear and scale-only merge.
+
+Linear: against numpy binary64 matmul on the exactly dequantized weights; one-hot
+inputs (pin the nibble order and scale indexing); W = 0 and B = 0 special cases;
+an all-ones weight (y = sum x).  Grouped: a single expert equals the linear,
+permuting tokens permutes rows, and every row equals numpy on its expert.
+Merge: identity at delta 0, one grid step up, exact-rational brute force with
+constructed ties, PyTorch casts on non-tie values, code plane byte-identical.
+"""
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mxfp4_bit_weight_amd import workloads as W
+from tests import exact as X
+
+
+def _f64(bits):
+    return W.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+@pytest.mark.parametrize("fmt", [O.NVFP4, O.MXFP4])
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_linear_vs_numpy(fmt, m):
+    w, x, a, b = W.linear_inputs(11, 96, 256, m)
+    codes, scales, st = O.quantize(fmt, w)
+    deq = O.dequantize(fmt, codes, scales, st, "f64")
+    want = _f64(x) @ deq.T + (_f64(x) @ _f64(a).T) @ _f64(b).T
+    got = O.linear(fmt, x, codes, scales, st, a, b)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    base = O.linear(fmt, x, codes, scales, st)
+    assert np.allclose(base, _f64(x) @ deq.T, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def test_linear_one_hot_pins_layout():
+    w, _, _, _ = W.linear_inputs(3, 16, 64, 1)
+    for fmt in (O.NVFP4, O.MXFP4):
+        codes, scales, st = O.quantize(fmt, w)
+        q = X.unpack(codes)
+        blk = O.BLOCK[fmt]
+        for kk in [0, 1, 15, 16, 17, 31, 32, 63]:
+            x = np.zeros((1, 64), np.uint16)
+            x[0, kk] = 0x3F80                                   # 1.0
+            y = O.linear(fmt, x, codes, scales, st)[0]
+            for n in range(16):
+                c = int(q[n, kk])
+                mag = X.E2M1_MAGS[c & 7] * (-1 if c & 8 else 1)
+                s = int(scales[n, kk // blk])
+                sv = X.E4M3_MAGS[s] * Fraction(float(st)) if fmt == O.NVFP4 else Fraction(2) ** (s - 127)
+                assert Fraction(y[n]) == mag * sv
+
+
+def test_linear_special_cases():
+    _, x, a, b = W.linear_inputs(4, 32, 128, 2)
+    zero_codes = np.zeros((32, 64), np.uint8)
+    scales = np.full((32, 8), 0x38, np.uint8)                   # E4M3 1.0
+    y = O.linear(O.NVFP4, x, zero_codes, scales, 1.0, a, b)
+    assert np.allclose(y, (_f64(x) @ _f64(a).T) @ _f64(b).T, rtol=1e-12)
+    # B = 0: base only
+    w, _, _, _ = W.linear_inputs(4, 32, 128, 2)
+    codes, sc, st = O.quantize(O.NVFP4, w)
+    y0 = O.linear(O.NVFP4, x, codes, sc, st, a, np.zeros_like(b))
+    assert np.array_equal(y0, O.linear(O.NVFP4, x, codes, sc, st))
+    # every weight 1.0: codes 0x2 in both nibbles, block scale 1.0, s_t = 1 -> y = sum(x)
+    ones = np.full((32, 64), 0x22, np.uint8)
+    y1 = O.linear(O.NVFP4, x, ones, scales, 1.0)
+    assert np.array_equal(y1, np.repeat(_f64(x).sum(axis=1, keepdims=True), 32, axis=1))
+
+
+def test_linear_sampled_matches_full():
+    w, x, a, b = W.linear_inputs(5, 64, 256, 4)
+    codes, scales, st = O.quantize(O.NVFP4, w)
+    full = O.linear(O.NVFP4, x, codes, scales, st, a, b)
+    rows = np.array([0, 3, 1, 2, 3])
+    cols = np.array([0, 63, 7, 31, 5])
+    s = O.linear_sampled(O.NVFP4, x, codes, scales, st, rows, cols, a, b)
+    assert np.array_equal(s, full[rows, cols])
+
+
+def _moe_case(seed, experts=6, n=32, k=64, tokens=10, topk=2):
+    row_index, offsets = W.moe_routing(seed, tokens=tokens, experts=experts, topk=topk)
+    x = W.normal_bf16(seed, W.TID_X, (tokens, k), 1.0)
+    wts = W.moe_expert_weights(seed, experts, n, k)
+    q = [O.quantize(O.NVFP4, wts[e]) for e in range(experts)]
+    codes = np.stack([c for c, _, _ in q])
+    scales = np.stack([s for _, s, _ in q])
+    ts = np.array([t for _, _, t in q], np.float32)
+    return x, row_index, offsets, codes, scales, ts
+
+
+def test_grouped_matches_numpy_per_expert():
+    x, ri, off, codes, scales, ts = _moe_case(1)
+    y = O.grouped_linear(O.NVFP4, x, ri, off, codes, scales, ts)
+    for e in range(codes.shape[0]):
+        deq = O.dequantize(O.NVFP4, codes[e], scales[e], ts[e], "f64")
+        rows = slice(off[e], off[e + 1])
+        want = _f64(x)[ri[rows]] @ deq.T
+        assert np.allclose(y[rows], want, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_single_expert_is_linear_and_permutation():
+    x, ri, off, codes, scales, ts = _moe_case(2, experts=1, topk=1)
+    y = O.grouped_linear(O.NVFP4, x, ri, off, codes, scales, ts)
+    lin = O.linear(O.NVFP4, x[ri], codes[0], scales[0], ts[0])
+    assert np.array_equal(y, lin)
+    perm = np.random.default_rng(0).permutation(ri.size)
+    yp = O.grouped_linear(O.NVFP4, x, ri[perm], off, codes, scales, ts)
+    assert np.array_equal(yp, y[perm])
+
+
+def test_grouped_empty_experts():
+    x, ri, off, codes, scales, ts = _moe_case(3, experts=40, topk=1, tokens=8)
+    assert (np.diff(off) == 0).any()
+    y = O.grouped_linear(O.NVFP4, x, ri, off, codes, scales, ts)
+    assert y.shape == (8, 32)
+
+
+# ---- merge -----------------------------------------------------------------
+
+E8M0_MAGS = [Fraction(2) ** (c - 127) for c in range(255)]
+
+
+def _merge_exact(fmt, code, delta):
+    base = X.E4M3_MAGS[code] if fmt == O.NVFP4 else E8M0_MAGS[code]
+    v = base + Fraction(float(np.float32(delta)))
+    if v <= 0:
+        return 0
+    return X.nearest_even(v, X.E4M3_MAGS if fmt == O.NVFP4 else E8M0_MAGS)
+
+
+def test_merge_identity_and_one_step():
+    for c in range(0x7F):
+        assert O.merge_scale(O.NVFP4, c, 0.0) == c
+        if c < 0x7E:
+            step = float(X.E4M3_MAGS[c + 1] - X.E4M3_MAGS[c])
+            assert O.merge_scale(O.NVFP4, c, step) == c + 1
+    for c in range(255):
+        assert O.merge_scale(O.MXFP4, c, 0.0) == c
+    for c in range(0, 200):
+        assert O.merge_scale(O.MXFP4, c, float(2.0 ** (c - 127))) == c + 1
+
+
+def test_merge_vs_exact_with_ties():
+    rng = random.Random(5)
+    for _ in range(4000):
+        fmt = rng.choice([O.NVFP4, O.MXFP4])
+        if fmt == O.NVFP4:
+            c = rng.randrange(0, 0x7F)
+            base = X.E4M3_MAGS[c]
+            if rng.random() < 0.3 and c < 0x7D:      # land exactly on a midpoint
+                j = rng.randrange(0, 0x7E)
+                delta = (X.E4M3_MAGS[j] + X.E4M3_MAGS[j + 1]) / 2 - base
+            else:
+                delta = Fraction(rng.gauss(0, 0.05) * float(base if base else 1))
+        else:
+            c = rng.randrange(60, 200)
+            base = E8M0_MAGS[c]
+            if rng.random() < 0.3:
+                j = rng.randrange(60, 200)
+                delta = Fraction(3, 2) * E8M0_MAGS[j] - base
+            else:
+                delta = Fraction(rng.gauss(0, 0.5) * float(base))
+        d32 = np.float32(float(delta))
+        assert O.merge_scale(fmt, c, float(d32)) == _merge_exact(fmt, c, d32)
+
+
+def test_merge_tiny_delta_next_to_midpoint():
+    # a delta far below the scale's precision still decides an exact tie
+    c = 0x38                                   # E4M3 1.0; midpoint to 1.125 is 1.0625
+    tie = np.float32(0.0625)
+    assert O.merge_scale(O.NVFP4, c, float(tie)) == 0x38            # tie -> even code 0x38
+    assert O.merge_scale(O.MXFP4, 127, 0.5) == 128                  # 1.5: tie -> even code 128
+    assert O.merge_scale(O.MXFP4, 127, float(np.nextafter(np.float32(0.5), np.float32(0)))) == 127
+
+
+def test_merge_matches_torch_cast_off_ties():
+    rng = np.random.default_rng(0)
+    codes = rng.integers(0, 0x7F, 5000)
+    dec = np.array([float(X.E4M3_MAGS[c]) for c in codes])
+    # targets representable in binary32, deltas chosen so dec + delta hits them exactly
+    v32 = (dec * (1 + 0.05 * rng.standard_normal(5000))).astype(np.float32)
+    deltas = (v32.astype(np.float64) - dec).astype(np.float32)
+    v = dec + deltas.astype(np.float64)
+    exact32 = v == v32.astype(np.float64)
+    ref = torch.from_numpy(np.clip(v, 0, 448).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([O.merge_scale(O.NVFP4, int(c), float(d)) for c, d in zip(codes, deltas)])
+    assert exact32.mean() > 0.9
+    assert np.array_equal(got[exact32], ref[exact32])
+    # E8M0: PyTorch rounds ties up; away from ties it is nearest in the linear domain
+    ec = rng.integers(100, 150, 2000)
+    ed = (rng.standard_normal(2000) * 0.5 * np.exp2(ec - 127.0)).astype(np.float32)
+    ev = np.exp2(ec - 127.0) + ed.astype(np.float64)
+    pos = ev > 0
+    tref = torch.from_numpy(ev[pos].astype(np.float32)).to(torch.float8_e8m0fnu).view(torch.uint8).numpy()
+    tgot = np.array([O.merge_scale(O.MXFP4, int(c), float(d)) for c, d in zip(ec[pos], ed[pos])])
+    assert np.array_equal(tgot, tref)
+
+
+def test_merge_copies_codes_verbatim():
+    w = W.outlier_weights(8, 0, (64, 256))
+    codes, scales, st = O.quantize(O.NVFP4, w)
+    z = W.merge_noise(8, scales.size)
+    dec = np.array([O.e4m3_decode(s) for s in scales.reshape(-1)])
+    deltas = (0.05 * dec * z).astype(np.float32)
+    new_scales, new_codes = O.merge_scales(O.NVFP4, scales, deltas, codes)
+    assert new_codes.tobytes() == codes.tobytes()
+    assert new_scales.shape == scales.shape
+    assert (new_scales != scales).mean() > 0.1
+    # the merged tensor decodes to what a scale-only forward uses: codes * new scales
+    d_new = O.dequantize(O.NVFP4, codes, new_scales.reshape(scales.shape), st, "f64")
+    q = X.unpack(codes)
+    mags = np.array([float(m) for m in X.E2M1_MAGS])
+    sgn = np.where(q & 8, -1.0, 1.0)
+    sv = np.repeat(np.array([O.e4m3_decode(s) for s in new_scales.reshape(-1)]).reshape(scales.shape), 16, axis=1)
+    assert np.array_equal(d_new, sgn * mags[q & 7] * sv * float(st))

@@ -1,0 +1,185 @@
+/*
+ * fp4w.h -- C ABI of libfp4w.so: block-scaled 4-bit weights (NVFP4, MXFP4) and
+ * the dequant-fused weight-only (W4A16) linear on AMD Instinct MI355X (gfx950).
+ *
+ * Sources on the pages:
+ *  - The weight format is a 4-bit E2M1 code plus a scale shared by its block, in
+ *    NVFP4 and MXFP4 (rit.work, "Scale-QLoRA: merge native 4-bit models",
+ *    paragraph on the formats).
+ *  - Weight-only quantization with a LoRA adapter in parallel to the base, as in
+ *    QLoRA; rollouts are memory-bound and served by a W4A16 kernel
+ *    (tggo.me/sberlogasci/42740, sections "Metod" and "Eksperimenty").
+ *  - Dynamic ("max") scales recomputed from the current tensors, or frozen
+ *    calibrated scales with only the codes recomputed (aikraft.ru, "Nemotron 3.5
+ *    Lightning: NVFP4 via QAD", section 03).
+ *  - Scale-only merge: trained scale bytes are written on the format's scale grid
+ *    and the codes are copied verbatim (Scale-QLoRA page, merge paragraph).
+ * The bit layouts are the OCP ones (E2M1, E4M3 "FN", E8M0); block sizes, the
+ * tensor scale and round-to-nearest-even on exact quotients are stated readings.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'ed or equivalent) unless
+ *    stated; the caller owns and allocates every buffer, including workspaces.
+ *    The library never allocates, frees or synchronizes.
+ *  - Every call enqueues its kernels on `stream` (a hipStream_t; NULL = the
+ *    default stream) and returns after host-side validation.  A negative status
+ *    means nothing was launched (FP4W_ERR_HIP: a launch itself failed).
+ *  - Arrays are row-major.  W is (n, k); codes are (n, k/2) bytes with element k
+ *    in the low nibble when k is even; NVFP4 block scales are (n, k/16) E4M3
+ *    bytes plus one fp32 tensor scale; MXFP4 block scales are (n, k/32) E8M0
+ *    bytes.  bf16 tensors are 2-byte bf16 values.
+ *  - k must be a multiple of 32; `w`, `x`, `codes`, `out` and `lora_a` must be
+ *    16-byte aligned, bf16 outputs and the NVFP4 scales of the linear calls
+ *    2-byte aligned, the linear's workspace 256-byte aligned.  n and m may be 0 (nothing is launched).
+ *  - Values the device computes from non-finite inputs are not reported through
+ *    the status: NVFP4 gives a non-finite tensor scale, MXFP4 the NaN scale 0xFF.
+ *  - Calls on different buffers are thread-safe.  Calls that share an output or
+ *    a workspace and overlap in time race.
+ */
+#ifndef FP4W_H
+#define FP4W_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* formats */
+#define FP4W_NVFP4 0   /* 16-element blocks, E4M3 block scale, fp32 tensor scale */
+#define FP4W_MXFP4 1   /* 32-element blocks, E8M0 block scale                     */
+
+/* status codes */
+#define FP4W_OK             0
+#define FP4W_ERR_ARG       (-1)  /* null pointer where one is required, negative size */
+#define FP4W_ERR_SHAPE     (-2)  /* k % 32 != 0, r outside [0, 64], too large        */
+#define FP4W_ERR_ALIGN     (-3)  /* a pointer that must be 16-byte aligned is not    */
+#define FP4W_ERR_FORMAT    (-4)  /* unknown format or flag                            */
+#define FP4W_ERR_HIP       (-5)  /* a kernel launch failed                            */
+#define FP4W_ERR_WORKSPACE (-6)  /* workspace missing or smaller than required       */
+
+/* flags */
+#define FP4W_FROZEN_SCALES 0x1u  /* fp4w_quantize: scales (and tensor scale) are inputs */
+#define FP4W_OUT_FP32      0x2u  /* fp4w_dequantize: write fp32 instead of bf16         */
+
+/* Largest LoRA rank the fused linear accepts. */
+#define FP4W_MAX_LORA_RANK 64
+
+/*
+ * fp4w_quantize -- bf16 weights W (n, k) -> codes (n, k/2) and block scales.
+ *
+ * NVFP4, dynamic ("max") scales: A = max |w| over the whole tensor; the tensor
+ *   scale s_t = fl32(A / 2688) (correctly rounded binary32 division, 2688 = 6*448)
+ *   is written to *tensor_scale (device, one float; it is also the amax scratch
+ *   word during the call); block scale sb = RNE_sat(a_b / (6 s_t)) on the E4M3
+ *   grid (0 when s_t == 0); code = sign | RNE_sat(|w| / (dec(sb) s_t)) on the
+ *   E2M1 grid, with the quotients taken exactly; a block whose scale decodes to 0
+ *   gets signed-zero codes.
+ * MXFP4: per 32-block e = clamp(floor(log2 a_b) - 2, -127, 127) (a_b == 0 gives
+ *   -127), scale byte e + 127, code = sign | RNE_sat(|w| * 2^-e); tensor_scale is
+ *   not used (may be NULL).
+ * FP4W_FROZEN_SCALES: `scales` and (NVFP4) `*tensor_scale` are read, not written;
+ *   only the codes are computed (frozen-scale training, Nemotron QAD page,
+ *   section 03).  The given scales must be valid non-negative scale codes
+ *   (E4M3 0x00..0x7E, E8M0 0x00..0xFE) and s_t finite and >= 0.
+ * RNE_sat: round to nearest, ties to the even code, saturate at the grid top.
+ * -0 encodes as 0x8.
+ */
+int fp4w_quantize(int fmt, const void *w_bf16, int64_t n, int64_t k,
+                  uint8_t *codes, uint8_t *scales, float *tensor_scale,
+                  uint32_t flags, void *stream);
+
+/*
+ * fp4w_dequantize -- codes + scales -> W (n, k): the exact value
+ * e2m1(c) * dec(sb) * s_t (NVFP4) or e2m1(c) * 2^(sb-127) (MXFP4), rounded once
+ * to nearest even to bf16 (default) or to fp32 (FP4W_OUT_FP32).  This is the
+ * fake-quant forward the training pages insert (QATFactory page, section on how
+ * training repeats the engine's arithmetic).  tensor_scale is a device pointer
+ * (NVFP4) or ignored (MXFP4).
+ */
+int fp4w_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
+                    const float *tensor_scale, int64_t n, int64_t k,
+                    void *out, uint32_t flags, void *stream);
+
+/*
+ * Workspace for fp4w_linear, in bytes, for x (m, k), W (n, k) and LoRA rank r
+ * (0 when there is no LoRA); 0 for invalid arguments.  It holds the LoRA
+ * intermediate t = x A^T (fp32), split-K partial sums and, in its first
+ * 8 KiB at fixed offsets, arrival counters.  The counters must be zero before
+ * the first call: zero-fill a new workspace once; every call returns its
+ * counters to zero when it completes, so one workspace serves calls of any
+ * shape in stream order.
+ */
+size_t fp4w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
+
+/*
+ * fp4w_linear -- y (m, n) bf16 = x (m, k) deq(W)^T + (x A^T) B^T, with fp32
+ * accumulation: the W4A16 linear with a parallel LoRA branch (Telegram post,
+ * "Metod"; QATFactory page: the product runs on 16-bit values).
+ *   x_bf16     (m, k) bf16
+ *   codes, scales, tensor_scale   a quantized W (n, k), as fp4w_quantize writes
+ *   lora_a     (r, k) bf16 or NULL;  lora_b (n, r) bf16 or NULL;  r in [0, 64]
+ *              (both NULL or r == 0: no LoRA; any LoRA scaling is folded into B)
+ *   y_bf16     (m, n) bf16, rounded once from the fp32 result
+ *   workspace  >= fp4w_linear_workspace_bytes(m, n, k, r) bytes, see above
+ * Launches: with a LoRA, first the down-projection t = x A^T (fp32); then for
+ * m <= 16 the decode-shaped kernel (HBM-bound, split over K when n is small),
+ * for m > 16 the LDS-staged bf16 MFMA GEMM.  The LoRA product is added in fp32
+ * (GEMM: t is split into two bf16 parts for the matrix cores).
+ */
+int fp4w_linear(int fmt, const void *x_bf16, int64_t m, int64_t k,
+                const uint8_t *codes, const uint8_t *scales, const float *tensor_scale,
+                int64_t n, const void *lora_a, const void *lora_b, int r,
+                void *y_bf16, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fp4w_grouped_linear -- the W4A16 linear over the experts of a mixture of
+ * experts (QATFactory page: dense and MoE models; Nemotron page: 30B-A3B base).
+ * For every expert e and every row q in [expert_offsets[e], expert_offsets[e+1]):
+ *   y[q, :] = x[row_index[q], :] deq(W_e)^T
+ *   x_bf16          (num_tokens, k) bf16
+ *   row_index       (total_rows) int32, device; token of each routed row
+ *   expert_offsets  (num_experts + 1) int32, device, non-decreasing, [0]=0,
+ *                   [num_experts] = total_rows; the routing stays on the device
+ *   codes           (num_experts, n, k/2);  scales (num_experts, n, k/blk)
+ *   tensor_scales   (num_experts) fp32, device (NVFP4) or NULL (MXFP4)
+ *   y_bf16          (total_rows, n) bf16
+ * Device-side checks: offsets are clamped to [0, total_rows] (an expert whose
+ * range is empty does nothing); a row whose row_index is outside
+ * [0, num_tokens) is written as NaN; rows no expert covers are left unchanged.
+ * There is no LoRA branch here.
+ */
+int fp4w_grouped_linear(int fmt, const void *x_bf16, int64_t num_tokens,
+                        const int32_t *row_index, const int32_t *expert_offsets,
+                        int64_t num_experts, int64_t total_rows, int64_t n, int64_t k,
+                        const uint8_t *codes, const uint8_t *scales,
+                        const float *tensor_scales, void *y_bf16, void *stream);
+
+/*
+ * fp4w_merge_scales -- scale-only merge (Scale-QLoRA page, merge paragraph):
+ * per block, v = dec(scales_in[i]) + deltas[i] exactly (deltas are fp32, in the
+ * decoded scale domain, before any tensor scale); v <= 0 gives code 0x00, else
+ * the nearest value of the format's scale grid (E4M3 or E8M0, nearest in the
+ * linear domain), ties to the even code, saturating at 448 (0x7E) or 2^127
+ * (0xFE); a NaN scale or delta gives the NaN code.  scales_out may equal
+ * scales_in.  When codes_out != codes_in and both are non-NULL, the code plane
+ * (code_bytes bytes) is copied byte for byte; with codes_out == codes_in or NULL
+ * nothing is copied.  The NVFP4 tensor scale is not touched.
+ */
+int fp4w_merge_scales(int fmt, const uint8_t *scales_in, const float *deltas,
+                      int64_t num_blocks, uint8_t *scales_out,
+                      const uint8_t *codes_in, uint8_t *codes_out, int64_t code_bytes,
+                      void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *fp4w_status_string(int status);
+
+/* Library ABI version (increments on any signature change). */
+int fp4w_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4W_H */

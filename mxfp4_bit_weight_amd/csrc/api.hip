@@ -1,0 +1,141 @@
+// api.hip -- the C ABI of libfp4w.so (declared in include/fp4w.h): host-side
+// argument validation, then the launchers.  Nothing here allocates, frees or
+// synchronizes; every kernel goes on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include "../../include/fp4w.h"
+#include "fp4w_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+
+bool valid_fmt(int fmt) { return fmt == FP4W_NVFP4 || fmt == FP4W_MXFP4; }
+
+// Largest element count the kernels index with 64-bit offsets but whose grid
+// strides stay well inside int64: 2^40 elements (a 2 TiB bf16 tensor).
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+int check_nk(int64_t n, int64_t k) {
+  if (n < 0 || k < 0) return FP4W_ERR_ARG;
+  if (k % 32 != 0) return FP4W_ERR_SHAPE;
+  if (n > 0 && k > 0 && n > kMaxElems / k) return FP4W_ERR_SHAPE;
+  return FP4W_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP4W_OK : FP4W_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fp4w_version(void) { return 2; }
+
+const char* fp4w_status_string(int status) {
+  switch (status) {
+    case FP4W_OK: return "ok";
+    case FP4W_ERR_ARG: return "invalid argument (null pointer or negative size)";
+    case FP4W_ERR_SHAPE: return "invalid shape (k % 32 != 0, rank outside [0, 64] or too large)";
+    case FP4W_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FP4W_ERR_FORMAT: return "unknown format or flag";
+    case FP4W_ERR_HIP: return "HIP kernel launch failed";
+    case FP4W_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int fp4w_quantize(int fmt, const void* w_bf16, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                  float* tensor_scale, uint32_t flags, void* stream) {
+  if (!valid_fmt(fmt) || (flags & ~FP4W_FROZEN_SCALES)) return FP4W_ERR_FORMAT;
+  int st = check_nk(n, k);
+  if (st) return st;
+  if (n * k == 0) return FP4W_OK;
+  if (!w_bf16 || !codes || !scales) return FP4W_ERR_ARG;
+  if (fmt == FP4W_NVFP4 && !tensor_scale) return FP4W_ERR_ARG;
+  if (!aligned16(w_bf16) || !aligned16(codes)) return FP4W_ERR_ALIGN;
+  if (fmt == FP4W_NVFP4 && ((reinterpret_cast<uintptr_t>(tensor_scale) & 3u) != 0)) return FP4W_ERR_ALIGN;
+  return hip_status(fp4w::launch_quantize(fmt, w_bf16, n, k, codes, scales, tensor_scale,
+                                          (flags & FP4W_FROZEN_SCALES) != 0, as_stream(stream)));
+}
+
+int fp4w_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t n,
+                    int64_t k, void* out, uint32_t flags, void* stream) {
+  if (!valid_fmt(fmt) || (flags & ~FP4W_OUT_FP32)) return FP4W_ERR_FORMAT;
+  int st = check_nk(n, k);
+  if (st) return st;
+  if (n * k == 0) return FP4W_OK;
+  if (!codes || !scales || !out) return FP4W_ERR_ARG;
+  if (fmt == FP4W_NVFP4 && !tensor_scale) return FP4W_ERR_ARG;
+  if (!aligned16(codes) || !aligned16(out)) return FP4W_ERR_ALIGN;
+  return hip_status(fp4w::launch_dequantize(fmt, codes, scales, tensor_scale, n, k, out,
+                                            (flags & FP4W_OUT_FP32) != 0, as_stream(stream)));
+}
+
+size_t fp4w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
+  if (m < 0 || n < 0 || k < 0 || r < 0 || r > FP4W_MAX_LORA_RANK) return 0;
+  return fp4w::plan_linear(m, n, k, r).bytes;
+}
+
+int fp4w_linear(int fmt, const void* x_bf16, int64_t m, int64_t k, const uint8_t* codes, const uint8_t* scales,
+                const float* tensor_scale, int64_t n, const void* lora_a, const void* lora_b, int r, void* y_bf16,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_fmt(fmt)) return FP4W_ERR_FORMAT;
+  if (m < 0 || n < 0 || k < 0 || r < 0) return FP4W_ERR_ARG;
+  int st = check_nk(n, k);
+  if (st) return st;
+  if (r > FP4W_MAX_LORA_RANK) return FP4W_ERR_SHAPE;
+  if (m > 0 && k > 0 && m > kMaxElems / k) return FP4W_ERR_SHAPE;
+  if (m == 0 || n == 0) return FP4W_OK;
+  if (!x_bf16 || !y_bf16 || (k > 0 && (!codes || !scales))) return FP4W_ERR_ARG;
+  if (fmt == FP4W_NVFP4 && !tensor_scale) return FP4W_ERR_ARG;
+  const bool lora = r > 0 && (lora_a || lora_b);
+  if (lora && (!lora_a || !lora_b)) return FP4W_ERR_ARG;
+  if (!aligned16(x_bf16) || !aligned16(codes) || !aligned2(y_bf16)) return FP4W_ERR_ALIGN;
+  if (fmt == FP4W_NVFP4 && !aligned2(scales)) return FP4W_ERR_ALIGN;
+  if (lora && (!aligned16(lora_a) || !aligned2(lora_b))) return FP4W_ERR_ALIGN;
+  const int rr = lora ? r : 0;
+  const fp4w::LinearPlan plan = fp4w::plan_linear(m, n, k, rr);
+  if (!workspace || workspace_bytes < plan.bytes) return FP4W_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP4W_ERR_ALIGN;
+  return hip_status(fp4w::launch_linear(fmt, x_bf16, m, k, codes, scales, tensor_scale, n, lora ? lora_a : nullptr,
+                                        lora ? lora_b : nullptr, rr, y_bf16, workspace, plan, as_stream(stream)));
+}
+
+int fp4w_grouped_linear(int fmt, const void* x_bf16, int64_t num_tokens, const int32_t* row_index,
+                        const int32_t* expert_offsets, int64_t num_experts, int64_t total_rows, int64_t n,
+                        int64_t k, const uint8_t* codes, const uint8_t* scales, const float* tensor_scales,
+                        void* y_bf16, void* stream) {
+  if (!valid_fmt(fmt)) return FP4W_ERR_FORMAT;
+  if (num_tokens < 0 || num_experts < 0 || total_rows < 0) return FP4W_ERR_ARG;
+  int st = check_nk(n, k);
+  if (st) return st;
+  if (num_experts > 0 && n > 0 && k > 0 && num_experts > kMaxElems / (n * k)) return FP4W_ERR_SHAPE;
+  if (num_experts == 0 || total_rows == 0 || n == 0) return FP4W_OK;
+  if (!x_bf16 || !row_index || !expert_offsets || !y_bf16 || (k > 0 && (!codes || !scales))) return FP4W_ERR_ARG;
+  if (fmt == FP4W_NVFP4 && !tensor_scales) return FP4W_ERR_ARG;
+  if (!aligned16(x_bf16) || !aligned16(codes) || !aligned2(y_bf16)) return FP4W_ERR_ALIGN;
+  if (fmt == FP4W_NVFP4 && !aligned2(scales)) return FP4W_ERR_ALIGN;
+  if (num_experts * ((n + 15) / 16) > 0x7FFFFFFF) return FP4W_ERR_SHAPE;
+  return hip_status(fp4w::launch_grouped_linear(fmt, x_bf16, num_tokens, row_index, expert_offsets, num_experts,
+                                                total_rows, n, k, codes, scales, tensor_scales, y_bf16,
+                                                as_stream(stream)));
+}
+
+int fp4w_merge_scales(int fmt, const uint8_t* scales_in, const float* deltas, int64_t num_blocks,
+                      uint8_t* scales_out, const uint8_t* codes_in, uint8_t* codes_out, int64_t code_bytes,
+                      void* stream) {
+  if (!valid_fmt(fmt)) return FP4W_ERR_FORMAT;
+  if (num_blocks < 0 || code_bytes < 0) return FP4W_ERR_ARG;
+  if (num_blocks > 0 && (!scales_in || !deltas || !scales_out)) return FP4W_ERR_ARG;
+  const bool copy = codes_in && codes_out && codes_in != codes_out && code_bytes > 0;
+  if (copy && (!aligned16(codes_in) || !aligned16(codes_out))) return FP4W_ERR_ALIGN;
+  if (num_blocks > kMaxElems || code_bytes > kMaxElems) return FP4W_ERR_SHAPE;
+  if (num_blocks == 0 && !copy) return FP4W_OK;
+  return hip_status(fp4w::launch_merge_scales(fmt, scales_in, deltas, num_blocks, scales_out, codes_in, codes_out,
+                                              code_bytes, as_stream(stream)));
+}
+
+}  // extern "C"

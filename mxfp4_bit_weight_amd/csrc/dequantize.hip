@@ -1,0 +1,189 @@
+// dequantize.hip -- codes + block scales -> bf16 or fp32 weights on gfx950.
+//
+// The decoded weight is the exact product e2m1(c) * dec(sb) * s_t (NVFP4) or
+// e2m1(c) * 2^(sb-127) (MXFP4), rounded once to the output type.  This is the
+// dequantization a fake-quant training forward inserts so that training sees the
+// engine's values (QATFactory page, section on how training repeats the target
+// engine's arithmetic).  One thread handles 32 elements (16 bytes of codes).
+//
+// NVFP4: u = e2m1 * dec(sb) has at most 6 significant bits, so it is exact in
+// fp32; u * s_t rounds once (the fp32 output).  For bf16, hi = fl32(u * s_t)
+// and lo = fma(u, s_t, -hi) is the exact remainder, and bf16_rne_from_pair
+// breaks the one case where rounding hi again would differ (hi exactly on a
+// bf16 tie).  Tensor scales below 2^-90 could make the remainder underflow; the
+// product is then formed in binary64 instead.
+// MXFP4: the scaled conversions produce e2m1 * 2^e exactly; blocks whose
+// exponent can overflow (sb >= 0xFD) or whose scale is NaN take a plain path.
+#include "fp4w_device.hpp"
+#include "fp4w_internal.hpp"
+
+namespace fp4w {
+
+__device__ __forceinline__ void nvfp4_pair(f32x2_t t, float d, float st, bool tiny, float& o0, float& o1,
+                                           uint32_t& b01, bool want_bf16) {
+  float u0 = t.x * d, u1 = t.y * d;                // exact
+  if (!want_bf16) {
+    o0 = u0 * st;
+    o1 = u1 * st;
+    return;
+  }
+  float h0, h1, l0, l1;
+  if (!tiny) {
+    h0 = u0 * st; l0 = __builtin_fmaf(u0, st, -h0);
+    h1 = u1 * st; l1 = __builtin_fmaf(u1, st, -h1);
+  } else {
+    double v0 = (double)u0 * (double)st, v1 = (double)u1 * (double)st;   // exact
+    h0 = (float)v0; l0 = (float)(v0 - (double)h0);
+    h1 = (float)v1; l1 = (float)(v1 - (double)h1);
+  }
+  b01 = bf16_rne_from_pair(h0, l0) | (bf16_rne_from_pair(h1, l1) << 16);
+}
+
+__device__ __forceinline__ uint32_t canon_nan_f32(float v) {
+  uint32_t u = __float_as_uint(v);
+  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC00000u : u;
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint4* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            const float* __restrict__ tensor_scale,
+                                                            int64_t ngroups, void* __restrict__ out) {
+  const float st = *tensor_scale;
+  const bool tiny = !(st >= 0x1p-90f);
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < ngroups; g += (int64_t)gridDim.x * 256) {
+    uint4 c = codes[g];
+    uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    float d[2] = {e4m3_to_f32(scales[2 * g]), e4m3_to_f32(scales[2 * g + 1])};
+    if (OUT_F32) {
+      uint32_t o[32];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        float dd = d[j >> 1];
+        float v[8];
+        uint32_t dummy;
+        nvfp4_pair(fp4x2_to_f32x2<0>(cw[j], 1.0f), dd, st, tiny, v[0], v[1], dummy, false);
+        nvfp4_pair(fp4x2_to_f32x2<1>(cw[j], 1.0f), dd, st, tiny, v[2], v[3], dummy, false);
+        nvfp4_pair(fp4x2_to_f32x2<2>(cw[j], 1.0f), dd, st, tiny, v[4], v[5], dummy, false);
+        nvfp4_pair(fp4x2_to_f32x2<3>(cw[j], 1.0f), dd, st, tiny, v[6], v[7], dummy, false);
+#pragma unroll
+        for (int e = 0; e < 8; e++) o[8 * j + e] = canon_nan_f32(v[e]);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(out) + 8 * g;
+#pragma unroll
+      for (int q = 0; q < 8; q++) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    } else {
+      uint32_t o[16];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        float dd = d[j >> 1];
+        float f0, f1;
+        nvfp4_pair(fp4x2_to_f32x2<0>(cw[j], 1.0f), dd, st, tiny, f0, f1, o[4 * j + 0], true);
+        nvfp4_pair(fp4x2_to_f32x2<1>(cw[j], 1.0f), dd, st, tiny, f0, f1, o[4 * j + 1], true);
+        nvfp4_pair(fp4x2_to_f32x2<2>(cw[j], 1.0f), dd, st, tiny, f0, f1, o[4 * j + 2], true);
+        nvfp4_pair(fp4x2_to_f32x2<3>(cw[j], 1.0f), dd, st, tiny, f0, f1, o[4 * j + 3], true);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(out) + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 4; q++) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    }
+  }
+}
+
+// Plain MXFP4 path: e2m1 as fp32, times 2^(sb-127) in one rounded multiply
+// (exact, or +-inf on overflow), NaN for the NaN scale.
+__device__ __forceinline__ void mx_plain8(uint32_t cw, uint32_t sb, float* v) {
+  const bool nan_scale = sb == 0xFFu;
+  const float p = e8m0_to_f32(sb);
+  f32x2_t t0 = fp4x2_to_f32x2<0>(cw, 1.0f), t1 = fp4x2_to_f32x2<1>(cw, 1.0f);
+  f32x2_t t2 = fp4x2_to_f32x2<2>(cw, 1.0f), t3 = fp4x2_to_f32x2<3>(cw, 1.0f);
+  float e[8] = {t0.x, t0.y, t1.x, t1.y, t2.x, t2.y, t3.x, t3.y};
+#pragma unroll
+  for (int i = 0; i < 8; i++) v[i] = nan_scale ? __uint_as_float(0x7FC00000u) : e[i] * p;
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint4* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            int64_t ngroups, void* __restrict__ out) {
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < ngroups; g += (int64_t)gridDim.x * 256) {
+    uint4 c = codes[g];
+    uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t sb = scales[g];
+    const bool plain = sb >= 0xFDu;
+    if (OUT_F32) {
+      uint32_t o[32];
+      if (!plain) {
+        const float s = e8m0_scale_operand(sb);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          f32x2_t a = fp4x2_to_f32x2<0>(cw[j], s), b = fp4x2_to_f32x2<1>(cw[j], s);
+          f32x2_t c2 = fp4x2_to_f32x2<2>(cw[j], s), d2 = fp4x2_to_f32x2<3>(cw[j], s);
+          o[8 * j + 0] = __float_as_uint(a.x); o[8 * j + 1] = __float_as_uint(a.y);
+          o[8 * j + 2] = __float_as_uint(b.x); o[8 * j + 3] = __float_as_uint(b.y);
+          o[8 * j + 4] = __float_as_uint(c2.x); o[8 * j + 5] = __float_as_uint(c2.y);
+          o[8 * j + 6] = __float_as_uint(d2.x); o[8 * j + 7] = __float_as_uint(d2.y);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          float v[8];
+          mx_plain8(cw[j], sb, v);
+#pragma unroll
+          for (int e = 0; e < 8; e++) o[8 * j + e] = __float_as_uint(v[e]);
+        }
+      }
+      uint4* dst = reinterpret_cast<uint4*>(out) + 8 * g;
+#pragma unroll
+      for (int q = 0; q < 8; q++) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    } else {
+      uint32_t o[16];
+      if (!plain) {
+        const float s = e8m0_scale_operand(sb);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          o[4 * j + 0] = fp4x2_to_bf16x2_scaled<0>(cw[j], s);
+          o[4 * j + 1] = fp4x2_to_bf16x2_scaled<1>(cw[j], s);
+          o[4 * j + 2] = fp4x2_to_bf16x2_scaled<2>(cw[j], s);
+          o[4 * j + 3] = fp4x2_to_bf16x2_scaled<3>(cw[j], s);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          float v[8];
+          mx_plain8(cw[j], sb, v);
+          // values are exact in bf16 (<= 2 significant bits) or +-inf / NaN
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            o[4 * j + e] = f32_to_bf16_rne(v[2 * e]) | (f32_to_bf16_rne(v[2 * e + 1]) << 16);
+        }
+      }
+      uint4* dst = reinterpret_cast<uint4*>(out) + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 4; q++) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    }
+  }
+}
+
+hipError_t launch_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                             int64_t n, int64_t k, void* out, bool out_fp32, hipStream_t stream) {
+  const int64_t ngroups = n * k / 32;
+  if (ngroups == 0) return hipSuccess;
+  int64_t g = (ngroups + 255) / 256;
+  const int grid = (int)(g > 16384 ? 16384 : g);
+  const uint4* c = reinterpret_cast<const uint4*>(codes);
+  if (fmt == FMT_NVFP4) {
+    if (out_fp32)
+      hipLaunchKernelGGL(nvfp4_dequant_kernel<true>, dim3(grid), dim3(256), 0, stream, c, scales, tensor_scale, ngroups, out);
+    else
+      hipLaunchKernelGGL(nvfp4_dequant_kernel<false>, dim3(grid), dim3(256), 0, stream, c, scales, tensor_scale, ngroups, out);
+  } else {
+    if (out_fp32)
+      hipLaunchKernelGGL(mxfp4_dequant_kernel<true>, dim3(grid), dim3(256), 0, stream, c, scales, ngroups, out);
+    else
+      hipLaunchKernelGGL(mxfp4_dequant_kernel<false>, dim3(grid), dim3(256), 0, stream, c, scales, ngroups, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp4w

@@ -1,0 +1,51 @@
+// fp4w_internal.hpp -- launchers the C ABI (api.hip) calls; one per kernel family.
+// Shapes and pointers are validated by the caller before any launcher runs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp4w {
+
+hipError_t launch_quantize(int fmt, const void* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                           float* tensor_scale, bool frozen, hipStream_t stream);
+
+hipError_t launch_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                             int64_t n, int64_t k, void* out, bool out_fp32, hipStream_t stream);
+
+hipError_t launch_merge_scales(int fmt, const uint8_t* scales_in, const float* deltas, int64_t num_blocks,
+                               uint8_t* scales_out, const uint8_t* codes_in, uint8_t* codes_out,
+                               int64_t code_bytes, hipStream_t stream);
+
+// Linear (dense).  The plan fixes the kernel shape and the workspace layout:
+//   [counters: kCounterSlots u32, fixed][t: m x r fp32][t partials][split-K partials]
+// The arrival counters sit at fixed offsets for every shape, so a counter a call
+// returns to zero is zero for the next call whatever its shape.  Slots
+// [0, kLoraSlots) serve the LoRA down-projection's m-tiles, the rest the
+// decode kernel's weight tiles; the planner only splits when the tiles fit.
+constexpr int kCounterSlots = 2048;
+constexpr int kLoraSlots = 16;
+constexpr int kTileSlots = kCounterSlots - kLoraSlots;
+
+struct LinearPlan {
+  int path;            // 0 = skinny (m <= 16), 1 = GEMM
+  int splits;          // K splits of the skinny kernel (1 = none)
+  int lora_parts;      // K slices of the LoRA down-projection (0 = no LoRA)
+  size_t off_t;        // workspace offset of t partials: [lora_parts][m][r] fp32
+  size_t off_part;     // workspace offset of split-K partials: [splits][n][m] fp32
+  size_t off_count;    // workspace offset of per-row-tile arrival counters: [n/16] u32
+  size_t bytes;        // total workspace bytes
+};
+LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r);
+
+hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uint8_t* codes,
+                         const uint8_t* scales, const float* tensor_scale, int64_t n, const void* lora_a,
+                         const void* lora_b, int r, void* y, void* workspace, const LinearPlan& plan,
+                         hipStream_t stream);
+
+hipError_t launch_grouped_linear(int fmt, const void* x, int64_t num_tokens, const int32_t* row_index,
+                                 const int32_t* expert_offsets, int64_t num_experts, int64_t total_rows,
+                                 int64_t n, int64_t k, const uint8_t* codes, const uint8_t* scales,
+                                 const float* tensor_scales, void* y, hipStream_t stream);
+
+}  // namespace fp4w

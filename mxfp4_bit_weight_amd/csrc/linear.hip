@@ -1,0 +1,514 @@
+// linear.hip -- y = x deq(W)^T + (x A^T) B^T on gfx950 (W4A16 with a parallel LoRA).
+//
+// The pages: weight-only NVFP4 with a LoRA adapter in parallel to the frozen
+// base, as in QLoRA (tggo.me/sberlogasci/42740, section "Metod"); rollouts are
+// memory-bound (same post, "Eksperimenty"); the product runs on 16-bit values
+// (QATFactory page, section on how training repeats the engine's arithmetic).
+//
+// Launches per call:
+//   1. lora_down_kernel      t = x A^T (fp32, M x r), split over K, ordered sum
+//   2. m <= 16: linear_skinny_kernel (decode-shaped, HBM-bound; skinny.hpp)
+//      m >  16: linear_gemm_kernel   (LDS-staged bf16 MFMA GEMM, dequantizing
+//                                      each weight tile once into LDS)
+// Split-K partial sums are combined by the last workgroup to arrive, in a fixed
+// order, so results do not depend on scheduling.  Its arrival counters live in
+// the caller's workspace and are returned to zero by that last workgroup.
+#include "fp4w_device.hpp"
+#include "fp4w_internal.hpp"
+#include "skinny.hpp"
+
+namespace fp4w {
+
+// ---------------------------------------------------------------------------------
+// Cross-workgroup helpers: partial sums are written and read with agent-scope
+// atomics so no workgroup sees a stale cached copy.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Returns true in every thread of the last workgroup to arrive at counter *cnt
+// out of `expected`; that workgroup also resets the counter.  Partials must have
+// been stored before the call.
+__device__ __forceinline__ bool arrive_last(uint32_t* cnt, uint32_t expected, int* flag_lds) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t old = atomicAdd(cnt, 1u);
+    bool last = old == expected - 1u;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag_lds = last ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = *flag_lds != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+// ---------------------------------------------------------------------------------
+// LoRA down-projection t = x A^T.  Workgroup (m-tile of 16 rows, K slice p);
+// its 4 waves interleave 32-wide K steps; v_mfma_f32_16x16x32_bf16 with x as A
+// (rows m) and the LoRA A rows as B (columns j), RB = ceil(r/16) column tiles.
+// ---------------------------------------------------------------------------------
+constexpr int LD_MAX_RB = 4;
+
+__global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                        const uint16_t* __restrict__ a, int r, int P,
+                                                        int steps_per_part, float* __restrict__ tp,
+                                                        float* __restrict__ t, uint32_t* __restrict__ cnt) {
+  __shared__ float red[4 * LD_MAX_RB * 4 * 64];
+  __shared__ int flag;
+  const int mt = blockIdx.x / P, p = blockIdx.x % P;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 15, g = lane >> 4;
+  const int RB = (r + 15) / 16;
+  const int64_t m = (int64_t)mt * 16 + li;
+  const int nsteps = (int)((K + 31) / 32);
+  const int s0 = p * steps_per_part, s1 = min(nsteps, s0 + steps_per_part);
+  f32x4_t acc[LD_MAX_RB];
+#pragma unroll
+  for (int b = 0; b < LD_MAX_RB; b++) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int step = s0 + wave; step < s1; step += 4) {
+    const int64_t k = (int64_t)step * 32 + 8 * g;
+    u32x4_t xa = {0u, 0u, 0u, 0u};
+    if (m < M && k < K) xa = load16(x + m * K + k);
+#pragma unroll
+    for (int b = 0; b < LD_MAX_RB; b++) {
+      if (b < RB) {
+        const int j = b * 16 + li;
+        u32x4_t av = {0u, 0u, 0u, 0u};
+        if (j < r && k < K) av = load16(a + (int64_t)j * K + k);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(av), acc[b], 0, 0, 0);
+      }
+    }
+  }
+  // reduce the 4 waves: D row = 4 g + i (m), column li (j within the tile)
+#pragma unroll
+  for (int b = 0; b < LD_MAX_RB; b++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) red[((wave * LD_MAX_RB + b) * 4 + i) * 64 + lane] = acc[b][i];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int b = 0; b < LD_MAX_RB; b++) {
+      if (b < RB) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float s = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; w++) s += red[((w * LD_MAX_RB + b) * 4 + i) * 64 + lane];
+          const int64_t mm = (int64_t)mt * 16 + 4 * g + i;
+          const int j = b * 16 + li;
+          if (mm < M && j < r) {
+            if (P == 1) t[mm * r + j] = s;
+            else store_agent(&tp[((int64_t)p * M + mm) * r + j], s);
+          }
+        }
+      }
+    }
+  }
+  if (P == 1) return;
+  if (!arrive_last(&cnt[mt], (uint32_t)P, &flag)) return;
+  for (int e = threadIdx.x; e < 16 * r; e += 256) {
+    const int64_t mm = (int64_t)mt * 16 + e / r;
+    const int j = e % r;
+    if (mm >= M) continue;
+    float s = 0.f;
+    for (int q = 0; q < P; q++) s += load_agent(&tp[((int64_t)q * M + mm) * r + j]);
+    t[mm * r + j] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Decode-shaped linear (m <= 16).
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ float lora_term(const float* __restrict__ t, const uint16_t* __restrict__ lb, int r,
+                                           int64_t m, int64_t row) {
+  float s = 0.f;
+  for (int j = 0; j < r; j++) s = __builtin_fmaf(t[m * r + j], __uint_as_float((uint32_t)lb[row * r + j] << 16), s);
+  return s;
+}
+
+template <int FMT, int MG, int U>
+__global__ __launch_bounds__(SK_THREADS) void linear_skinny_kernel(
+    const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t N,
+    const float* __restrict__ t, const uint16_t* __restrict__ lora_b, int r, uint16_t* __restrict__ y,
+    float* __restrict__ part, uint32_t* __restrict__ cnt, int S, int steps_per_split, int nsteps) {
+  __shared__ float red[SK_WAVES * 16 * 64];
+  __shared__ float fin[16 * 16];
+  __shared__ int flag;
+  const int tile = blockIdx.x / S, s = blockIdx.x % S;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4;
+  const int64_t row = (int64_t)tile * SK_TILE_N + (lane & 15);
+  const int64_t blk = (FMT == FMT_NVFP4) ? 16 : 32;
+  const uint8_t* codes_row = row < N ? codes + row * (K / 2) : nullptr;
+  const uint8_t* scales_row = row < N ? scales + row * (K / blk) : nullptr;
+  const uint16_t* xrow[MG];
+#pragma unroll
+  for (int mg = 0; mg < MG; mg++) {
+    const int m = a_operand_row<FMT>(lane, mg);
+    xrow[mg] = (m >= 0 && m < M) ? x + (int64_t)m * K : nullptr;
+  }
+  const int sb = s * steps_per_split, se = min(nsteps, sb + steps_per_split);
+  SkinnyTileResult res;
+  skinny_tile<FMT, MG, U>(codes_row, scales_row, xrow, K, sb, se, wave, g, res);
+  skinny_reduce<FMT, MG>(res, red, fin, M);
+
+  const int tid = threadIdx.x;
+  const int m = tid >> 4, nn = tid & 15;
+  const int64_t orow = (int64_t)tile * SK_TILE_N + nn;
+  const bool mine = m < M && orow < N;
+  float v = mine ? fin[m * 16 + nn] : 0.f;
+  if (S > 1) {
+    if (mine) store_agent(&part[((int64_t)s * N + orow) * M + m], v);
+    if (!arrive_last(&cnt[tile], (uint32_t)S, &flag)) return;
+    if (mine) {
+      v = 0.f;
+      for (int q = 0; q < S; q++) v += load_agent(&part[((int64_t)q * N + orow) * M + m]);
+    }
+  }
+  if (mine) {
+    const float st = (FMT == FMT_NVFP4) ? *tensor_scale : 1.0f;
+    float o = st * v;
+    if (t) o += lora_term(t, lora_b, r, m, orow);
+    y[(int64_t)m * N + orow] = (uint16_t)f32_to_bf16_rne(o);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// GEMM (m > 16): 256 x 256 output tile per workgroup, K tile 64, 4 waves in a
+// 2 x 2 grid of 128 x 128, v_mfma_f32_16x16x32_bf16.  Each K tile of x is
+// copied to LDS, each K tile of W is loaded as codes and dequantized once into
+// LDS as exact bf16 (e2m1 * dec(sb); the tensor scale is applied at the end).
+// The next tile's global loads are in flight while the current one is used.
+// ---------------------------------------------------------------------------------
+constexpr int G_BM = 256, G_BN = 256, G_BK = 64;
+constexpr int G_LDA = G_BK + 8;   // bf16 elements per LDS row (16 bytes of padding)
+
+template <int FMT>
+struct GemmStage {
+  u32x4_t xv[8];     // 8 x 16 bytes of x
+  u32x4_t cv[2];     // 2 x 16 bytes of codes (two 32-code halves)
+  uint32_t sv[2];    // their scale bytes
+};
+
+template <int FMT>
+__device__ __forceinline__ void gemm_load(GemmStage<FMT>& st, const uint16_t* __restrict__ x, int64_t M,
+                                          int64_t K, const uint8_t* __restrict__ codes,
+                                          const uint8_t* __restrict__ scales, int64_t N, int64_t m0, int64_t n0,
+                                          int64_t k0) {
+  const int tid = threadIdx.x;
+  // x: 256 rows x 64 bf16 = 2048 chunks of 16 B; thread handles rows tid/8 + 32 i, chunk tid % 8
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int64_t mr = m0 + (tid >> 3) + 32 * i;
+    const int64_t k = k0 + 8 * (tid & 7);
+    st.xv[i] = (u32x4_t){0u, 0u, 0u, 0u};
+    if (mr < M && k < K) st.xv[i] = load16(x + mr * K + k);
+  }
+  // W: 256 rows x 64 codes = 512 chunks of 32 codes; thread handles rows tid/2 and tid/2 + 128
+  const int64_t blk = (FMT == FMT_NVFP4) ? 16 : 32;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const int64_t nr = n0 + (tid >> 1) + 128 * h;
+    const int64_t k = k0 + 32 * (tid & 1);
+    st.cv[h] = (u32x4_t){0u, 0u, 0u, 0u};
+    st.sv[h] = 0u;
+    if (nr < N && k < K) {
+      st.cv[h] = load16(codes + nr * (K / 2) + k / 2);
+      if (FMT == FMT_NVFP4) st.sv[h] = *reinterpret_cast<const uint16_t*>(scales + nr * (K / blk) + k / blk);
+      else st.sv[h] = scales[nr * (K / blk) + k / blk];
+    }
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void gemm_store_lds(const GemmStage<FMT>& st, uint16_t* sa, uint16_t* sb) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int rr = (tid >> 3) + 32 * i, c = 8 * (tid & 7);
+    *reinterpret_cast<u32x4_t*>(sa + rr * G_LDA + c) = st.xv[i];
+  }
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const int rr = (tid >> 1) + 128 * h, c = 32 * (tid & 1);
+    u32x4_t o[4];
+    if (FMT == FMT_NVFP4) {
+      const float d0 = e4m3_to_f32(st.sv[h] & 0xFFu), d1 = e4m3_to_f32(st.sv[h] >> 8);
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const float d = q < 2 ? d0 : d1;
+        const uint32_t dw = st.cv[h][q];
+        f32x2_t a0 = fp4x2_to_f32x2<0>(dw, 1.0f), a1 = fp4x2_to_f32x2<1>(dw, 1.0f);
+        f32x2_t a2 = fp4x2_to_f32x2<2>(dw, 1.0f), a3 = fp4x2_to_f32x2<3>(dw, 1.0f);
+        // e2m1 * dec(sb) has at most 6 significant bits: exact in fp32 and in bf16
+        o[q].x = (__float_as_uint(a0.x * d) >> 16) | (__float_as_uint(a0.y * d) & 0xFFFF0000u);
+        o[q].y = (__float_as_uint(a1.x * d) >> 16) | (__float_as_uint(a1.y * d) & 0xFFFF0000u);
+        o[q].z = (__float_as_uint(a2.x * d) >> 16) | (__float_as_uint(a2.y * d) & 0xFFFF0000u);
+        o[q].w = (__float_as_uint(a3.x * d) >> 16) | (__float_as_uint(a3.y * d) & 0xFFFF0000u);
+      }
+    } else {
+      const float s = e8m0_scale_operand(st.sv[h]);
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const uint32_t dw = st.cv[h][q];
+        o[q].x = fp4x2_to_bf16x2_scaled<0>(dw, s);
+        o[q].y = fp4x2_to_bf16x2_scaled<1>(dw, s);
+        o[q].z = fp4x2_to_bf16x2_scaled<2>(dw, s);
+        o[q].w = fp4x2_to_bf16x2_scaled<3>(dw, s);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) *reinterpret_cast<u32x4_t*>(sb + rr * G_LDA + c + 8 * q) = o[q];
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256, 1) void linear_gemm_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t N,
+    const float* __restrict__ t, const uint16_t* __restrict__ lora_b, int r, uint16_t* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  // LDS: [A stage 0][A stage 1][B stage 0][B stage 1]
+  uint16_t* const sA0 = smem;
+  uint16_t* const sB0 = smem + 2 * G_BM * G_LDA;
+  const int tiles_n = (int)((N + G_BN - 1) / G_BN);
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int64_t m0 = (int64_t)tm * G_BM, n0 = (int64_t)tn * G_BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 15, g = lane >> 4;
+
+  f32x4_t acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int j = 0; j < 8; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (int)((K + G_BK - 1) / G_BK);
+  GemmStage<FMT> stage;
+  gemm_load<FMT>(stage, x, M, K, codes, scales, N, m0, n0, 0);
+  gemm_store_lds<FMT>(stage, sA0, sB0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt++) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gemm_load<FMT>(stage, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 1) * G_BK);
+    const uint16_t* a = sA0 + cur * (G_BM * G_LDA);
+    const uint16_t* b = sB0 + cur * (G_BN * G_LDA);
+#pragma unroll
+    for (int kk = 0; kk < G_BK / 32; kk++) {
+      bf16x8_t af[8], bfr[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        af[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(a + (wm * 128 + i * 16 + li) * G_LDA + kk * 32 + 8 * g));
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(b + (wn * 128 + j * 16 + li) * G_LDA + kk * 32 + 8 * g));
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) gemm_store_lds<FMT>(stage, sA0 + (cur ^ 1) * (G_BM * G_LDA), sB0 + (cur ^ 1) * (G_BN * G_LDA));
+    __syncthreads();
+  }
+
+  // epilogue: y = s_t * acc + LoRA, with the LoRA as extra MFMA steps over
+  // K' = [t_hi | t_lo] (t split into two bf16 parts) against [B | B].
+  const float st = (FMT == FMT_NVFP4) ? *tensor_scale : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) acc[i][j][e] *= st;
+  if (t) {
+    const int rpad = ((r + 15) / 16) * 16;
+    for (int jb = 0; jb < rpad; jb += 16) {
+      // K' slice: 32 entries = t_hi[jb..jb+16) then t_lo[jb..jb+16); lane group g
+      // covers entries 8g..8g+7 -> part (g >> 1) of LoRA index jb + 8 (g & 1) + e
+      const int jj = jb + 8 * (g & 1);
+      const bool lo_part = (g >> 1) != 0;
+      bf16x8_t tf[8], bfv[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int64_t mr = m0 + wm * 128 + i * 16 + li;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (mr < M) {
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const int j = jj + e;
+            const float tv = j < r ? t[mr * r + j] : 0.f;
+            const uint32_t hi = f32_to_bf16_rne(tv);
+            h[e] = lo_part ? f32_to_bf16_rne(tv - __uint_as_float(hi << 16)) : hi;
+          }
+          v.x = h[0] | (h[1] << 16); v.y = h[2] | (h[3] << 16);
+          v.z = h[4] | (h[5] << 16); v.w = h[6] | (h[7] << 16);
+        }
+        tf[i] = as_bf16x8(v);
+      }
+#pragma unroll
+      for (int j2 = 0; j2 < 8; j2++) {
+        const int64_t nr = n0 + wn * 128 + j2 * 16 + li;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (nr < N) {
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const int j = jj + e;
+            h[e] = j < r ? lora_b[nr * r + j] : 0u;
+          }
+          v.x = h[0] | (h[1] << 16); v.y = h[2] | (h[3] << 16);
+          v.z = h[4] | (h[5] << 16); v.w = h[6] | (h[7] << 16);
+        }
+        bfv[j2] = as_bf16x8(v);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int j2 = 0; j2 < 8; j2++) acc[i][j2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf[i], bfv[j2], acc[i][j2], 0, 0, 0);
+    }
+  }
+  // store: lane holds rows 4 g + e, column li of each 16 x 16 sub-tile
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int64_t nc = n0 + wn * 128 + j * 16 + li;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int64_t mr = m0 + wm * 128 + i * 16 + 4 * g + e;
+        if (mr < M && nc < N) y[mr * N + nc] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Planning and launch.
+// ---------------------------------------------------------------------------------
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static int lora_parts_for(int64_t m, int64_t k) {
+  const int64_t steps = (k + 31) / 32;
+  if ((m + 15) / 16 > kLoraSlots || m > 16) return 1;
+  int64_t p = steps / 8;
+  if (p < 1) p = 1;
+  if (p > 64) p = 64;
+  return (int)p;
+}
+
+static int skinny_splits_for(int64_t n, int64_t k) {
+  const int64_t tiles = (n + SK_TILE_N - 1) / SK_TILE_N;
+  const int64_t nsteps = (k + SK_STEP_K - 1) / SK_STEP_K;
+  if (tiles > kTileSlots) return 1;
+  int64_t s = (1024 + tiles - 1) / tiles;     // aim for >= 1024 workgroups
+  const int64_t max_s = nsteps / 4 > 0 ? nsteps / 4 : 1;   // keep >= 4 steps (one per wave)
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return (int)s;
+}
+
+LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
+  LinearPlan p{};
+  p.path = m <= 16 ? 0 : 1;
+  p.lora_parts = r > 0 ? lora_parts_for(m, k) : 0;
+  p.splits = p.path == 0 ? skinny_splits_for(n, k) : 1;
+  size_t off = 0;
+  p.off_count = off;
+  off += sizeof(uint32_t) * kCounterSlots;
+  p.off_t = off;
+  if (r > 0) {
+    off += align256(sizeof(float) * (size_t)m * (size_t)r);                           // t
+    if (p.lora_parts > 1) off += align256(sizeof(float) * (size_t)p.lora_parts * m * r);   // partials
+  }
+  p.off_part = off;
+  if (p.splits > 1) off += align256(sizeof(float) * (size_t)p.splits * (size_t)n * (size_t)m);
+  p.bytes = off;
+  return p;
+}
+
+template <int FMT>
+static void launch_skinny(int mg, const void* x, int64_t m, int64_t k, const uint8_t* codes, const uint8_t* scales,
+                          const float* ts, int64_t n, const float* t, const void* lb, int r, void* y, float* part,
+                          uint32_t* cnt, int S, hipStream_t stream) {
+  const int64_t tiles = (n + SK_TILE_N - 1) / SK_TILE_N;
+  const int nsteps = (int)((k + SK_STEP_K - 1) / SK_STEP_K);
+  const int sps = (nsteps + S - 1) / S;
+  const dim3 grid((unsigned)(tiles * S)), block(SK_THREADS);
+  const uint16_t* xx = reinterpret_cast<const uint16_t*>(x);
+  const uint16_t* bb = reinterpret_cast<const uint16_t*>(lb);
+  uint16_t* yy = reinterpret_cast<uint16_t*>(y);
+#define FP4W_SKINNY(MGv, Uv)                                                                                    \
+  hipLaunchKernelGGL((linear_skinny_kernel<FMT, MGv, Uv>), grid, block, 0, stream, xx, (int)m, k, codes, scales, \
+                     ts, n, t, bb, r, yy, part, cnt, S, sps, nsteps)
+  switch (mg) {
+    case 1: FP4W_SKINNY(1, 4); break;
+    case 2: FP4W_SKINNY(2, 2); break;
+    case 3: FP4W_SKINNY(3, 1); break;
+    default: FP4W_SKINNY(4, 1); break;
+  }
+#undef FP4W_SKINNY
+}
+
+hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uint8_t* codes,
+                         const uint8_t* scales, const float* tensor_scale, int64_t n, const void* lora_a,
+                         const void* lora_b, int r, void* y, void* workspace, const LinearPlan& plan,
+                         hipStream_t stream) {
+  if (m == 0 || n == 0) return hipSuccess;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  const bool has_lora = r > 0 && lora_a && lora_b;
+  float* t = has_lora ? reinterpret_cast<float*>(ws + plan.off_t) : nullptr;
+  float* tp = (has_lora && plan.lora_parts > 1)
+                  ? reinterpret_cast<float*>(ws + plan.off_t + align256(sizeof(float) * (size_t)m * r))
+                  : nullptr;
+  float* part = reinterpret_cast<float*>(ws + plan.off_part);
+  uint32_t* cnt_m = reinterpret_cast<uint32_t*>(ws + plan.off_count);
+  uint32_t* cnt_n = cnt_m + kLoraSlots;
+  if (has_lora) {
+    const int64_t nsteps = (k + 31) / 32;
+    const int P = plan.lora_parts;
+    const int spp = (int)((nsteps + P - 1) / P);
+    const int64_t mtiles = (m + 15) / 16;
+    hipLaunchKernelGGL(lora_down_kernel, dim3((unsigned)(mtiles * P)), dim3(256), 0, stream,
+                       reinterpret_cast<const uint16_t*>(x), m, k, reinterpret_cast<const uint16_t*>(lora_a), r, P,
+                       spp, tp, t, cnt_m);
+  }
+  if (plan.path == 0) {
+    if (fmt == FMT_NVFP4)
+      launch_skinny<FMT_NVFP4>((int)((m + 3) / 4), x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part,
+                               cnt_n, plan.splits, stream);
+    else
+      launch_skinny<FMT_MXFP4>(1, x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part, cnt_n,
+                               plan.splits, stream);
+  } else {
+    const int64_t tiles = ((m + G_BM - 1) / G_BM) * ((n + G_BN - 1) / G_BN);
+    const size_t lds = sizeof(uint16_t) * 2 * (G_BM + G_BN) * G_LDA;
+    const uint16_t* xx = reinterpret_cast<const uint16_t*>(x);
+    const uint16_t* bb = reinterpret_cast<const uint16_t*>(lora_b);
+    uint16_t* yy = reinterpret_cast<uint16_t*>(y);
+    static bool lds_set[2] = {false, false};
+    if (!lds_set[fmt]) {
+      hipError_t e = fmt == FMT_NVFP4
+                         ? hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_gemm_kernel<FMT_NVFP4>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
+                         : hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_gemm_kernel<FMT_MXFP4>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      lds_set[fmt] = true;
+    }
+    if (fmt == FMT_NVFP4)
+      hipLaunchKernelGGL(linear_gemm_kernel<FMT_NVFP4>, dim3((unsigned)tiles), dim3(256), lds, stream, xx, m, k,
+                         codes, scales, tensor_scale, n, t, bb, has_lora ? r : 0, yy);
+    else
+      hipLaunchKernelGGL(linear_gemm_kernel<FMT_MXFP4>, dim3((unsigned)tiles), dim3(256), lds, stream, xx, m, k,
+                         codes, scales, tensor_scale, n, t, bb, has_lora ? r : 0, yy);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp4w

@@ -1,0 +1,202 @@
+"""Thin Python binding of ``libfp4w.so`` (C ABI in ``include/fp4w.h``).
+
+Argument marshalling only: every step runs in the library's gfx950 kernels.
+PyTorch supplies device memory and the current HIP stream.  The functions carry
+the C entry points' names without the ``fp4w_`` prefix.  Importing this module
+fails loudly if the library has not been built (``__graft_entry__.build()`` or
+``python mxfp4_bit_weight_amd/build.py``).
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+NVFP4 = 0
+MXFP4 = 1
+BLOCK = {NVFP4: 16, MXFP4: 32}
+FROZEN_SCALES = 0x1
+OUT_FP32 = 0x2
+MAX_LORA_RANK = 64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4w.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
+                      "(python mxfp4_bit_weight_amd/build.py)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p, _i64, _int, _u32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32, ctypes.c_size_t
+
+
+def _sig(name, restype, *args):
+    f = getattr(_lib, name)
+    f.restype = restype
+    f.argtypes = list(args)
+    return f
+
+
+_quantize = _sig("fp4w_quantize", _int, _int, _p, _i64, _i64, _p, _p, _p, _u32, _p)
+_dequantize = _sig("fp4w_dequantize", _int, _int, _p, _p, _p, _i64, _i64, _p, _u32, _p)
+_ws_bytes = _sig("fp4w_linear_workspace_bytes", _sz, _i64, _i64, _i64, _int)
+_linear = _sig("fp4w_linear", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _int, _p, _p, _sz, _p)
+_grouped = _sig("fp4w_grouped_linear", _int, _int, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p)
+_merge = _sig("fp4w_merge_scales", _int, _int, _p, _p, _i64, _p, _p, _p, _i64, _p)
+_status = _sig("fp4w_status_string", ctypes.c_char_p, _int)
+_version = _sig("fp4w_version", _int)
+
+EXPORTED = ["fp4w_quantize", "fp4w_dequantize", "fp4w_linear_workspace_bytes", "fp4w_linear",
+            "fp4w_grouped_linear", "fp4w_merge_scales", "fp4w_status_string", "fp4w_version"]
+
+
+class Fp4wError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_status(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise Fp4wError(status, what)
+
+
+def status_string(status: int) -> str:
+    return _status(int(status)).decode()
+
+
+def version() -> int:
+    return _version()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name):
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor on the GPU")
+
+
+@dataclass
+class QWeight:
+    """A block-scaled 4-bit weight W (n, k): codes (n, k/2) uint8, scales
+    (n, k/blk) uint8, and for NVFP4 a one-element fp32 tensor scale."""
+    fmt: int
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tensor_scale: Optional[torch.Tensor]
+    n: int
+    k: int
+
+
+def empty_qweight(fmt: int, n: int, k: int, device) -> QWeight:
+    dev = torch.device(device)
+    return QWeight(fmt, torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+                   torch.empty((n, k // BLOCK[fmt]), dtype=torch.uint8, device=dev),
+                   torch.empty(1, dtype=torch.float32, device=dev) if fmt == NVFP4 else None, n, k)
+
+
+def quantize(w: torch.Tensor, fmt: int = NVFP4, out: Optional[QWeight] = None,
+             frozen: Optional[QWeight] = None) -> QWeight:
+    """fp4w_quantize.  ``frozen``: reuse its scales (and tensor scale) and compute codes only."""
+    _need(w, torch.bfloat16, "w")
+    n, k = w.shape
+    q = out if out is not None else empty_qweight(fmt, n, k, w.device)
+    flags = 0
+    if frozen is not None:
+        flags = FROZEN_SCALES
+        q.scales, q.tensor_scale = frozen.scales, frozen.tensor_scale
+    _check(_quantize(fmt, _ptr(w), n, k, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), flags,
+                     _stream(w.device)), "fp4w_quantize")
+    return q
+
+
+def dequantize(q: QWeight, dtype=torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4w_dequantize: the exact decoded values rounded once to bf16 or fp32."""
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("dtype must be bfloat16 or float32")
+    y = out if out is not None else torch.empty((q.n, q.k), dtype=dtype, device=q.codes.device)
+    _check(_dequantize(q.fmt, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.n, q.k, _ptr(y),
+                       OUT_FP32 if dtype == torch.float32 else 0, _stream(q.codes.device)), "fp4w_dequantize")
+    return y
+
+
+def linear_workspace_bytes(m: int, n: int, k: int, r: int) -> int:
+    return int(_ws_bytes(m, n, k, r))
+
+
+_workspaces = {}
+
+
+def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A zero-filled workspace per (device, current stream), grown on demand.  The
+    library returns its counters to zero after every call, so it is reused as is."""
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def linear(x: torch.Tensor, q: QWeight, lora_a: Optional[torch.Tensor] = None,
+           lora_b: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4w_linear: y = x deq(W)^T + (x A^T) B^T, bf16 in and out, fp32 accumulation."""
+    _need(x, torch.bfloat16, "x")
+    m, k = x.shape
+    if k != q.k:
+        raise ValueError(f"x has k={k}, the weight k={q.k}")
+    r = 0
+    if lora_a is not None or lora_b is not None:
+        _need(lora_a, torch.bfloat16, "lora_a")
+        _need(lora_b, torch.bfloat16, "lora_b")
+        r = lora_a.shape[0]
+        if lora_a.shape != (r, k) or lora_b.shape != (q.n, r):
+            raise ValueError("lora_a must be (r, k) and lora_b (n, r)")
+    y = out if out is not None else torch.empty((m, q.n), dtype=torch.bfloat16, device=x.device)
+    nbytes = linear_workspace_bytes(m, q.n, k, r)
+    ws = workspace if workspace is not None else workspace_for(x.device, nbytes)
+    _check(_linear(q.fmt, _ptr(x), m, k, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.n,
+                   _ptr(lora_a), _ptr(lora_b), r, _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)),
+           "fp4w_linear")
+    return y
+
+
+def grouped_linear(x: torch.Tensor, row_index: torch.Tensor, expert_offsets: torch.Tensor, fmt: int,
+                   codes: torch.Tensor, scales: torch.Tensor, tensor_scales: Optional[torch.Tensor],
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4w_grouped_linear over experts: codes (E, n, k/2), scales (E, n, k/blk)."""
+    _need(x, torch.bfloat16, "x")
+    _need(row_index, torch.int32, "row_index")
+    _need(expert_offsets, torch.int32, "expert_offsets")
+    e, n, kh = codes.shape
+    k = kh * 2
+    total = row_index.numel()
+    y = out if out is not None else torch.empty((total, n), dtype=torch.bfloat16, device=x.device)
+    _check(_grouped(fmt, _ptr(x), x.shape[0], _ptr(row_index), _ptr(expert_offsets), e, total, n, k,
+                    _ptr(codes), _ptr(scales), _ptr(tensor_scales), _ptr(y), _stream(x.device)),
+           "fp4w_grouped_linear")
+    return y
+
+
+def merge_scales(q: QWeight, deltas: torch.Tensor, in_place: bool = False) -> QWeight:
+    """fp4w_merge_scales: new scales on the format's grid; codes shared (in place)
+    or copied byte for byte into a new tensor; the tensor scale is shared."""
+    _need(deltas, torch.float32, "deltas")
+    if deltas.numel() != q.scales.numel():
+        raise ValueError("one delta per block scale")
+    if in_place:
+        _check(_merge(q.fmt, _ptr(q.scales), _ptr(deltas), q.scales.numel(), _ptr(q.scales), None, None, 0,
+                      _stream(q.codes.device)), "fp4w_merge_scales")
+        return q
+    new = QWeight(q.fmt, torch.empty_like(q.codes), torch.empty_like(q.scales), q.tensor_scale, q.n, q.k)
+    _check(_merge(q.fmt, _ptr(q.scales), _ptr(deltas), q.scales.numel(), _ptr(new.scales), _ptr(q.codes),
+                  _ptr(new.codes), q.codes.numel(), _stream(q.codes.device)), "fp4w_merge_scales")
+    return new

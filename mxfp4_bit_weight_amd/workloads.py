@@ -3,8 +3,8 @@
 This module draws random numbers and builds input structure only; it holds none
 of the 4-bit format's arithmetic.  Every tensor comes from its own stream,
 ``numpy.random.Generator(PCG64(SeedSequence([seed, tensor_id])))``, drawn in
-binary64, cast to binary32 and then rounded to nearest even to bf16 (by
-PyTorch's CPU cast).  bf16 tensors are returned as ``uint16`` bit patterns.
+binary32 and rounded to nearest even to bf16 (by PyTorch's CPU cast).  bf16
+tensors are returned as ``uint16`` bit patterns.
 
 Shapes and distributions follow the workloads the pages discuss: Qwen-2.5-7B
 decode projections (Telegram post tggo.me/sberlogasci/42740, section
@@ -39,9 +39,30 @@ def rng(seed: int, tensor_id: int) -> np.random.Generator:
 
 
 def to_bf16_bits(a: np.ndarray) -> np.ndarray:
-    """binary64 -> binary32 -> bf16 (round to nearest even), as uint16 bits."""
+    """(binary64 ->) binary32 -> bf16 (round to nearest even), as uint16 bits."""
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _normal32(g: np.random.Generator, shape, std: float) -> np.ndarray:
+    a = g.standard_normal(shape, dtype=np.float32)
+    a *= np.float32(std)
+    return a
+
+
+def bernoulli_positions(g: np.random.Generator, count: int, p: float) -> np.ndarray:
+    """Flat indices of a Bernoulli(p) mask over `count` entries, drawn as the
+    geometric gaps between successes (the same process, far fewer draws)."""
+    out = []
+    pos = -1
+    while True:
+        gaps = g.geometric(p, size=int(count * p * 1.2) + 64)
+        idx = pos + np.cumsum(gaps)
+        out.append(idx[idx < count])
+        if idx[-1] >= count:
+            break
+        pos = int(idx[-1])
+    return np.concatenate(out)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -50,23 +71,33 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def normal_bf16(seed: int, tid: int, shape, std: float) -> np.ndarray:
-    return to_bf16_bits(rng(seed, tid).standard_normal(shape) * std)
+    return to_bf16_bits(_normal32(rng(seed, tid), shape, std))
 
 
 def outlier_weights(seed: int, tid: int, shape, std=0.02, p=0.001, mult=20.0) -> np.ndarray:
     """N(0, std) with a Bernoulli(p) mask of entries multiplied by ``mult`` (sign kept)."""
     g = rng(seed, tid)
-    w = g.standard_normal(shape) * std
-    mask = g.random(shape) < p
-    w[mask] *= mult
+    w = _normal32(g, shape, std)
+    flat = w.reshape(-1)
+    flat[bernoulli_positions(g, flat.size, p)] *= np.float32(mult)
     return to_bf16_bits(w)
 
 
 def student_t_weights(seed: int, tid: int, shape, std=0.02, nu=4.0) -> np.ndarray:
-    """Student-t(nu) scaled to standard deviation ``std`` (t_nu has std sqrt(nu/(nu-2)))."""
+    """Student-t(nu) scaled to standard deviation ``std`` (t_nu has std sqrt(nu/(nu-2))),
+    drawn as Z * sqrt(nu / (2 G)) with Z ~ N(0, 1) and G ~ Gamma(nu/2, 1); for an
+    even nu, G is the sum of nu/2 standard exponentials."""
     g = rng(seed, tid)
-    w = g.standard_t(nu, size=shape) * (std / np.sqrt(nu / (nu - 2.0)))
-    return to_bf16_bits(w)
+    z = g.standard_normal(shape, dtype=np.float32)
+    if float(nu).is_integer() and int(nu) % 2 == 0:
+        gam = g.standard_exponential(shape, dtype=np.float32)
+        for _ in range(int(nu) // 2 - 1):
+            gam += g.standard_exponential(shape, dtype=np.float32)
+    else:
+        gam = g.standard_gamma(nu / 2.0, size=shape, dtype=np.float32)
+    z *= np.sqrt(np.float32(nu) / (np.float32(2.0) * gam))
+    z *= np.float32(std / np.sqrt(nu / (nu - 2.0)))
+    return to_bf16_bits(z)
 
 
 def weights(kind: str, seed: int, tid: int, shape) -> np.ndarray:
@@ -91,7 +122,7 @@ def linear_inputs(seed: int, n: int, k: int, m: int, rank: int = LORA_RANK, wkin
 def merge_noise(seed: int, count: int) -> np.ndarray:
     """Standard normal draws, one per block; a scale-delta is 0.05 * s * z for the
     block's decoded scale s (the caller multiplies)."""
-    return rng(seed, TID_DELTA).standard_normal(count).astype(np.float32)
+    return rng(seed, TID_DELTA).standard_normal(count, dtype=np.float32)
 
 
 def moe_routing(seed: int, tokens=MOE["tokens"], experts=MOE["experts"], topk=MOE["topk"]):

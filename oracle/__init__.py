@@ -57,6 +57,7 @@ _sig("orc_merge_scale", _int, _int, _int, _flt)
 _sig("orc_nvfp4_tensor_scale", _flt, _p, _i64)
 _sig("orc_nvfp4_quantize", None, _p, _i64, _i64, _p, _p, _p)
 _sig("orc_nvfp4_quantize_frozen", None, _p, _i64, _i64, _p, _flt, _p)
+_sig("orc_nvfp4_quantize_with_tensor_scale", None, _p, _i64, _i64, _flt, _p, _p)
 _sig("orc_mxfp4_quantize", None, _p, _i64, _i64, _p, _p)
 _sig("orc_mxfp4_quantize_frozen", None, _p, _i64, _i64, _p, _p)
 _sig("orc_dequantize_f64", None, _int, _p, _p, _flt, _i64, _i64, _p)
@@ -141,6 +142,16 @@ def quantize(fmt: int, w: np.ndarray):
         return codes, scales, np.float32(st[0])
     _lib.orc_mxfp4_quantize(_ptr(w), n, k, _ptr(codes), _ptr(scales))
     return codes, scales, np.float32(1.0)
+
+
+def nvfp4_quantize_with_tensor_scale(w: np.ndarray, tensor_scale):
+    """NVFP4 block scales and codes of rows of a tensor whose s_t is given."""
+    w = _c(w, np.uint16)
+    n, k = w.shape
+    codes = np.zeros((n, k // 2), np.uint8)
+    scales = np.zeros((n, k // 16), np.uint8)
+    _lib.orc_nvfp4_quantize_with_tensor_scale(_ptr(w), n, k, float(tensor_scale), _ptr(codes), _ptr(scales))
+    return codes, scales
 
 
 def quantize_frozen(fmt: int, w: np.ndarray, scales: np.ndarray, tensor_scale=1.0):

@@ -241,13 +241,12 @@ static void nvfp4_codes_row(const uint16_t *wrow, int64_t k, const uint8_t *srow
 
 /* NVFP4 quantize: tensor scale, then per 16-block along K the E4M3 block
  * scale sb = RNE_sat(a_b / (6 s_t)) (0 when s_t == 0), then the codes. */
-void orc_nvfp4_quantize(const uint16_t *w, int64_t n, int64_t k,
-                        uint8_t *codes, uint8_t *scales, float *tensor_scale) {
-    float st;
+/* Steps after the tensor scale, for rows of a tensor whose s_t is given (the
+ * tests use it to check sampled rows of large tensors). */
+void orc_nvfp4_quantize_with_tensor_scale(const uint16_t *w, int64_t n, int64_t k, float st,
+                                          uint8_t *codes, uint8_t *scales) {
     int64_t r;
     init_grids();
-    st = orc_nvfp4_tensor_scale(w, n * k);
-    *tensor_scale = st;
 #pragma omp parallel for schedule(static)
     for (r = 0; r < n; r++) {
         const uint16_t *wrow = w + r * k;
@@ -264,6 +263,13 @@ void orc_nvfp4_quantize(const uint16_t *w, int64_t n, int64_t k,
         }
         nvfp4_codes_row(wrow, k, srow, st, codes + r * (k / 2));
     }
+}
+
+void orc_nvfp4_quantize(const uint16_t *w, int64_t n, int64_t k,
+                        uint8_t *codes, uint8_t *scales, float *tensor_scale) {
+    float st = orc_nvfp4_tensor_scale(w, n * k);
+    *tensor_scale = st;
+    orc_nvfp4_quantize_with_tensor_scale(w, n, k, st, codes, scales);
 }
 
 void orc_nvfp4_quantize_frozen(const uint16_t *w, int64_t n, int64_t k,
@@ -368,8 +374,10 @@ void orc_dequantize_f32(int fmt, const uint8_t *codes, const uint8_t *scales, fl
     init_grids();
 #pragma omp parallel for schedule(static) private(kk)
     for (r = 0; r < n; r++)
-        for (kk = 0; kk < k; kk++)
-            out[r * k + kk] = (float)weight_value(fmt, codes + r * (k / 2), scales + r * sb_per_row, st, kk);
+        for (kk = 0; kk < k; kk++) {
+            double v = weight_value(fmt, codes + r * (k / 2), scales + r * sb_per_row, st, kk);
+            out[r * k + kk] = isnan(v) ? NAN : (float)v;    /* one canonical quiet NaN */
+        }
 }
 
 /* Rounded once to bf16 (RNE), returned as bit patterns. */

@@ -1,0 +1,99 @@
+"""The C-ABI library loads and exports every symbol include/fp4w.h declares, and
+host-side validation rejects bad arguments before any launch (no GPU needed:
+every call here returns from validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4w.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4w_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mxfp4_bit_weight_amd import fp4w
+    return fp4w
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for n in ["fp4w_quantize", "fp4w_dequantize", "fp4w_linear", "fp4w_grouped_linear", "fp4w_merge_scales"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    for name in _declared():
+        assert hasattr(raw, name), name
+    assert set(_declared()) == set(lib.EXPORTED)
+
+
+def test_status_strings(lib):
+    for code in range(-6, 1):
+        assert lib.status_string(code) and lib.status_string(code) != "unknown status"
+    assert lib.status_string(-99) == "unknown status"
+    assert lib.version() >= 1
+
+
+def test_workspace_bytes(lib):
+    a = lib.linear_workspace_bytes(1, 18944, 3584, 16)
+    b = lib.linear_workspace_bytes(8, 3584, 18944, 16)
+    c = lib.linear_workspace_bytes(16384, 18944, 3584, 16)
+    assert a > 0 and b > 0 and c >= 16384 * 16 * 4
+    assert lib.linear_workspace_bytes(1, 10, 64, 65) == 0          # rank above the maximum
+    assert lib.linear_workspace_bytes(-1, 10, 64, 0) == 0
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_validation_errors_without_launch(lib):
+    q = lib._quantize
+    A = 0x10000                  # aligned fake addresses; validation fails before use
+    assert q(7, _fake(A), 4, 32, _fake(A), _fake(A), _fake(A), 0, None) == -4      # format
+    assert q(0, _fake(A), 4, 32, _fake(A), _fake(A), _fake(A), 0x10, None) == -4   # flag
+    assert q(0, _fake(A), 4, 48, _fake(A), _fake(A), _fake(A), 0, None) == -2      # k % 32
+    assert q(0, _fake(A), -1, 32, _fake(A), _fake(A), _fake(A), 0, None) == -1     # negative
+    assert q(0, None, 4, 32, _fake(A), _fake(A), _fake(A), 0, None) == -1          # null w
+    assert q(0, _fake(A), 4, 32, _fake(A), _fake(A), None, 0, None) == -1          # NVFP4 needs s_t
+    assert q(0, _fake(A + 8), 4, 32, _fake(A), _fake(A), _fake(A), 0, None) == -3  # alignment
+    assert q(0, _fake(A), 0, 32, None, None, None, 0, None) == 0                   # empty: no-op
+    d = lib._dequantize
+    assert d(0, _fake(A), _fake(A), None, 4, 32, _fake(A), 0, None) == -1
+    assert d(1, _fake(A), _fake(A), None, 4, 32, _fake(A + 4), 0, None) == -3
+    assert d(1, _fake(A), _fake(A), None, 4, 32, _fake(A), 0x1, None) == -4
+    lin = lib._linear
+    ws = lib.linear_workspace_bytes(2, 16, 64, 16)
+    args = dict(x=_fake(A), m=2, k=64, codes=_fake(A), scales=_fake(A), ts=_fake(A), n=16,
+                a=_fake(A), b=_fake(A), r=16, y=_fake(A), ws=_fake(A), wsb=ws)
+
+    def call(**kw):
+        v = dict(args, **kw)
+        return lin(0, v["x"], v["m"], v["k"], v["codes"], v["scales"], v["ts"], v["n"], v["a"], v["b"], v["r"],
+                   v["y"], v["ws"], v["wsb"], None)
+    assert call(r=65) == -2
+    assert call(k=48) == -2
+    assert call(b=None) == -1
+    assert call(wsb=ws - 1) == -6
+    assert call(ws=None) == -6
+    assert call(ws=_fake(A + 16)) == -3
+    assert call(x=_fake(A + 2)) == -3
+    assert call(m=0) == 0
+    g = lib._grouped
+    assert g(0, _fake(A), 8, None, _fake(A), 4, 8, 16, 64, _fake(A), _fake(A), _fake(A), _fake(A), None) == -1
+    assert g(0, _fake(A), 8, _fake(A), _fake(A), 4, 8, 16, 60, _fake(A), _fake(A), _fake(A), _fake(A), None) == -2
+    assert g(0, _fake(A), 8, _fake(A), _fake(A), 0, 8, 16, 64, _fake(A), _fake(A), _fake(A), _fake(A), None) == 0
+    mg = lib._merge
+    assert mg(3, _fake(A), _fake(A), 4, _fake(A), None, None, 0, None) == -4
+    assert mg(0, None, _fake(A), 4, _fake(A), None, None, 0, None) == -1
+    assert mg(0, _fake(A), _fake(A), 4, _fake(A), _fake(A + 1), _fake(A + 64), 16, None) == -3
+    assert mg(0, _fake(A), _fake(A), 0, _fake(A), None, None, 0, None) == 0

@@ -1,0 +1,81 @@
+"""GPU parity of the grouped (MoE) W4A16 linear against the binary64 oracle:
+128 experts with gate/up (768, 2048) and down (2048, 768) weights, 64 tokens
+routed top-8; plus empty experts, experts with more than 16 rows, a single
+expert, and out-of-range token indices (NaN rows)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mxfp4_bit_weight_amd import workloads as W
+from tests.gpu_util import DEV, bf16_dev, bits_host, check_bound, f32_dev, f64_of_bf16, i32_dev, say, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fp4w():
+    from mxfp4_bit_weight_amd import fp4w as F
+    return F
+
+
+def _experts(fmt, seed, e, n, k):
+    wts = W.moe_expert_weights(seed, e, n, k)
+    q = [O.quantize(fmt, wts[i]) for i in range(e)]
+    return (np.stack([c for c, _, _ in q]), np.stack([s for _, s, _ in q]),
+            np.array([t for _, _, t in q], np.float32))
+
+
+def _case(fp4w, fmt, x, row_index, offsets, codes, scales, ts, what):
+    say(f"[grouped] {what} fmt={fmt} experts={codes.shape[0]} n={codes.shape[1]} k={codes.shape[2] * 2} rows={row_index.size}")
+    y = fp4w.grouped_linear(bf16_dev(x), i32_dev(row_index), i32_dev(offsets), fmt, u8_dev(codes), u8_dev(scales),
+                            f32_dev(ts) if fmt == 0 else None)
+    torch.cuda.synchronize()
+    yg = f64_of_bf16(bits_host(y))
+    y64 = O.grouped_linear(fmt, x, row_index, offsets, codes, scales, ts)
+    xn = np.sqrt((f64_of_bf16(x) ** 2).sum(axis=1))[row_index][:, None]
+    wn = np.zeros((row_index.size, codes.shape[1]))
+    for e in range(codes.shape[0]):
+        if offsets[e + 1] > offsets[e]:
+            d = O.dequantize(fmt, codes[e], scales[e], ts[e], "f64")
+            wn[offsets[e]:offsets[e + 1]] = np.sqrt((d * d).sum(axis=1))[None, :]
+    check_bound(yg, y64, xn, wn, what)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_moe_gate_and_down(fp4w, fmt):
+    cfg = W.MOE
+    row_index, offsets = W.moe_routing(0)
+    assert row_index.size == cfg["tokens"] * cfg["topk"]
+    x = W.normal_bf16(0, W.TID_X, (cfg["tokens"], cfg["d_model"]), 1.0)
+    codes, scales, ts = _experts(fmt, 0, cfg["experts"], cfg["d_ff"], cfg["d_model"])
+    _case(fp4w, fmt, x, row_index, offsets, codes, scales, ts, "gate (768, 2048)")
+    # down projection: input rows are the routed rows themselves (identity index)
+    xd = W.normal_bf16(0, W.TID_DOWN_IN, (row_index.size, cfg["d_ff"]), 1.0)
+    codes, scales, ts = _experts(fmt, 1, cfg["experts"], cfg["d_model"], cfg["d_ff"])
+    _case(fp4w, fmt, xd, np.arange(row_index.size, dtype=np.int32), offsets, codes, scales, ts, "down (2048, 768)")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_uneven_routing(fp4w, fmt):
+    # expert 0: 40 rows (three chunks of up to 16), expert 1: 0 rows, expert 2: 1 row, expert 3: 13 rows
+    counts = np.array([40, 0, 1, 13])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rng = np.random.default_rng(9)
+    row_index = rng.integers(0, 30, offsets[-1]).astype(np.int32)
+    x = W.normal_bf16(2, W.TID_X, (30, 544), 1.0)
+    codes, scales, ts = _experts(fmt, 2, 4, 70, 544)
+    _case(fp4w, fmt, x, row_index, offsets, codes, scales, ts, "uneven routing")
+
+
+def test_bad_token_index_gives_nan_rows(fp4w):
+    offsets = np.array([0, 3, 5], np.int32)
+    row_index = np.array([0, 99, 1, -1, 2], np.int32)
+    x = W.normal_bf16(3, W.TID_X, (4, 64), 1.0)
+    codes, scales, ts = _experts(0, 3, 2, 16, 64)
+    y = fp4w.grouped_linear(bf16_dev(x), i32_dev(row_index), i32_dev(offsets), 0, u8_dev(codes), u8_dev(scales),
+                            f32_dev(ts))
+    torch.cuda.synchronize()
+    yh = y.float().cpu().numpy()
+    assert np.isnan(yh[1]).all() and np.isnan(yh[3]).all()
+    assert np.isfinite(yh[[0, 2, 4]]).all()

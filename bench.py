@@ -1,0 +1,424 @@
+"""Benchmark of the W4A16 hot path on one MI355X.
+
+One step = one decode pass of the Qwen-2.5-7B projection shapes (18944x3584
+gate/up, 3584x18944 down, 3584x3584 qkv-o) at M = 1 through ``fp4w.linear``
+with NVFP4 weights and a rank-16 LoRA, on weights rotated over more than 1 GiB
+of distinct copies so that every call streams its weights from HBM.  ``value``
+is the step's algorithmic bytes over its time (GB/s).  The JSON line also holds
+the roofline of the decode kernel (HIP events around each launch), the CPU
+oracle timed on a bounded sample, and the other hot-path rows (M = 8, MXFP4,
+the 16384-row prefill GEMM, quantize, merge, dequantize, grouped MoE).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-rows]
+Progress goes to stderr; stdout is exactly one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+ROTATE_BYTES = 1 << 30         # rotate each weight over at least 1 GiB (4x the 256 MB MALL)
+METRIC = "W4A16 NVFP4 linear: effective HBM GB/s (% peak) at M=1/8; TFLOP/s at M=16K"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--skip-rows", action="store_true", help="only the headline step and its roofline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
+    return p.parse_args()
+
+
+# ---- algorithmic work ---------------------------------------------------------------
+
+def linear_bytes(fmt, m, n, k, r):
+    blk = 16 if fmt == 0 else 32
+    w = n * k // 2 + n * k // blk + (4 if fmt == 0 else 0)
+    return w + 2 * r * (k + n) + 2 * m * (k + n)
+
+
+def linear_flops(m, n, k, r):
+    return 2 * m * n * k + 2 * m * r * (k + n)
+
+
+def quant_bytes(fmt, count):
+    blk = 16 if fmt == 0 else 32
+    return 2 * count + count // 2 + count // blk + (4 if fmt == 0 else 0)
+
+
+# ---- device helpers -------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        log(f"bench.py measures one GPU only: every box here has a single MI355X, so --gpus {args.gpus} "
+            "is not supported (the multi-GPU sharding of this path is described in DESIGN.md).")
+        sys.exit(2)
+    import torch
+    from mxfp4_bit_weight_amd import fp4w
+    from mxfp4_bit_weight_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def sync():
+        torch.cuda.synchronize(dev)
+
+    def copies_for(nbytes):
+        return max(2, -(-ROTATE_BYTES // nbytes))
+
+    def time_loop(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        sync()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            fn(warmup + i)
+        e1.record()
+        sync()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall
+
+    def time_per_launch(fn, steps, warmup):
+        """Average duration of single-launch calls, from an event pair around each.
+        A sleep kernel at the head of the stream lets the host queue every event and
+        launch before the GPU reaches them, so host latency is not timed."""
+        for i in range(warmup):
+            fn(i)
+        sync()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda._sleep(int(2.4e9 * 0.05))          # about 50 ms of queue head start
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            fn(warmup + i)
+            b.record()
+        sync()
+        d = np.array([a.elapsed_time(b) for a, b in evs])
+        return float(d.mean()), float(np.median(d))
+
+    def time_graph(fn, steps, warmup):
+        """Capture `warmup` and `steps` calls of fn into two HIP graphs and time the
+        replay of the second (launch overhead off the critical path)."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(s)
+        sync()
+        gw, gt = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw):
+            for i in range(warmup):
+                fn(i)
+        with torch.cuda.graph(gt):
+            for i in range(steps):
+                fn(warmup + i)
+        gw.replay()
+        sync()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        gt.replay()
+        e1.record()
+        sync()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall
+
+    # ---- decode weights: quantize once on the device, then clone for rotation ----------
+    rank = W.LORA_RANK
+    shapes = W.QWEN7B_SHAPES
+    decode = {}
+    t_gen = time.time()
+    for fmt in (0, 1):
+        for si, (name, (n, k)) in enumerate(shapes.items()):
+            wkind = "outlier" if fmt == 0 else "student_t"
+            w, x1, a, b = W.linear_inputs(100 + si, n, k, 1, rank=rank, wkind=wkind)
+            x8 = W.normal_bf16(100 + si, W.TID_X + 50, (8, k), 1.0)
+            q0 = fp4w.quantize(bf16(w), fmt)
+            nb = linear_bytes(fmt, 1, n, k, rank)
+            reps = copies_for(nb)
+            qs = []
+            ad, bd = bf16(a), bf16(b)
+            for _ in range(reps):
+                qs.append((fp4w.QWeight(fmt, q0.codes.clone(), q0.scales.clone(),
+                                        q0.tensor_scale.clone() if q0.tensor_scale is not None else None, n, k),
+                           ad.clone(), bd.clone()))
+            decode[(fmt, name)] = dict(n=n, k=k, x1=bf16(x1), x8=bf16(x8), qs=qs, host=(w, x1, a, b))
+            log(f"[bench] prepared fmt={fmt} {name} ({n},{k}) x{reps} copies")
+    sync()
+    log(f"[bench] inputs ready in {time.time() - t_gen:.1f}s")
+
+    # ---- headline step: NVFP4, M = 1, three shapes, LoRA r = 16 ------------------------
+    ys = {name: torch.empty((8, d["n"]), dtype=torch.bfloat16, device=dev)
+          for (fmt, name), d in decode.items() if fmt == 0}
+    ws_bytes = max(fp4w.linear_workspace_bytes(m, n, k, rank) for (n, k) in shapes.values() for m in (1, 8))
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)      # zero-filled once, reused by every call
+
+    def step(i):
+        for name in shapes:
+            d = decode[(0, name)]
+            q, a, b = d["qs"][i % len(d["qs"])]
+            fp4w.linear(d["x1"], q, a, b, out=ys[name][:1], workspace=ws)
+
+    step_bytes = sum(linear_bytes(0, 1, n, k, rank) for n, k in shapes.values())
+    ms_step, wall = time_graph(step, args.steps, args.warmup)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"[bench] step (graph replay): {ms_step * 1e3:.2f} us, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of peak)")
+    ms_eager, _ = time_loop(step, args.steps, args.warmup)
+    log(f"[bench] step (eager launches): {ms_eager * 1e3:.2f} us")
+
+    # ---- roofline: the decode kernel alone (gate/up, M = 1, no LoRA: one launch) --------
+    dg = decode[(0, "gate_up")]
+    n, k = dg["n"], dg["k"]
+
+    def gemv_only(i):
+        q, _, _ = dg["qs"][i % len(dg["qs"])]
+        fp4w.linear(dg["x1"], q, out=ys["gate_up"][:1], workspace=ws)
+
+    per_launch_ms, med_ms = time_per_launch(gemv_only, max(args.steps, 100), args.warmup)
+    gemv_bytes = linear_bytes(0, 1, n, k, 0)
+    achieved = gemv_bytes / (per_launch_ms * 1e-3) / 1e9
+    roofline = {"kernel": "linear_skinny_kernel<NVFP4, 1 m-group> on (18944, 3584), M=1",
+                "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(gemv_bytes),
+                "avg_launch_us": round(per_launch_ms * 1e3, 3), "median_launch_us": round(med_ms * 1e3, 3),
+                "algorithmic_bytes_per_launch": gemv_bytes}
+    log(f"[bench] decode kernel alone: {per_launch_ms * 1e3:.2f} us/launch, {achieved:.1f} GB/s")
+
+    rows = {}
+    if not args.skip_rows:
+        rows = other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_graph, rank)
+
+    cpu = cpu_baseline(args, W, decode, rank, step_bytes)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Qwen-2.5-7B decode projections (18944x3584, 3584x18944, 3584x3584), "
+                               "NVFP4 W4A16, M=1, LoRA r=16, weights rotated over >1 GiB",
+                   "batch_rows": 1, "lora_rank": rank, "format": "nvfp4",
+                   "step_algorithmic_bytes": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "timing": "HIP graph replay of the timed steps", "eager_us_per_step": round(ms_eager * 1e3, 2),
+                   "wall_s_timed_region": round(wall, 4)},
+        "roofline": roofline, "cpu_baseline": cpu, "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def pmc_traffic(alg_bytes):
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3 --pmc
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "skinny_gate_up_m1_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for f in ("skinny.hpp", "linear.hip", "fp4w_device.hpp"):
+        h.update(open(os.path.join(ROOT, "mxfp4_bit_weight_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_graph, rank):
+    rows = {}
+    reps = max(20, args.steps // 4)
+    ws_bytes = max(fp4w.linear_workspace_bytes(m, n, k, rank) for (n, k) in W.QWEN7B_SHAPES.values() for m in (1, 8))
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    # decode linears, every shape, M = 1 and 8, both formats
+    dec = {}
+    for (fmt, name), d in decode.items():
+        for m in (1, 8):
+            x = d["x1"] if m == 1 else d["x8"]
+            y = torch.empty((m, d["n"]), dtype=torch.bfloat16, device=dev)
+
+            def f(i, d=d, x=x, y=y):
+                q, a, b = d["qs"][i % len(d["qs"])]
+                fp4w.linear(x, q, a, b, out=y, workspace=ws)
+            ms, _ = time_graph(f, reps, 5)
+            nb = linear_bytes(fmt, m, d["n"], d["k"], rank)
+            gbs = nb / (ms * 1e-3) / 1e9
+            dec[f"{'nvfp4' if fmt == 0 else 'mxfp4'}/{name}/M{m}"] = {
+                "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                "algorithmic_bytes": nb}
+    rows["decode_linear_with_lora"] = dec
+    log("[bench] decode rows done")
+
+    # prefill GEMM: x 16384 x 3584, W (18944, 3584), LoRA r = 16
+    d = decode[(0, "gate_up")]
+    n, k = d["n"], d["k"]
+    mrows = W.PREFILL_M
+    x = bf16(W.normal_bf16(300, W.TID_X, (mrows, k), 1.0))
+    y = torch.empty((mrows, n), dtype=torch.bfloat16, device=dev)
+    q, a, b = d["qs"][0]
+    wsg = torch.zeros(fp4w.linear_workspace_bytes(mrows, n, k, rank), dtype=torch.uint8, device=dev)
+    gms, _ = time_loop(lambda i: fp4w.linear(x, q, a, b, out=y, workspace=wsg), 5, 2)
+    fl = linear_flops(mrows, n, k, rank)
+    tf = fl / (gms * 1e-3) / 1e12
+    rows["prefill_gemm_nvfp4"] = {"m": mrows, "n": n, "k": k, "ms": round(gms, 3), "TFLOP/s": round(tf, 1),
+                                  "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 1), "algorithmic_flop": fl}
+    log(f"[bench] prefill GEMM {gms:.3f} ms, {tf:.1f} TFLOP/s")
+    del x, y
+    torch.cuda.empty_cache()
+
+    # quantize over a 7B-shaped set: 28 layers x {2 x (18944,3584), (3584,18944), 4 x (3584,3584)}
+    for fmt in (0, 1):
+        base = {}
+        for name, (n, k) in W.QWEN7B_SHAPES.items():
+            base[(n, k)] = bf16(decode[(fmt, name)]["host"][0])      # the decode weights of this format
+        tensors, outs = [], []
+        for _ in range(W.QWEN7B_LAYERS):
+            for (n, k) in W.QWEN7B_LAYER:
+                tensors.append(base[(n, k)].clone())
+                outs.append(fp4w.empty_qweight(fmt, n, k, dev))
+        count = sum(t.numel() for t in tensors)
+
+        def qpass(i):
+            for t, o in zip(tensors, outs):
+                fp4w.quantize(t, fmt, out=o)
+        ms, _ = time_loop(qpass, 3, 1)
+        nb = sum(quant_bytes(fmt, t.numel()) for t in tensors)
+        gbs = nb / (ms * 1e-3) / 1e9
+        rows[f"quantize_7b_set_{'nvfp4' if fmt == 0 else 'mxfp4'}"] = {
+            "weights": count, "tensors": len(tensors), "ms": round(ms, 3), "GB/s": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "weights_per_s": round(count / (ms * 1e-3), 1),
+            "algorithmic_bytes": nb}
+        log(f"[bench] quantize fmt={fmt}: {ms:.2f} ms, {gbs:.1f} GB/s")
+        # dequantize the same set (bf16 out)
+        deq = [torch.empty((o.n, o.k), dtype=torch.bfloat16, device=dev) for o in outs[:7]]
+
+        def dpass(i):
+            for j, o in enumerate(outs):
+                fp4w.dequantize(o, out=deq[j % 7])
+        ms_d, _ = time_loop(dpass, 3, 1)
+        nbd = sum(o.n * o.k * 2 + o.n * o.k // 2 + o.n * o.k // (16 if fmt == 0 else 32) for o in outs)
+        rows[f"dequantize_7b_set_{'nvfp4' if fmt == 0 else 'mxfp4'}"] = {
+            "ms": round(ms_d, 3), "GB/s": round(nbd / (ms_d * 1e-3) / 1e9, 1), "algorithmic_bytes": nbd}
+        if fmt == 0:
+            # scale-only merge of the (18944, 3584) weight, in place; ratio to re-quantizing it
+            o = outs[0]
+            s_t = o.scales.reshape(-1).cpu()
+            dec_s = s_t.view(torch.float8_e4m3fn).to(torch.float32).numpy()
+            z = W.merge_noise(401, o.scales.numel())
+            deltas = torch.from_numpy((np.float32(0.05) * dec_s * z).astype(np.float32)).to(dev).reshape(o.scales.shape)
+            merged = torch.empty_like(o.scales)
+
+            def mpass(i):
+                fp4w.merge_scales(o, deltas, scales_out=merged)
+            ms_m, _ = time_loop(mpass, 50, 5)
+            ms_q, _ = time_loop(lambda i: fp4w.quantize(tensors[0], 0, out=outs[0]), 20, 3)
+            nbm = o.scales.numel() * (1 + 4 + 1)
+            rows["merge_scales_nvfp4"] = {"blocks": o.scales.numel(), "us": round(ms_m * 1e3, 2),
+                                          "GB/s": round(nbm / (ms_m * 1e-3) / 1e9, 1), "algorithmic_bytes": nbm,
+                                          "requantize_same_tensor_us": round(ms_q * 1e3, 2),
+                                          "speedup_vs_requantize": round(ms_q / ms_m, 1)}
+        del tensors, outs, base, deq
+        torch.cuda.empty_cache()
+    log("[bench] quantize/dequantize/merge rows done")
+
+    # grouped MoE: 128 experts, gate/up (768, 2048), down (2048, 768), 64 tokens top-8
+    cfg = W.MOE
+    row_index, offsets = W.moe_routing(500)
+    active = int((np.diff(offsets) > 0).sum())
+    ri, off = torch.from_numpy(row_index).to(dev), torch.from_numpy(offsets).to(dev)
+    x = bf16(W.normal_bf16(500, W.TID_X, (cfg["tokens"], cfg["d_model"]), 1.0))
+    xd = bf16(W.normal_bf16(500, W.TID_DOWN_IN, (row_index.size, cfg["d_ff"]), 1.0))
+    rid = torch.arange(row_index.size, dtype=torch.int32, device=dev)
+    experts = {}
+    for ti, (n, k, tag) in enumerate([(cfg["d_ff"], cfg["d_model"], "gate"), (cfg["d_ff"], cfg["d_model"], "up"),
+                                      (cfg["d_model"], cfg["d_ff"], "down")]):
+        wd = bf16(W.moe_expert_weights(600 + ti, cfg["experts"], n, k))
+        codes = torch.empty((cfg["experts"], n, k // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((cfg["experts"], n, k // 16), dtype=torch.uint8, device=dev)
+        ts = torch.empty(cfg["experts"], dtype=torch.float32, device=dev)
+        for e in range(cfg["experts"]):          # per-expert tensor scale
+            fp4w.quantize(wd[e], 0, out=fp4w.QWeight(0, codes[e], scales[e], ts[e:e + 1], n, k))
+        experts[tag] = (codes, scales, ts, n, k)
+        del wd
+    copies = 4
+    moe = [{tag: (c.clone(), s.clone(), t.clone(), n, k) for tag, (c, s, t, n, k) in experts.items()}
+           for _ in range(copies)]
+    yg = torch.empty((row_index.size, cfg["d_ff"]), dtype=torch.bfloat16, device=dev)
+    yd = torch.empty((row_index.size, cfg["d_model"]), dtype=torch.bfloat16, device=dev)
+
+    def moe_pass(i):
+        e = moe[i % copies]
+        for tag in ("gate", "up"):
+            c, s, t, n, k = e[tag]
+            fp4w.grouped_linear(x, ri, off, 0, c, s, t, out=yg)
+        c, s, t, n, k = e["down"]
+        fp4w.grouped_linear(xd, rid, off, 0, c, s, t, out=yd)
+    ms, _ = time_loop(moe_pass, 30, 5)
+    nb = 0
+    for tag, (c, s, t, n, k) in experts.items():
+        nb += active * (n * k // 2 + n * k // 16 + 4)
+    nb += 2 * (2 * cfg["tokens"] * cfg["d_model"] + 2 * row_index.size * cfg["d_ff"])
+    nb += 2 * row_index.size * cfg["d_ff"] + 2 * row_index.size * cfg["d_model"]
+    gbs = nb / (ms * 1e-3) / 1e9
+    rows["grouped_moe_nvfp4"] = {"experts": cfg["experts"], "active_experts": active, "rows": int(row_index.size),
+                                 "us_per_gate_up_down": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                                 "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "algorithmic_bytes": nb}
+    log(f"[bench] grouped MoE {ms * 1e3:.1f} us, {gbs:.1f} GB/s")
+    return rows
+
+
+def cpu_baseline(args, W, decode, rank, step_bytes):
+    """The CPU oracle (test infrastructure, binary64) on the same decode step, on
+    all host cores it is given, repeated for about --cpu-seconds."""
+    import oracle as O
+    host = {name: decode[(0, name)]["host"] for name in W.QWEN7B_SHAPES}
+    prepared = {}
+    for name, (w, x1, a, b) in host.items():
+        c, s, st = O.quantize(O.NVFP4, w)
+        prepared[name] = (x1, c, s, st, a, b)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for name, (x1, c, s, st, a, b) in prepared.items():
+            O.linear(O.NVFP4, x1, c, s, st, a, b)
+        reps += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(step_bytes * reps / dt / 1e9, 3), "unit": "GB/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} decode steps (the three Qwen-2.5-7B shapes at M=1, NVFP4, LoRA r=16), binary64 "
+                      f"oracle with OpenMP, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -7,7 +7,7 @@
 //
 // Launches per call:
 //   1. lora_down_kernel      t = x A^T (fp32, M x r), split over K, ordered sum
-//   2. m <= 16: linear_skinny_kernel (decode-shaped, HBM-bound; skinny.hpp)
+//   2. m <= 16: linear_decode_kernel (decode-shaped, HBM-bound; skinny.hpp)
 //      m >  16: linear_gemm_kernel   (LDS-staged bf16 MFMA GEMM, dequantizing
 //                                      each weight tile once into LDS)
 // Split-K partial sums are combined by the last workgroup to arrive, in a fixed
@@ -20,8 +20,13 @@
 namespace fp4w {
 
 // ---------------------------------------------------------------------------------
-// Cross-workgroup helpers: partial sums are written and read with agent-scope
-// atomics so no workgroup sees a stale cached copy.
+// Cross-workgroup partial sums.  Partials are stored and loaded as relaxed
+// agent-scope atomics: on gfx950 these are emitted with the SC1 bit, which makes
+// them coherent across the XCDs' separate L2s without an L2-wide writeback or
+// invalidate (a __threadfence() costs both, on every workgroup).  The writer
+// waits for its stores to complete (s_waitcnt) before it increments the arrival
+// counter, and the reader issues its loads only after the increment returned,
+// so the last arrival sees every partial.
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ void store_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -29,23 +34,38 @@ __device__ __forceinline__ void store_agent(float* p, float v) {
 __device__ __forceinline__ float load_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void wait_stores_complete() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
-// Returns true in every thread of the last workgroup to arrive at counter *cnt
-// out of `expected`; that workgroup also resets the counter.  Partials must have
-// been stored before the call.
+// Workgroup version: every thread calls it after storing its partials; returns
+// true in all threads of the last workgroup to arrive (which resets the counter).
 __device__ __forceinline__ bool arrive_last(uint32_t* cnt, uint32_t expected, int* flag_lds) {
-  __threadfence();
+  wait_stores_complete();
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t old = atomicAdd(cnt, 1u);
+    uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     bool last = old == expected - 1u;
     if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag_lds = last ? 1 : 0;
   }
   __syncthreads();
-  const bool last = *flag_lds != 0;
-  if (last) __threadfence();
-  return last;
+  return *flag_lds != 0;
+}
+
+// Wave version: every lane calls it after storing its partials.
+__device__ __forceinline__ bool wave_arrive_last(uint32_t* cnt, uint32_t expected, int lane) {
+  wait_stores_complete();
+  uint32_t old = 0;
+  if (lane == 0) {
+    old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == expected - 1u) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  old = (uint32_t)__shfl((int)old, 0, 64);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return old == expected - 1u;
 }
 
 // ---------------------------------------------------------------------------------
@@ -131,51 +151,148 @@ __device__ __forceinline__ float lora_term(const float* __restrict__ t, const ui
   return s;
 }
 
-template <int FMT, int MG, int U>
-__global__ __launch_bounds__(SK_THREADS) void linear_skinny_kernel(
+// One wave per (16-row weight tile, K split).  WPW waves per workgroup share the
+// split: its x rows and the scale bytes of the workgroup's tile rows are staged
+// in LDS.  The staging loads are issued first, then each wave's ring prologue,
+// so the memory latencies overlap; the LDS writes follow.  With one split the
+// wave writes y; with several, the last wave of a tile to arrive adds the
+// partials in split order and writes y.
+//   scales16: scale rows of every split start 16-byte aligned (16-byte staging)
+constexpr int DECODE_STAGE_CHUNK = 8;     // 16-byte staging units per thread issued before the ring
+
+template <int FMT, int MG, int DEPTH, int WPW>
+__global__ __launch_bounds__(64 * WPW) void linear_decode_kernel(
     const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t N,
     const float* __restrict__ t, const uint16_t* __restrict__ lora_b, int r, uint16_t* __restrict__ y,
-    float* __restrict__ part, uint32_t* __restrict__ cnt, int S, int steps_per_split, int nsteps) {
-  __shared__ float red[SK_WAVES * 16 * 64];
-  __shared__ float fin[16 * 16];
-  __shared__ int flag;
-  const int tile = blockIdx.x / S, s = blockIdx.x % S;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4;
-  const int64_t row = (int64_t)tile * SK_TILE_N + (lane & 15);
-  const int64_t blk = (FMT == FMT_NVFP4) ? 16 : 32;
-  const uint8_t* codes_row = row < N ? codes + row * (K / 2) : nullptr;
-  const uint8_t* scales_row = row < N ? scales + row * (K / blk) : nullptr;
-  const uint16_t* xrow[MG];
-#pragma unroll
-  for (int mg = 0; mg < MG; mg++) {
-    const int m = a_operand_row<FMT>(lane, mg);
-    xrow[mg] = (m >= 0 && m < M) ? x + (int64_t)m * K : nullptr;
-  }
-  const int sb = s * steps_per_split, se = min(nsteps, sb + steps_per_split);
-  SkinnyTileResult res;
-  skinny_tile<FMT, MG, U>(codes_row, scales_row, xrow, K, sb, se, wave, g, res);
-  skinny_reduce<FMT, MG>(res, red, fin, M);
+    float* __restrict__ part, uint32_t* __restrict__ cnt, int S, int steps_per_split, int nsteps_total,
+    int ntiles, int scales16) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];     // see DecodeLds
+  constexpr int NT = 64 * WPW;
+  constexpr int BLK = DecodeLds<FMT>::BLK;
+  const int s = blockIdx.x % S, tg = blockIdx.x / S;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kslice = steps_per_split * SK_STEP_K;
+  const int step0 = s * steps_per_split;
+  const int nsteps = min(steps_per_split, nsteps_total - step0);
+  const int64_t k0 = (int64_t)step0 * SK_STEP_K;
+  const int srow = DecodeLds<FMT>::srow_bytes(kslice);
+  uint8_t* lds_s = reinterpret_cast<uint8_t*>(xs + DECODE_XS_ZERO + M * kslice);
+  const int64_t krem = K - k0;
+  const int svalid = krem <= 0 ? 0 : (int)((krem < kslice ? krem : kslice) / BLK);   // scale bytes per row here
+  const int64_t srow_g = K / BLK;                                                       // global scale row length
+  const int64_t row_base = (int64_t)tg * WPW * SK_TILE_N;
 
-  const int tid = threadIdx.x;
-  const int m = tid >> 4, nn = tid & 15;
-  const int64_t orow = (int64_t)tile * SK_TILE_N + nn;
-  const bool mine = m < M && orow < N;
-  float v = mine ? fin[m * 16 + nn] : 0.f;
-  if (S > 1) {
-    if (mine) store_agent(&part[((int64_t)s * N + orow) * M + m], v);
-    if (!arrive_last(&cnt[tile], (uint32_t)S, &flag)) return;
-    if (mine) {
-      v = 0.f;
-      for (int q = 0; q < S; q++) v += load_agent(&part[((int64_t)q * N + orow) * M + m]);
+  // staging units of 16 bytes: x first, then (if aligned) whole 16-byte scale units
+  const int ux = M * kslice / 8;
+  const int us_row = svalid / 16;                     // full 16-byte units per scale row
+  const int us = scales16 ? WPW * SK_TILE_N * us_row : 0;
+  const int utotal = ux + us;
+  auto unit_src = [&](int u, bool& ok) -> const void* {
+    if (u < ux) {
+      const int m = (8 * u) / kslice, kk = 8 * u - m * kslice;
+      ok = k0 + kk < K;
+      return x + (int64_t)m * K + (ok ? k0 + kk : 0);
+    }
+    const int v = u - ux, rw = v / (us_row > 0 ? us_row : 1), q = v - rw * us_row;
+    int64_t grow = row_base + rw;
+    ok = grow < N;
+    grow = grow < N ? grow : N - 1;
+    return scales + grow * srow_g + k0 / BLK + 16 * q;
+  };
+  auto unit_dst = [&](int u) -> u32x4_t* {
+    if (u < ux) return reinterpret_cast<u32x4_t*>(xs + DECODE_XS_ZERO + 8 * u);
+    const int v = u - ux, rw = v / (us_row > 0 ? us_row : 1), q = v - rw * us_row;
+    return reinterpret_cast<u32x4_t*>(lds_s + rw * srow + 16 * q);
+  };
+  u32x4_t stage[DECODE_STAGE_CHUNK];
+  bool stage_ok[DECODE_STAGE_CHUNK];
+#pragma unroll
+  for (int c = 0; c < DECODE_STAGE_CHUNK; c++) {
+    const int u = tid + c * NT;
+    bool ok = false;
+    const void* src = unit_src(u < utotal ? u : 0, ok);
+    stage[c] = load16(src);
+    stage_ok[c] = ok && u < utotal;
+  }
+
+  const int tile_raw = tg * WPW + wave;
+  const bool has_tile = tile_raw < ntiles;
+  const int tile = has_tile ? tile_raw : ntiles - 1;
+  const int g = lane >> 4, n = lane & 15;
+  const int64_t row = (int64_t)tile * SK_TILE_N + n;
+  const int64_t rrow = row < N ? row : N - 1;          // rows past N read row N - 1 (never stored)
+  DecodeRing<FMT, MG, DEPTH> ring;
+  ring.prologue(codes + rrow * (K / 2), k0, K, nsteps, lane);
+
+  if (tid < DECODE_XS_ZERO / 8) *reinterpret_cast<u32x4_t*>(xs + 8 * tid) = (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int c = 0; c < DECODE_STAGE_CHUNK; c++) {
+    const int u = tid + c * NT;
+    if (u < utotal) *unit_dst(u) = stage_ok[c] ? stage[c] : (u32x4_t){0u, 0u, 0u, 0u};
+  }
+  for (int u = tid + DECODE_STAGE_CHUNK * NT; u < utotal; u += NT) {
+    bool ok;
+    const void* src = unit_src(u, ok);
+    const u32x4_t v = load16(src);
+    *unit_dst(u) = ok ? v : (u32x4_t){0u, 0u, 0u, 0u};
+  }
+  // remaining scale bytes (unaligned rows, a partial last unit, padding): byte by byte
+  {
+    const int first = scales16 ? 16 * us_row : 0;
+    const int per_row = srow - first;
+    for (int idx = tid; idx < WPW * SK_TILE_N * per_row; idx += NT) {
+      const int rw = idx / per_row, b = first + (idx - rw * per_row);
+      const int64_t grow = row_base + rw;
+      uint8_t val = 0;
+      if (b < svalid && grow < N) val = scales[grow * srow_g + k0 / BLK + b];
+      lds_s[rw * srow + b] = val;
     }
   }
-  if (mine) {
-    const float st = (FMT == FMT_NVFP4) ? *tensor_scale : 1.0f;
-    float o = st * v;
-    if (t) o += lora_term(t, lora_b, r, m, orow);
-    y[(int64_t)m * N + orow] = (uint16_t)f32_to_bf16_rne(o);
+  __syncthreads();
+  if (!has_tile) return;
+  float v[MG][4];
+  ring.run(xs, kslice, lds_s + (wave * SK_TILE_N + n) * srow, M, lane, v);
+
+  // the (m, n) outputs this lane owns (see DecodeRing)
+  const float st = (FMT == FMT_NVFP4) ? *tensor_scale : 1.0f;
+  auto owns = [&](int mg, int e, int& m) -> bool {
+    m = (FMT == FMT_NVFP4) ? 4 * mg + e : 4 * g + e;
+    const bool lane_ok = (FMT == FMT_NVFP4) ? (g == 0) : (mg == 0);
+    return lane_ok && m < M && row < N;
+  };
+  if (S > 1) {
+#pragma unroll
+    for (int mg = 0; mg < MG; mg++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        int m;
+        if (owns(mg, e, m)) store_agent(&part[((int64_t)s * N + row) * M + m], v[mg][e]);
+      }
+    if (!wave_arrive_last(&cnt[tile], (uint32_t)S, lane)) return;
+#pragma unroll
+    for (int mg = 0; mg < MG; mg++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        int m;
+        if (owns(mg, e, m)) {
+          float sum = 0.f;
+          for (int q = 0; q < S; q++) sum += load_agent(&part[((int64_t)q * N + row) * M + m]);
+          v[mg][e] = sum;
+        }
+      }
   }
+#pragma unroll
+  for (int mg = 0; mg < MG; mg++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      int m;
+      if (owns(mg, e, m)) {
+        float o = st * v[mg][e];
+        if (t) o += lora_term(t, lora_b, r, m, row);
+        y[(int64_t)m * N + row] = (uint16_t)f32_to_bf16_rne(o);
+      }
+    }
 }
 
 // ---------------------------------------------------------------------------------
@@ -401,15 +518,22 @@ static int lora_parts_for(int64_t m, int64_t k) {
   return (int)p;
 }
 
-static int skinny_splits_for(int64_t n, int64_t k) {
+// x rows of one split are staged in LDS: at most this many bytes per workgroup.
+constexpr int64_t kDecodeLdsBytes = 32768;
+// Aim for at least this many waves (one per tile and split) in the decode kernel.
+constexpr int64_t kDecodeTargetWaves = 1024;
+
+static int decode_splits_for(int64_t m, int64_t n, int64_t k) {
   const int64_t tiles = (n + SK_TILE_N - 1) / SK_TILE_N;
   const int64_t nsteps = (k + SK_STEP_K - 1) / SK_STEP_K;
-  if (tiles > kTileSlots) return 1;
-  int64_t s = (1024 + tiles - 1) / tiles;     // aim for >= 1024 workgroups
-  const int64_t max_s = nsteps / 4 > 0 ? nsteps / 4 : 1;   // keep >= 4 steps (one per wave)
-  if (s > max_s) s = max_s;
+  const int64_t max_steps = kDecodeLdsBytes / (2 * SK_STEP_K * (m > 0 ? m : 1) + 4 * SK_TILE_N * 8);  // LDS per split
+  int64_t s_lds = (nsteps + max_steps - 1) / max_steps;
+  int64_t s_par = (kDecodeTargetWaves + tiles - 1) / tiles;
+  const int64_t max_par = nsteps / 2 > 0 ? nsteps / 2 : 1;            // keep >= 2 steps per wave
+  if (s_par > max_par) s_par = max_par;
+  int64_t s = s_lds > s_par ? s_lds : s_par;
+  if (s > nsteps) s = nsteps;
   if (s < 1) s = 1;
-  if (s > 64) s = 64;
   return (int)s;
 }
 
@@ -417,7 +541,8 @@ LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
   LinearPlan p{};
   p.path = m <= 16 ? 0 : 1;
   p.lora_parts = r > 0 ? lora_parts_for(m, k) : 0;
-  p.splits = p.path == 0 ? skinny_splits_for(n, k) : 1;
+  p.splits = p.path == 0 ? decode_splits_for(m, n, k) : 1;
+  if (p.splits > 1 && (n + SK_TILE_N - 1) / SK_TILE_N > kTileSlots) p.path = 1;   // counters would not fit
   size_t off = 0;
   p.off_count = off;
   off += sizeof(uint32_t) * kCounterSlots;
@@ -432,27 +557,50 @@ LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
   return p;
 }
 
+// Waves per workgroup of the decode kernel: 1 while the staged x slice is small
+// (every wave independent), 4 when it is large enough that sharing it matters.
+static int decode_wpw(int64_t m) { return m <= 4 ? 1 : 4; }
+
 template <int FMT>
-static void launch_skinny(int mg, const void* x, int64_t m, int64_t k, const uint8_t* codes, const uint8_t* scales,
-                          const float* ts, int64_t n, const float* t, const void* lb, int r, void* y, float* part,
-                          uint32_t* cnt, int S, hipStream_t stream) {
-  const int64_t tiles = (n + SK_TILE_N - 1) / SK_TILE_N;
+static hipError_t launch_decode(int mg, const void* x, int64_t m, int64_t k, const uint8_t* codes,
+                                const uint8_t* scales, const float* ts, int64_t n, const float* t, const void* lb,
+                                int r, void* y, float* part, uint32_t* cnt, int S, hipStream_t stream) {
+  constexpr int BLK = DecodeLds<FMT>::BLK;
+  const int ntiles = (int)((n + SK_TILE_N - 1) / SK_TILE_N);
   const int nsteps = (int)((k + SK_STEP_K - 1) / SK_STEP_K);
-  const int sps = (nsteps + S - 1) / S;
-  const dim3 grid((unsigned)(tiles * S)), block(SK_THREADS);
+  // steps per split: a multiple of 4 when the split is real (16-byte aligned
+  // scale slices for both formats); the split count can only shrink
+  int sps = (nsteps + S - 1) / S;
+  if (S > 1) {
+    sps = (sps + 3) & ~3;
+    S = (nsteps + sps - 1) / sps;
+  }
+  const int kslice = sps * SK_STEP_K;
+  const int wpw = decode_wpw(m);
+  const int groups = (ntiles + wpw - 1) / wpw;
+  const size_t lds = DecodeLds<FMT>::bytes((int)m, kslice, wpw * SK_TILE_N);
+  const int scales16 = ((reinterpret_cast<uintptr_t>(scales) & 15u) == 0 && (k / BLK) % 16 == 0 &&
+                        (kslice / BLK) % 16 == 0) ? 1 : 0;
+  const dim3 grid((unsigned)((int64_t)groups * S));
   const uint16_t* xx = reinterpret_cast<const uint16_t*>(x);
   const uint16_t* bb = reinterpret_cast<const uint16_t*>(lb);
   uint16_t* yy = reinterpret_cast<uint16_t*>(y);
-#define FP4W_SKINNY(MGv, Uv)                                                                                    \
-  hipLaunchKernelGGL((linear_skinny_kernel<FMT, MGv, Uv>), grid, block, 0, stream, xx, (int)m, k, codes, scales, \
-                     ts, n, t, bb, r, yy, part, cnt, S, sps, nsteps)
-  switch (mg) {
-    case 1: FP4W_SKINNY(1, 4); break;
-    case 2: FP4W_SKINNY(2, 2); break;
-    case 3: FP4W_SKINNY(3, 1); break;
-    default: FP4W_SKINNY(4, 1); break;
+#define FP4W_DECODE(MGv, WPWv)                                                                                   \
+  hipLaunchKernelGGL((linear_decode_kernel<FMT, MGv, (MGv == 1 ? 8 : 4), WPWv>), grid, dim3(64 * WPWv), lds,     \
+                     stream, xx, (int)m, k, codes, scales, ts, n, t, bb, r, yy, part, cnt, S, sps, nsteps, ntiles, \
+                     scales16)
+  if (FMT == FMT_MXFP4) {
+    if (wpw == 1) FP4W_DECODE(1, 1); else FP4W_DECODE(1, 4);
+  } else {
+    switch (mg) {
+      case 1: FP4W_DECODE(1, 1); break;
+      case 2: FP4W_DECODE(2, 4); break;
+      case 3: FP4W_DECODE(3, 4); break;
+      default: FP4W_DECODE(4, 4); break;
+    }
   }
-#undef FP4W_SKINNY
+#undef FP4W_DECODE
+  return hipSuccess;
 }
 
 hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uint8_t* codes,
@@ -480,10 +628,10 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
   }
   if (plan.path == 0) {
     if (fmt == FMT_NVFP4)
-      launch_skinny<FMT_NVFP4>((int)((m + 3) / 4), x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part,
+      launch_decode<FMT_NVFP4>((int)((m + 3) / 4), x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part,
                                cnt_n, plan.splits, stream);
     else
-      launch_skinny<FMT_MXFP4>(1, x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part, cnt_n,
+      launch_decode<FMT_MXFP4>(1, x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part, cnt_n,
                                plan.splits, stream);
   } else {
     const int64_t tiles = ((m + G_BM - 1) / G_BM) * ((n + G_BN - 1) / G_BN);

@@ -214,4 +214,139 @@ __device__ __forceinline__ void skinny_reduce(const SkinnyTileResult& res, float
   __syncthreads();
 }
 
+
+// ---------------------------------------------------------------------------------
+// Decode kernel building blocks.  One wave owns one 16-row weight tile over a
+// K range (split).  Its workgroup first stages, in LDS, the split's x rows and
+// the block-scale bytes of every tile row, then each wave streams its codes
+// through a ring of DEPTH steps of loads in flight: step j is consumed while
+// step j + DEPTH loads.  Per step a lane then issues one 16-byte global load;
+// scales and x come from LDS (a separate counter, so they never wait behind the
+// ring).  Every global load is unconditional (addresses clamped into the
+// tensor) so the compiler can count outstanding loads instead of draining:
+//   * a row past N reads row N - 1; it only feeds output column n, never stored;
+//   * a K group past K or past the split reads the row start; it is consumed
+//     with zero x and a zero scale, so it adds nothing;
+//   * x lanes that carry no row read a 64-byte zero area at the start of LDS.
+// LDS layout: [64 zero bytes][x: M rows x kslice bf16][scales: rows x srow bytes]
+// ---------------------------------------------------------------------------------
+constexpr int DECODE_XS_ZERO = 32;   // bf16 elements of zeros in front of the staged x rows
+
+template <int FMT>
+struct DecodeLds {
+  static constexpr int BLK = FMT == FMT_NVFP4 ? 16 : 32;
+  // bytes of one staged scale row for a split of `kslice` weights, padded to 16
+  __host__ __device__ static int srow_bytes(int kslice) { return ((kslice / BLK) + 15) & ~15; }
+  __host__ __device__ static size_t bytes(int M, int kslice, int rows) {
+    return 2 * (size_t)DECODE_XS_ZERO + 2 * (size_t)M * kslice + (size_t)rows * srow_bytes(kslice);
+  }
+};
+
+// `valid` false: this lane's K group is past K or past the split; it then reads
+// zero x and a zero scale, so the step adds nothing (no branch, see above).
+template <int FMT, int MG>
+__device__ __forceinline__ void decode_step(u32x4_t cw, uint32_t sc, bool valid, const uint16_t* __restrict__ xs,
+                                            int xs_stride, int kl, int lane, int M, f32x4_t* acc, float (*nacc)[4]) {
+  const int i = lane & 15, g = lane >> 4;
+  sc = valid ? sc : 0u;
+  bf16x8_t b[4];
+  if (FMT == FMT_NVFP4) {
+#pragma unroll
+    for (int s = 0; s < 4; s++) b[s] = codes8_to_bf16(cw[s], 1.0f);
+    const float d0 = e4m3_to_f32(sc & 0xFFu), d1 = e4m3_to_f32(sc >> 8);
+#pragma unroll
+    for (int mg = 0; mg < MG; mg++) {
+      // block-diagonal A: lane (i, g) carries x row 4 mg + (i & 3) only when i / 4 == g
+      const int m = 4 * mg + (i & 3);
+      const bool active = valid && (i >> 2) == g && m < M;
+      const uint16_t* xr = active ? xs + DECODE_XS_ZERO + m * xs_stride + kl : xs;
+      u32x4_t xa[4];
+#pragma unroll
+      for (int s = 0; s < 4; s++) xa[s] = *reinterpret_cast<const u32x4_t*>(xr + 8 * s);
+      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[0]), b[0], z, 0, 0, 0);
+      p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[1]), b[1], p0, 0, 0, 0);
+      f32x4_t p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[2]), b[2], z, 0, 0, 0);
+      p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[3]), b[3], p1, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; e++) nacc[mg][e] = __builtin_fmaf(d1, p1[e], __builtin_fmaf(d0, p0[e], nacc[mg][e]));
+    }
+  } else {
+    const float s = e8m0_scale_operand(sc);
+#pragma unroll
+    for (int q = 0; q < 4; q++) b[q] = codes8_to_bf16(cw[q], s);
+    const uint16_t* xr = (valid && i < M) ? xs + DECODE_XS_ZERO + i * xs_stride + kl : xs;
+    u32x4_t xa[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) xa[q] = *reinterpret_cast<const u32x4_t*>(xr + 8 * q);
+#pragma unroll
+    for (int q = 0; q < 4; q++) acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[q]), b[q], acc[0], 0, 0, 0);
+  }
+}
+
+// The code ring of one wave.  After run(), v[mg][e] holds:
+//   NVFP4 -> (m = 4 mg + e, n = lane % 16), complete after the K-group sum,
+//            in lanes 0..15;
+//   MXFP4 -> (m = 4 (lane / 16) + e, n = lane % 16).
+// codes_row must point into the tensor (clamped by the caller).
+template <int FMT, int MG, int DEPTH>
+struct DecodeRing {
+  u32x4_t ring[DEPTH];
+  const uint8_t* codes_row;
+  int64_t k0, K;
+  int nsteps, g;
+
+  __device__ __forceinline__ void load(int j, u32x4_t& c) const {
+    const int64_t k = k0 + (int64_t)j * SK_STEP_K + 32 * g;
+    c = load16(codes_row + ((j < nsteps && k < K) ? k : 0) / 2);     // clamped into the row
+  }
+  __device__ __forceinline__ void prologue(const uint8_t* cr, int64_t k0_, int64_t K_, int nsteps_, int lane) {
+    codes_row = cr; k0 = k0_; K = K_; nsteps = nsteps_; g = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < DEPTH; u++) load(u, ring[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // srow: this lane's staged scale row in LDS.  The scheduling barriers keep
+  // each refill where it is written: without them the scheduler sinks the loads
+  // next to their uses and the ring collapses.
+  __device__ __forceinline__ void run(const uint16_t* __restrict__ xs, int xs_stride, const uint8_t* __restrict__ srow,
+                                      int M, int lane, float (*v)[4]) {
+    f32x4_t acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+    float nacc[MG][4];
+#pragma unroll
+    for (int mg = 0; mg < MG; mg++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) nacc[mg][e] = 0.f;
+    for (int base = 0; base < nsteps; base += DEPTH) {
+#pragma unroll
+      for (int u = 0; u < DEPTH; u++) {
+        const int j = base + u;
+        const int kl = j * SK_STEP_K + 32 * g;                     // k within the split
+        const bool valid = j < nsteps && k0 + kl < K;
+        const int jc = j < nsteps ? j : 0;
+        uint32_t sc;
+        if (FMT == FMT_NVFP4) sc = *reinterpret_cast<const uint16_t*>(srow + (jc * SK_STEP_K + 32 * g) / 16);
+        else sc = srow[(jc * SK_STEP_K + 32 * g) / 32];
+        decode_step<FMT, MG>(ring[u], sc, valid, xs, xs_stride, kl, lane, M, acc, nacc);
+        load(j + DEPTH, ring[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (FMT == FMT_NVFP4) {
+#pragma unroll
+      for (int mg = 0; mg < MG; mg++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          float s = nacc[mg][e];
+          s += __shfl_xor(s, 16, 64);
+          s += __shfl_xor(s, 32, 64);
+          v[mg][e] = s;
+        }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[0][e] = acc[0][e];
+    }
+  }
+};
+
 }  // namespace fp4w

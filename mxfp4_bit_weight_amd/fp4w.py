@@ -186,16 +186,23 @@ def grouped_linear(x: torch.Tensor, row_index: torch.Tensor, expert_offsets: tor
     return y
 
 
-def merge_scales(q: QWeight, deltas: torch.Tensor, in_place: bool = False) -> QWeight:
-    """fp4w_merge_scales: new scales on the format's grid; codes shared (in place)
-    or copied byte for byte into a new tensor; the tensor scale is shared."""
+def merge_scales(q: QWeight, deltas: torch.Tensor, in_place: bool = False,
+                 scales_out: Optional[torch.Tensor] = None) -> QWeight:
+    """fp4w_merge_scales: new scales on the format's grid.  ``in_place``: q's
+    scales are overwritten; ``scales_out``: written there, codes shared;
+    otherwise a new QWeight whose codes are copied byte for byte.  The tensor
+    scale is shared in every case."""
     _need(deltas, torch.float32, "deltas")
     if deltas.numel() != q.scales.numel():
         raise ValueError("one delta per block scale")
-    if in_place:
-        _check(_merge(q.fmt, _ptr(q.scales), _ptr(deltas), q.scales.numel(), _ptr(q.scales), None, None, 0,
+    if in_place or scales_out is not None:
+        dst = q.scales if in_place else scales_out
+        _need(dst, torch.uint8, "scales_out")
+        if dst.numel() != q.scales.numel():
+            raise ValueError("scales_out must hold one byte per block")
+        _check(_merge(q.fmt, _ptr(q.scales), _ptr(deltas), q.scales.numel(), _ptr(dst), None, None, 0,
                       _stream(q.codes.device)), "fp4w_merge_scales")
-        return q
+        return q if in_place else QWeight(q.fmt, q.codes, dst, q.tensor_scale, q.n, q.k)
     new = QWeight(q.fmt, torch.empty_like(q.codes), torch.empty_like(q.scales), q.tensor_scale, q.n, q.k)
     _check(_merge(q.fmt, _ptr(q.scales), _ptr(deltas), q.scales.numel(), _ptr(new.scales), _ptr(q.codes),
                   _ptr(new.codes), q.codes.numel(), _stream(q.codes.device)), "fp4w_merge_scales")

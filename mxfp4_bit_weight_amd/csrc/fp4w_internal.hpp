@@ -27,12 +27,32 @@ constexpr int kCounterSlots = 2048;
 constexpr int kLoraSlots = 16;
 constexpr int kTileSlots = kCounterSlots - kLoraSlots;
 
+// Decode kernel on the block-scaled matrix core (decode.hip): a workgroup of
+// `nw` waves per tile of 16 weight rows, `splits` slices of K of `sps`
+// 128-wide steps, a ring of `depth` code loads per wave.
+struct DecodeConfig {
+  int nw;
+  int splits;
+  int sps;
+  int depth;
+};
+bool decode_f8f4_supports(int fmt, int64_t m);
+DecodeConfig plan_decode_f8f4(int fmt, int64_t m, int64_t n, int64_t k, int r);
+size_t decode_f8f4_lds_bytes(int fmt, int64_t m, int kslice, int nw, int r);
+// tp: LoRA partials [parts][m][r] fp32 (x A^T per K chunk), or nullptr
+hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c, const void* x, int64_t m, int64_t k,
+                              const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t n,
+                              const float* tp, int parts, const void* lb, int r, void* y, float* part,
+                              uint32_t* cnt, hipStream_t stream);
+int lora_part_count(int64_t k);
+
 struct LinearPlan {
-  int path;            // 0 = skinny (m <= 16), 1 = GEMM
-  int splits;          // K splits of the skinny kernel (1 = none)
+  int path;            // 0 = decode on the block-scaled MFMA, 2 = decode on bf16 MFMA, 1 = GEMM
+  DecodeConfig dq;     // path 0
+  int splits;          // K splits of the decode kernel (1 = none)
   int lora_parts;      // K slices of the LoRA down-projection (0 = no LoRA)
   size_t off_t;        // workspace offset of t partials: [lora_parts][m][r] fp32
-  size_t off_part;     // workspace offset of split-K partials: [splits][n][m] fp32
+  size_t off_part;     // workspace offset of split-K partials (fp32)
   size_t off_count;    // workspace offset of per-row-tile arrival counters: [n/16] u32
   size_t bytes;        // total workspace bytes
 };

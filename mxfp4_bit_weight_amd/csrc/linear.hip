@@ -16,57 +16,9 @@
 #include "fp4w_device.hpp"
 #include "fp4w_internal.hpp"
 #include "skinny.hpp"
+#include "sync.hpp"
 
 namespace fp4w {
-
-// ---------------------------------------------------------------------------------
-// Cross-workgroup partial sums.  Partials are stored and loaded as relaxed
-// agent-scope atomics: on gfx950 these are emitted with the SC1 bit, which makes
-// them coherent across the XCDs' separate L2s without an L2-wide writeback or
-// invalidate (a __threadfence() costs both, on every workgroup).  The writer
-// waits for its stores to complete (s_waitcnt) before it increments the arrival
-// counter, and the reader issues its loads only after the increment returned,
-// so the last arrival sees every partial.
-// ---------------------------------------------------------------------------------
-__device__ __forceinline__ void store_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_stores_complete() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// Workgroup version: every thread calls it after storing its partials; returns
-// true in all threads of the last workgroup to arrive (which resets the counter).
-__device__ __forceinline__ bool arrive_last(uint32_t* cnt, uint32_t expected, int* flag_lds) {
-  wait_stores_complete();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bool last = old == expected - 1u;
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag_lds = last ? 1 : 0;
-  }
-  __syncthreads();
-  return *flag_lds != 0;
-}
-
-// Wave version: every lane calls it after storing its partials.
-__device__ __forceinline__ bool wave_arrive_last(uint32_t* cnt, uint32_t expected, int lane) {
-  wait_stores_complete();
-  uint32_t old = 0;
-  if (lane == 0) {
-    old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == expected - 1u) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  old = (uint32_t)__shfl((int)old, 0, 64);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  return old == expected - 1u;
-}
 
 // ---------------------------------------------------------------------------------
 // LoRA down-projection t = x A^T.  Workgroup (m-tile of 16 rows, K slice p);
@@ -140,6 +92,69 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restri
     t[mm * r + j] = s;
   }
 }
+
+// ---------------------------------------------------------------------------------
+// LoRA down-projection for the decode path (m <= 16): partials only.  Workgroup p
+// owns 4 * SPW consecutive 32-wide K steps (each wave SPW of them, every load in
+// flight at once) and writes tp[p] = x[:, chunk p] A[:, chunk p]^T (m x r fp32).
+// The decode kernel adds the partials in chunk order while it stages, so no
+// arrival counter and no second pass are needed here.
+// ---------------------------------------------------------------------------------
+constexpr int LP_SPW = 8;
+constexpr int LP_STEPS = 4 * LP_SPW;      // 32-wide K steps per workgroup
+
+template <int RB>
+__global__ __launch_bounds__(256) void lora_part_kernel(const uint16_t* __restrict__ x, int M, int64_t K,
+                                                        const uint16_t* __restrict__ a, int r,
+                                                        float* __restrict__ tp) {
+  __shared__ float red[4 * RB * 4 * 64];
+  const int p = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 15, g = lane >> 4;
+  const int64_t step0 = ((int64_t)p * 4 + wave) * LP_SPW;
+  const bool xrow_ok = li < M;
+  u32x4_t xa[LP_SPW], av[LP_SPW][RB];
+#pragma unroll
+  for (int s = 0; s < LP_SPW; s++) {
+    const int64_t k = (step0 + s) * 32 + 8 * g;
+    const bool kin = k < K;
+    const int64_t kc = kin ? k : 0;
+    xa[s] = load16(x + (xrow_ok ? (int64_t)li * K : 0) + kc);
+    if (!(kin && xrow_ok)) xa[s] = (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int b = 0; b < RB; b++) {
+      const int j = b * 16 + li;
+      av[s][b] = load16(a + (j < r ? (int64_t)j * K : 0) + kc);
+      if (!(kin && j < r)) av[s][b] = (u32x4_t){0u, 0u, 0u, 0u};
+    }
+  }
+  f32x4_t acc[RB];
+#pragma unroll
+  for (int b = 0; b < RB; b++) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < LP_SPW; s++)
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[s]), as_bf16x8(av[s][b]), acc[b], 0, 0, 0);
+  // D row 4 g + i = m, column li = j within block b
+#pragma unroll
+  for (int b = 0; b < RB; b++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) red[((wave * RB + b) * 4 + i) * 64 + lane] = acc[b][i];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float v = ((red[((0 * RB + b) * 4 + i) * 64 + lane] + red[((1 * RB + b) * 4 + i) * 64 + lane]) +
+                         red[((2 * RB + b) * 4 + i) * 64 + lane]) + red[((3 * RB + b) * 4 + i) * 64 + lane];
+        const int m = 4 * g + i, j = b * 16 + li;
+        if (m < M && j < r) tp[((int64_t)p * M + m) * r + j] = v;
+      }
+  }
+}
+
+int lora_part_count(int64_t k) { return (int)(((k + 31) / 32 + LP_STEPS - 1) / LP_STEPS); }
 
 // ---------------------------------------------------------------------------------
 // Decode-shaped linear (m <= 16).
@@ -539,20 +554,34 @@ static int decode_splits_for(int64_t m, int64_t n, int64_t k) {
 
 LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
   LinearPlan p{};
-  p.path = m <= 16 ? 0 : 1;
-  p.lora_parts = r > 0 ? lora_parts_for(m, k) : 0;
-  p.splits = p.path == 0 ? decode_splits_for(m, n, k) : 1;
-  if (p.splits > 1 && (n + SK_TILE_N - 1) / SK_TILE_N > kTileSlots) p.path = 1;   // counters would not fit
+  p.path = m > 16 ? 1 : decode_f8f4_supports(FMT_NVFP4, m) ? 0 : 2;
+  // decode path: per-chunk LoRA partials, summed by the decode kernel
+  p.lora_parts = r <= 0 ? 0 : p.path == 0 ? lora_part_count(k) : lora_parts_for(m, k);
+  size_t part_floats = 0;
+  if (p.path == 0) {
+    // one plan for both formats: the NVFP4 layout is never smaller
+    p.dq = plan_decode_f8f4(FMT_NVFP4, m, n, k, r);
+    p.splits = p.dq.splits;
+    const int64_t tiles = (n + SK_TILE_N - 1) / SK_TILE_N;
+    if (p.splits > 1 && tiles > kTileSlots) p.path = 1;                       // counters would not fit
+    part_floats = (size_t)p.splits * tiles * SK_TILE_N * m;
+  } else if (p.path == 2) {
+    p.splits = decode_splits_for(m, n, k);
+    if (p.splits > 1 && (n + SK_TILE_N - 1) / SK_TILE_N > kTileSlots) p.path = 1;
+    part_floats = (size_t)p.splits * n * m;
+  }
+  if (p.path == 1) p.splits = 1;
   size_t off = 0;
   p.off_count = off;
   off += sizeof(uint32_t) * kCounterSlots;
   p.off_t = off;
   if (r > 0) {
     off += align256(sizeof(float) * (size_t)m * (size_t)r);                           // t
-    if (p.lora_parts > 1) off += align256(sizeof(float) * (size_t)p.lora_parts * m * r);   // partials
+    if (p.lora_parts > 1 || p.path == 0)
+      off += align256(sizeof(float) * (size_t)p.lora_parts * m * r);                  // partials
   }
   p.off_part = off;
-  if (p.splits > 1) off += align256(sizeof(float) * (size_t)p.splits * (size_t)n * (size_t)m);
+  if (p.splits > 1) off += align256(sizeof(float) * part_floats);
   p.bytes = off;
   return p;
 }
@@ -611,13 +640,23 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   const bool has_lora = r > 0 && lora_a && lora_b;
   float* t = has_lora ? reinterpret_cast<float*>(ws + plan.off_t) : nullptr;
-  float* tp = (has_lora && plan.lora_parts > 1)
+  float* tp = (has_lora && (plan.lora_parts > 1 || plan.path == 0))
                   ? reinterpret_cast<float*>(ws + plan.off_t + align256(sizeof(float) * (size_t)m * r))
                   : nullptr;
   float* part = reinterpret_cast<float*>(ws + plan.off_part);
   uint32_t* cnt_m = reinterpret_cast<uint32_t*>(ws + plan.off_count);
   uint32_t* cnt_n = cnt_m + kLoraSlots;
-  if (has_lora) {
+  if (has_lora && plan.path == 0) {
+    const int P = plan.lora_parts;
+    const uint16_t* xx = reinterpret_cast<const uint16_t*>(x);
+    const uint16_t* aa = reinterpret_cast<const uint16_t*>(lora_a);
+    switch ((r + 15) / 16) {
+      case 1: hipLaunchKernelGGL(lora_part_kernel<1>, dim3(P), dim3(256), 0, stream, xx, (int)m, k, aa, r, tp); break;
+      case 2: hipLaunchKernelGGL(lora_part_kernel<2>, dim3(P), dim3(256), 0, stream, xx, (int)m, k, aa, r, tp); break;
+      case 3: hipLaunchKernelGGL(lora_part_kernel<3>, dim3(P), dim3(256), 0, stream, xx, (int)m, k, aa, r, tp); break;
+      default: hipLaunchKernelGGL(lora_part_kernel<4>, dim3(P), dim3(256), 0, stream, xx, (int)m, k, aa, r, tp); break;
+    }
+  } else if (has_lora) {
     const int64_t nsteps = (k + 31) / 32;
     const int P = plan.lora_parts;
     const int spp = (int)((nsteps + P - 1) / P);
@@ -627,6 +666,10 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
                        spp, tp, t, cnt_m);
   }
   if (plan.path == 0) {
+    hipError_t e = launch_decode_f8f4(fmt, plan.dq, x, m, k, codes, scales, tensor_scale, n, tp, plan.lora_parts,
+                                      lora_b, r, y, part, cnt_n, stream);
+    if (e != hipSuccess) return e;
+  } else if (plan.path == 2) {
     if (fmt == FMT_NVFP4)
       launch_decode<FMT_NVFP4>((int)((m + 3) / 4), x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part,
                                cnt_n, plan.splits, stream);

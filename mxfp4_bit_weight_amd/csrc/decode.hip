@@ -449,7 +449,7 @@ DecodeConfig plan_decode_f8f4(int fmt, int64_t m, int64_t n, int64_t k, int r) {
   const int64_t ntiles = (n + DQ_ROWS - 1) / DQ_ROWS;
   const int64_t nsteps = (k + DQ_STEP - 1) / DQ_STEP;
   c.nw = ntiles * 4 >= kDqTargetWaves ? 4 : ntiles * 8 >= kDqTargetWaves ? 8 : 16;
-  if (m >= 3 && c.nw > 8) c.nw = 8;     // several MFMA chains per wave: 1024-thread groups would spill
+  if (m >= 2 && c.nw > 8) c.nw = 8;     // several MFMA chains per wave: 1024-thread groups would spill
   auto sps_for = [&](int64_t s) {
     int64_t sps = (nsteps + s - 1) / s;
     if (s > 1) sps = (sps + 3) & ~(int64_t)3;                         // 16-byte aligned scale slices
@@ -477,9 +477,9 @@ static void launch_nq(const DecodeConfig& c, dim3 grid, size_t lds, hipStream_t 
                      scales, ts, n, tp, parts, lb, r, y, part, cnt, c.splits, c.sps, nsteps, ntiles, scales16)
   if (c.nw == 4) {
     if (c.depth <= 8) FP4W_DQ(4, 8); else FP4W_DQ(4, 16);
-  } else if (c.nw == 8 || NQ > 2) {
+  } else if (c.nw == 8 || (FMT == FMT_NVFP4 && NQ > 1)) {
     if (c.depth <= 8) FP4W_DQ(8, 8); else FP4W_DQ(8, 16);
-  } else if constexpr (NQ <= 2) {
+  } else if constexpr (FMT == FMT_MXFP4 || NQ == 1) {
     if (c.depth <= 8) FP4W_DQ(16, 8); else FP4W_DQ(16, 16);
   }
 #undef FP4W_DQ
@@ -491,7 +491,7 @@ hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c0, const void* x, in
                               uint32_t* cnt, hipStream_t stream) {
   DecodeConfig c = c0;
   const int nq = fmt == FMT_NVFP4 ? (int)m : (int)((m + 7) / 8);
-  if (nq > 2 && c.nw > 8) c.nw = 8;      // 16-wave groups only for one or two MFMA chains (else they spill)
+  if (fmt == FMT_NVFP4 && nq > 1 && c.nw > 8) c.nw = 8;   // 16-wave groups only for one chain (else they spill)
   const int blk = fmt == FMT_NVFP4 ? 16 : 32;
   const int ntiles = (int)((n + DQ_ROWS - 1) / DQ_ROWS);
   const int nsteps = (int)((k + DQ_STEP - 1) / DQ_STEP);

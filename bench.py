@@ -5,11 +5,14 @@ gate/up, 3584x18944 down, 3584x3584 qkv-o) at M = 1 through ``fp4w.linear``
 with NVFP4 weights and a rank-16 LoRA, on weights rotated over more than 1 GiB
 of distinct copies so that every call streams its weights from HBM.  ``value``
 is the step's algorithmic bytes over its time (GB/s).  The JSON line also holds
-the roofline of the decode kernel (HIP events around each launch), the CPU
-oracle timed on a bounded sample, and the other hot-path rows (M = 8, MXFP4,
-the 16384-row prefill GEMM, quantize, merge, dequantize, grouped MoE).
+the roofline of the decode kernel (HIP events around a graph of back-to-back
+launches of it), the CPU oracle timed on a bounded sample, and the other
+hot-path rows (M = 8, MXFP4, the 16384-row prefill GEMM, quantize, merge,
+dequantize, grouped MoE).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-rows]
+       python bench.py --roofline-only   (the decode kernel's launches and a plain
+                                          copy of known size, for profiler runs)
 Progress goes to stderr; stdout is exactly one JSON line.
 """
 import argparse
@@ -40,6 +43,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--skip-rows", action="store_true", help="only the headline step and its roofline")
+    p.add_argument("--roofline-only", action="store_true",
+                   help="only the roofline launches of the decode kernel and a copy kernel of known size")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
     return p.parse_args()
 
@@ -101,23 +106,6 @@ def main():
         sync()
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
-
-    def time_per_launch(fn, steps, warmup):
-        """Average duration of single-launch calls, from an event pair around each.
-        A sleep kernel at the head of the stream lets the host queue every event and
-        launch before the GPU reaches them, so host latency is not timed."""
-        for i in range(warmup):
-            fn(i)
-        sync()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        torch.cuda._sleep(int(2.4e9 * 0.05))          # about 50 ms of queue head start
-        for i, (a, b) in enumerate(evs):
-            a.record()
-            fn(warmup + i)
-            b.record()
-        sync()
-        d = np.array([a.elapsed_time(b) for a, b in evs])
-        return float(d.mean()), float(np.median(d))
 
     def time_graph(fn, steps, warmup):
         """Capture `warmup` and `steps` calls of fn into two HIP graphs and time the
@@ -183,13 +171,17 @@ def main():
             fp4w.linear(d["x1"], q, a, b, out=ys[name][:1], workspace=ws)
 
     step_bytes = sum(linear_bytes(0, 1, n, k, rank) for n, k in shapes.values())
-    ms_step, wall = time_graph(step, args.steps, args.warmup)
+    if args.roofline_only:
+        ms_step, wall, ms_eager = float("nan"), 0.0, float("nan")
+    else:
+        ms_step, wall = time_graph(step, args.steps, args.warmup)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    log(f"[bench] step (graph replay): {ms_step * 1e3:.2f} us, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of peak)")
-    ms_eager, _ = time_loop(step, args.steps, args.warmup)
-    log(f"[bench] step (eager launches): {ms_eager * 1e3:.2f} us")
+    if not args.roofline_only:
+        log(f"[bench] step (graph replay): {ms_step * 1e3:.2f} us, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of peak)")
+        ms_eager, _ = time_loop(step, args.steps, args.warmup)
+        log(f"[bench] step (eager launches): {ms_eager * 1e3:.2f} us")
 
-    # ---- roofline: the decode kernel alone (gate/up, M = 1, no LoRA: one launch) --------
+    # ---- roofline: the decode kernel alone (gate/up, M = 1, no LoRA: one launch per call) -
     dg = decode[(0, "gate_up")]
     n, k = dg["n"], dg["k"]
 
@@ -197,15 +189,26 @@ def main():
         q, _, _ = dg["qs"][i % len(dg["qs"])]
         fp4w.linear(dg["x1"], q, out=ys["gate_up"][:1], workspace=ws)
 
-    per_launch_ms, med_ms = time_per_launch(gemv_only, max(args.steps, 100), args.warmup)
+    launches = max(args.steps, 100)
+    per_launch_ms, _ = time_graph(gemv_only, launches, args.warmup)
     gemv_bytes = linear_bytes(0, 1, n, k, 0)
     achieved = gemv_bytes / (per_launch_ms * 1e-3) / 1e9
-    roofline = {"kernel": "linear_skinny_kernel<NVFP4, 1 m-group> on (18944, 3584), M=1",
+    roofline = {"kernel": "decode_f8f4_kernel<NVFP4, 1 row, 4 waves, ring 8> on W (18944, 3584), M=1",
                 "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(gemv_bytes),
-                "avg_launch_us": round(per_launch_ms * 1e3, 3), "median_launch_us": round(med_ms * 1e3, 3),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(),
+                "avg_launch_us": round(per_launch_ms * 1e3, 3), "launches_timed": launches,
+                "timing": "HIP events around a graph of back-to-back launches (weights rotated over >1 GiB)",
                 "algorithmic_bytes_per_launch": gemv_bytes}
     log(f"[bench] decode kernel alone: {per_launch_ms * 1e3:.2f} us/launch, {achieved:.1f} GB/s")
+    if args.roofline_only:
+        # a plain copy of known size: the scale of the profiler's FETCH_SIZE / WRITE_SIZE
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        sync()
+        print(json.dumps({"roofline": roofline, "copy_kernel_bytes": src.numel()}), flush=True)
+        return
 
     rows = {}
     if not args.skip_rows:
@@ -228,10 +231,10 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def pmc_traffic(alg_bytes):
+def pmc_traffic():
     """HBM bytes per launch of the decode kernel from the committed rocprofv3 --pmc
     summary, if it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "skinny_gate_up_m1_pmc.txt")
+    path = os.path.join(ROOT, "profiles", "decode_gate_up_m1_nvfp4_pmc.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -247,9 +250,12 @@ def pmc_traffic(alg_bytes):
         return None
 
 
+KERNEL_SOURCES = ("decode.hip", "xenc.hpp", "sync.hpp", "fp4w_device.hpp", "fp4w_internal.hpp")
+
+
 def kernel_sources_sha256():
     h = hashlib.sha256()
-    for f in ("skinny.hpp", "linear.hip", "fp4w_device.hpp"):
+    for f in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, "mxfp4_bit_weight_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 

@@ -105,11 +105,11 @@ int fp4w_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
 /*
  * Workspace for fp4w_linear, in bytes, for x (m, k), W (n, k) and LoRA rank r
  * (0 when there is no LoRA); 0 for invalid arguments.  It holds the LoRA
- * intermediate t = x A^T (fp32), split-K partial sums and, in its first
- * 8 KiB at fixed offsets, arrival counters.  The counters must be zero before
- * the first call: zero-fill a new workspace once; every call returns its
- * counters to zero when it completes, so one workspace serves calls of any
- * shape in stream order.
+ * intermediate t = x A^T (fp32) or its per-chunk partials, split-K partial sums
+ * and, in its first 8 KiB at fixed offsets, arrival counters.  The counters
+ * must be zero before the first call: zero-fill a new workspace once; every call
+ * returns its counters to zero when it completes, so one workspace serves calls
+ * of any shape in stream order.
  */
 size_t fp4w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
 
@@ -123,10 +123,19 @@ size_t fp4w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
  *              (both NULL or r == 0: no LoRA; any LoRA scaling is folded into B)
  *   y_bf16     (m, n) bf16, rounded once from the fp32 result
  *   workspace  >= fp4w_linear_workspace_bytes(m, n, k, r) bytes, see above
- * Launches: with a LoRA, first the down-projection t = x A^T (fp32); then for
- * m <= 16 the decode-shaped kernel (HBM-bound, split over K when n is small),
- * for m > 16 the LDS-staged bf16 MFMA GEMM.  The LoRA product is added in fp32
- * (GEMM: t is split into two bf16 parts for the matrix cores).
+ * Launches (all on `stream`):
+ *  - m <= 8: with a LoRA, a kernel writing per-chunk
+ *    partials of t = x A^T; then the decode kernel on gfx950's block-scaled
+ *    MFMA, which feeds the codes to the matrix core as stored and x as two E4M3
+ *    terms per element under an E8M0 scale per 32 elements.  That split is exact
+ *    for every element within 2^13 of its block's largest magnitude; smaller
+ *    ones are off by at most 2^-21 of that maximum.  A non-finite x element
+ *    makes every output of its row NaN.
+ *  - 8 < m <= 16: the LoRA down-projection, then a decode kernel on the
+ *    bf16 MFMA (codes dequantized exactly to bf16 in registers).
+ *  - m > 16: the LoRA down-projection, then the LDS-staged bf16 MFMA GEMM.
+ * The LoRA product is added in fp32 (GEMM: t split into two bf16 parts for the
+ * matrix cores).
  */
 int fp4w_linear(int fmt, const void *x_bf16, int64_t m, int64_t k,
                 const uint8_t *codes, const uint8_t *scales, const float *tensor_scale,

@@ -311,20 +311,23 @@ __global__ __launch_bounds__(64 * WPW) void linear_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------------
-// GEMM (m > 16): 256 x 256 output tile per workgroup, K tile 64, 4 waves in a
-// 2 x 2 grid of 128 x 128, v_mfma_f32_16x16x32_bf16.  Each K tile of x is
-// copied to LDS, each K tile of W is loaded as codes and dequantized once into
-// LDS as exact bf16 (e2m1 * dec(sb); the tensor scale is applied at the end).
-// The next tile's global loads are in flight while the current one is used.
+// GEMM (m > 16): 256 x 256 output tile per workgroup, K tile 64, 8 waves in a
+// 4 x 2 grid of 64 x 128, v_mfma_f32_16x16x32_bf16; two waves per SIMD, so one
+// wave's LDS reads, loads and dequantization run under the other's MFMAs.  Each
+// K tile of x is copied to LDS, each K tile of W is loaded as codes and
+// dequantized once into LDS as exact bf16 (e2m1 * dec(sb) has at most 6
+// significant bits; the tensor scale is applied at the end).  The next tile's
+// global loads are in flight while the current one is used.
 // ---------------------------------------------------------------------------------
 constexpr int G_BM = 256, G_BN = 256, G_BK = 64;
 constexpr int G_LDA = G_BK + 8;   // bf16 elements per LDS row (16 bytes of padding)
+constexpr int G_THREADS = 512;
 
 template <int FMT>
 struct GemmStage {
-  u32x4_t xv[8];     // 8 x 16 bytes of x
-  u32x4_t cv[2];     // 2 x 16 bytes of codes (two 32-code halves)
-  uint32_t sv[2];    // their scale bytes
+  u32x4_t xv[4];     // 4 x 16 bytes of x
+  u32x4_t cv;        // 16 bytes of codes (32 codes of one row)
+  uint32_t sv;       // their scale bytes (NVFP4: two, MXFP4: one)
 };
 
 template <int FMT>
@@ -333,74 +336,68 @@ __device__ __forceinline__ void gemm_load(GemmStage<FMT>& st, const uint16_t* __
                                           const uint8_t* __restrict__ scales, int64_t N, int64_t m0, int64_t n0,
                                           int64_t k0) {
   const int tid = threadIdx.x;
-  // x: 256 rows x 64 bf16 = 2048 chunks of 16 B; thread handles rows tid/8 + 32 i, chunk tid % 8
+  // x: 256 rows x 64 bf16 = 2048 chunks of 16 B; thread handles rows tid/8 + 64 i, chunk tid % 8
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int64_t mr = m0 + (tid >> 3) + 32 * i;
+  for (int i = 0; i < 4; i++) {
+    const int64_t mr = m0 + (tid >> 3) + 64 * i;
     const int64_t k = k0 + 8 * (tid & 7);
-    st.xv[i] = (u32x4_t){0u, 0u, 0u, 0u};
-    if (mr < M && k < K) st.xv[i] = load16(x + mr * K + k);
+    const bool ok = mr < M && k < K;
+    st.xv[i] = load16(x + (ok ? mr * K + k : 0));
+    if (!ok) st.xv[i] = (u32x4_t){0u, 0u, 0u, 0u};
   }
-  // W: 256 rows x 64 codes = 512 chunks of 32 codes; thread handles rows tid/2 and tid/2 + 128
+  // W: 256 rows x 64 codes = 512 chunks of 32 codes; thread handles row tid/2, half tid % 2
   const int64_t blk = (FMT == FMT_NVFP4) ? 16 : 32;
-#pragma unroll
-  for (int h = 0; h < 2; h++) {
-    const int64_t nr = n0 + (tid >> 1) + 128 * h;
-    const int64_t k = k0 + 32 * (tid & 1);
-    st.cv[h] = (u32x4_t){0u, 0u, 0u, 0u};
-    st.sv[h] = 0u;
-    if (nr < N && k < K) {
-      st.cv[h] = load16(codes + nr * (K / 2) + k / 2);
-      if (FMT == FMT_NVFP4) st.sv[h] = *reinterpret_cast<const uint16_t*>(scales + nr * (K / blk) + k / blk);
-      else st.sv[h] = scales[nr * (K / blk) + k / blk];
-    }
-  }
+  const int64_t nr = n0 + (tid >> 1);
+  const int64_t k = k0 + 32 * (tid & 1);
+  const bool ok = nr < N && k < K;
+  const int64_t nrc = ok ? nr : 0, kc = ok ? k : 0;
+  st.cv = load16(codes + nrc * (K / 2) + kc / 2);
+  if (FMT == FMT_NVFP4) st.sv = *reinterpret_cast<const uint16_t*>(scales + nrc * (K / blk) + kc / blk);
+  else st.sv = scales[nrc * (K / blk) + kc / blk];
+  if (!ok) { st.cv = (u32x4_t){0u, 0u, 0u, 0u}; st.sv = 0u; }
 }
 
 template <int FMT>
 __device__ __forceinline__ void gemm_store_lds(const GemmStage<FMT>& st, uint16_t* sa, uint16_t* sb) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int rr = (tid >> 3) + 32 * i, c = 8 * (tid & 7);
+  for (int i = 0; i < 4; i++) {
+    const int rr = (tid >> 3) + 64 * i, c = 8 * (tid & 7);
     *reinterpret_cast<u32x4_t*>(sa + rr * G_LDA + c) = st.xv[i];
   }
+  const int rr = tid >> 1, c = 32 * (tid & 1);
+  u32x4_t o[4];
+  if (FMT == FMT_NVFP4) {
+    const float d0 = e4m3_to_f32(st.sv & 0xFFu), d1 = e4m3_to_f32((st.sv >> 8) & 0xFFu);
 #pragma unroll
-  for (int h = 0; h < 2; h++) {
-    const int rr = (tid >> 1) + 128 * h, c = 32 * (tid & 1);
-    u32x4_t o[4];
-    if (FMT == FMT_NVFP4) {
-      const float d0 = e4m3_to_f32(st.sv[h] & 0xFFu), d1 = e4m3_to_f32(st.sv[h] >> 8);
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const float d = q < 2 ? d0 : d1;
-        const uint32_t dw = st.cv[h][q];
-        f32x2_t a0 = fp4x2_to_f32x2<0>(dw, 1.0f), a1 = fp4x2_to_f32x2<1>(dw, 1.0f);
-        f32x2_t a2 = fp4x2_to_f32x2<2>(dw, 1.0f), a3 = fp4x2_to_f32x2<3>(dw, 1.0f);
-        // e2m1 * dec(sb) has at most 6 significant bits: exact in fp32 and in bf16
-        o[q].x = (__float_as_uint(a0.x * d) >> 16) | (__float_as_uint(a0.y * d) & 0xFFFF0000u);
-        o[q].y = (__float_as_uint(a1.x * d) >> 16) | (__float_as_uint(a1.y * d) & 0xFFFF0000u);
-        o[q].z = (__float_as_uint(a2.x * d) >> 16) | (__float_as_uint(a2.y * d) & 0xFFFF0000u);
-        o[q].w = (__float_as_uint(a3.x * d) >> 16) | (__float_as_uint(a3.y * d) & 0xFFFF0000u);
-      }
-    } else {
-      const float s = e8m0_scale_operand(st.sv[h]);
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const uint32_t dw = st.cv[h][q];
-        o[q].x = fp4x2_to_bf16x2_scaled<0>(dw, s);
-        o[q].y = fp4x2_to_bf16x2_scaled<1>(dw, s);
-        o[q].z = fp4x2_to_bf16x2_scaled<2>(dw, s);
-        o[q].w = fp4x2_to_bf16x2_scaled<3>(dw, s);
-      }
+    for (int q = 0; q < 4; q++) {
+      const float d = q < 2 ? d0 : d1;
+      const uint32_t dw = st.cv[q];
+      f32x2_t a0 = fp4x2_to_f32x2<0>(dw, 1.0f), a1 = fp4x2_to_f32x2<1>(dw, 1.0f);
+      f32x2_t a2 = fp4x2_to_f32x2<2>(dw, 1.0f), a3 = fp4x2_to_f32x2<3>(dw, 1.0f);
+      // e2m1 * dec(sb) has at most 6 significant bits: exact in fp32 and in bf16
+      o[q].x = (__float_as_uint(a0.x * d) >> 16) | (__float_as_uint(a0.y * d) & 0xFFFF0000u);
+      o[q].y = (__float_as_uint(a1.x * d) >> 16) | (__float_as_uint(a1.y * d) & 0xFFFF0000u);
+      o[q].z = (__float_as_uint(a2.x * d) >> 16) | (__float_as_uint(a2.y * d) & 0xFFFF0000u);
+      o[q].w = (__float_as_uint(a3.x * d) >> 16) | (__float_as_uint(a3.y * d) & 0xFFFF0000u);
     }
+  } else {
+    const float sc = e8m0_scale_operand(st.sv);
 #pragma unroll
-    for (int q = 0; q < 4; q++) *reinterpret_cast<u32x4_t*>(sb + rr * G_LDA + c + 8 * q) = o[q];
+    for (int q = 0; q < 4; q++) {
+      const uint32_t dw = st.cv[q];
+      o[q].x = fp4x2_to_bf16x2_scaled<0>(dw, sc);
+      o[q].y = fp4x2_to_bf16x2_scaled<1>(dw, sc);
+      o[q].z = fp4x2_to_bf16x2_scaled<2>(dw, sc);
+      o[q].w = fp4x2_to_bf16x2_scaled<3>(dw, sc);
+    }
   }
+#pragma unroll
+  for (int q = 0; q < 4; q++) *reinterpret_cast<u32x4_t*>(sb + rr * G_LDA + c + 8 * q) = o[q];
 }
 
 template <int FMT>
-__global__ __launch_bounds__(256, 1) void linear_gemm_kernel(
+__global__ __launch_bounds__(G_THREADS, 2) void linear_gemm_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t N,
     const float* __restrict__ t, const uint16_t* __restrict__ lora_b, int r, uint16_t* __restrict__ y) {
@@ -413,12 +410,13 @@ __global__ __launch_bounds__(256, 1) void linear_gemm_kernel(
   const int64_t m0 = (int64_t)tm * G_BM, n0 = (int64_t)tn * G_BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int li = lane & 15, g = lane >> 4;
+  constexpr int TI = 4, TJ = 8;                  // 16 x 16 sub-tiles of the wave's 64 x 128
 
-  f32x4_t acc[8][8];
+  f32x4_t acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 8; i++)
+  for (int i = 0; i < TI; i++)
 #pragma unroll
-    for (int j = 0; j < 8; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TJ; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (int)((K + G_BK - 1) / G_BK);
   GemmStage<FMT> stage;
@@ -432,17 +430,17 @@ __global__ __launch_bounds__(256, 1) void linear_gemm_kernel(
     const uint16_t* b = sB0 + cur * (G_BN * G_LDA);
 #pragma unroll
     for (int kk = 0; kk < G_BK / 32; kk++) {
-      bf16x8_t af[8], bfr[8];
+      bf16x8_t af[TI], bfr[TJ];
 #pragma unroll
-      for (int i = 0; i < 8; i++)
-        af[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(a + (wm * 128 + i * 16 + li) * G_LDA + kk * 32 + 8 * g));
+      for (int i = 0; i < TI; i++)
+        af[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(a + (wm * 64 + i * 16 + li) * G_LDA + kk * 32 + 8 * g));
 #pragma unroll
-      for (int j = 0; j < 8; j++)
+      for (int j = 0; j < TJ; j++)
         bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(b + (wn * 128 + j * 16 + li) * G_LDA + kk * 32 + 8 * g));
 #pragma unroll
-      for (int i = 0; i < 8; i++)
+      for (int i = 0; i < TI; i++)
 #pragma unroll
-        for (int j = 0; j < 8; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TJ; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) gemm_store_lds<FMT>(stage, sA0 + (cur ^ 1) * (G_BM * G_LDA), sB0 + (cur ^ 1) * (G_BN * G_LDA));
     __syncthreads();
@@ -452,9 +450,9 @@ __global__ __launch_bounds__(256, 1) void linear_gemm_kernel(
   // K' = [t_hi | t_lo] (t split into two bf16 parts) against [B | B].
   const float st = (FMT == FMT_NVFP4) ? *tensor_scale : 1.0f;
 #pragma unroll
-  for (int i = 0; i < 8; i++)
+  for (int i = 0; i < TI; i++)
 #pragma unroll
-    for (int j = 0; j < 8; j++)
+    for (int j = 0; j < TJ; j++)
 #pragma unroll
       for (int e = 0; e < 4; e++) acc[i][j][e] *= st;
   if (t) {
@@ -464,10 +462,10 @@ __global__ __launch_bounds__(256, 1) void linear_gemm_kernel(
       // covers entries 8g..8g+7 -> part (g >> 1) of LoRA index jb + 8 (g & 1) + e
       const int jj = jb + 8 * (g & 1);
       const bool lo_part = (g >> 1) != 0;
-      bf16x8_t tf[8], bfv[8];
+      bf16x8_t tf[TI], bfv[TJ];
 #pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const int64_t mr = m0 + wm * 128 + i * 16 + li;
+      for (int i = 0; i < TI; i++) {
+        const int64_t mr = m0 + wm * 64 + i * 16 + li;
         u32x4_t v = {0u, 0u, 0u, 0u};
         if (mr < M) {
           uint32_t h[8];
@@ -484,7 +482,7 @@ __global__ __launch_bounds__(256, 1) void linear_gemm_kernel(
         tf[i] = as_bf16x8(v);
       }
 #pragma unroll
-      for (int j2 = 0; j2 < 8; j2++) {
+      for (int j2 = 0; j2 < TJ; j2++) {
         const int64_t nr = n0 + wn * 128 + j2 * 16 + li;
         u32x4_t v = {0u, 0u, 0u, 0u};
         if (nr < N) {
@@ -500,20 +498,20 @@ __global__ __launch_bounds__(256, 1) void linear_gemm_kernel(
         bfv[j2] = as_bf16x8(v);
       }
 #pragma unroll
-      for (int i = 0; i < 8; i++)
+      for (int i = 0; i < TI; i++)
 #pragma unroll
-        for (int j2 = 0; j2 < 8; j2++) acc[i][j2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf[i], bfv[j2], acc[i][j2], 0, 0, 0);
+        for (int j2 = 0; j2 < TJ; j2++) acc[i][j2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf[i], bfv[j2], acc[i][j2], 0, 0, 0);
     }
   }
   // store: lane holds rows 4 g + e, column li of each 16 x 16 sub-tile
 #pragma unroll
-  for (int i = 0; i < 8; i++)
+  for (int i = 0; i < TI; i++)
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
+    for (int j = 0; j < TJ; j++) {
       const int64_t nc = n0 + wn * 128 + j * 16 + li;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const int64_t mr = m0 + wm * 128 + i * 16 + 4 * g + e;
+        const int64_t mr = m0 + wm * 64 + i * 16 + 4 * g + e;
         if (mr < M && nc < N) y[mr * N + nc] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
       }
     }
@@ -671,10 +669,10 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
     if (e != hipSuccess) return e;
   } else if (plan.path == 2) {
     if (fmt == FMT_NVFP4)
-      launch_decode<FMT_NVFP4>((int)((m + 3) / 4), x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part,
+      (void)launch_decode<FMT_NVFP4>((int)((m + 3) / 4), x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part,
                                cnt_n, plan.splits, stream);
     else
-      launch_decode<FMT_MXFP4>(1, x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part, cnt_n,
+      (void)launch_decode<FMT_MXFP4>(1, x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part, cnt_n,
                                plan.splits, stream);
   } else {
     const int64_t tiles = ((m + G_BM - 1) / G_BM) * ((n + G_BN - 1) / G_BN);
@@ -693,10 +691,10 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
       lds_set[fmt] = true;
     }
     if (fmt == FMT_NVFP4)
-      hipLaunchKernelGGL(linear_gemm_kernel<FMT_NVFP4>, dim3((unsigned)tiles), dim3(256), lds, stream, xx, m, k,
+      hipLaunchKernelGGL(linear_gemm_kernel<FMT_NVFP4>, dim3((unsigned)tiles), dim3(G_THREADS), lds, stream, xx, m, k,
                          codes, scales, tensor_scale, n, t, bb, has_lora ? r : 0, yy);
     else
-      hipLaunchKernelGGL(linear_gemm_kernel<FMT_MXFP4>, dim3((unsigned)tiles), dim3(256), lds, stream, xx, m, k,
+      hipLaunchKernelGGL(linear_gemm_kernel<FMT_MXFP4>, dim3((unsigned)tiles), dim3(G_THREADS), lds, stream, xx, m, k,
                          codes, scales, tensor_scale, n, t, bb, has_lora ? r : 0, yy);
   }
   return hipGetLastError();

@@ -86,14 +86,6 @@ __host__ __device__ inline DqLayout dq_layout(int fmt, int m, int kslice, int nw
   return L;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // raw buffer (stride 0): an access at or past `bytes` returns zeros, no memory traffic
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
 template <int FMT, int NQ, int NW, int DEPTH>
 __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
     const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ codes,
@@ -166,7 +158,7 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
   auto code_off = [&](int j) -> uint32_t {
     // steps past the part, and the K tail of the last step, read past the buffer
     const bool ok = (j < j1) & (j * DQ_STEP < lane_lim);
-    return ok ? lane_off + (uint32_t)(j * (DQ_STEP / 2)) : 0xFFFFFFF0u;
+    return ok ? lane_off + (uint32_t)(j * (DQ_STEP / 2)) : kBufferOob;
   };
   u32x4_t ring[DEPTH];
 #pragma unroll

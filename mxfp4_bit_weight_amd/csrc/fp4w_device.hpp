@@ -144,6 +144,19 @@ __device__ __forceinline__ uint32_t e2m1_code_exact(float a, float d, float st) 
   return code;
 }
 
+// ---- buffer loads ----------------------------------------------------------------
+// Raw buffer resource (stride 0) over [base, base + bytes): a load at or past
+// `bytes` returns zeros and makes no memory access, so predicated-off lanes are
+// given an offset past the end instead of a branch.
+constexpr uint32_t kBufferOob = 0xFFFFFFF0u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // ---- small reductions ----------------------------------------------------------
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -46,9 +46,29 @@ hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c, const void* x, int
                               uint32_t* cnt, hipStream_t stream);
 int lora_part_count(int64_t k);
 
+// Decode kernel with x held in registers (decode_xs.hip): K in `splits` spans of
+// `qspan` 32-wide groups, `nw` waves per workgroup, weight tiles of 16 rows.
+struct XsConfig {
+  int nw;
+  int splits;
+  int qspan;
+  int ntiles;
+};
+bool decode_xs_supports(int64_t m, int64_t n, int64_t k, int r);
+XsConfig plan_decode_xs(int64_t m, int64_t n, int64_t k, int r);
+// LoRA operands: la = A (r x k bf16, r <= decode_xs_fused_rank(): the kernel forms
+// t = x A^T itself) or t = x A^T (m x r fp32, complete), and lb = B (n x r bf16);
+// la and t both nullptr: no LoRA.
+int decode_xs_fused_rank();
+hipError_t launch_decode_xs(int fmt, const XsConfig& c, const void* x, int64_t m, int64_t k, const uint8_t* codes,
+                            const uint8_t* scales, const float* ts, int64_t n, const void* la, const float* t,
+                            const void* lb, int r, void* y, float* part, uint32_t* cnt, hipStream_t stream);
+
 struct LinearPlan {
-  int path;            // 0 = decode on the block-scaled MFMA, 2 = decode on bf16 MFMA, 1 = GEMM
+  int path;            // 0 = decode on the block-scaled MFMA, 2 = decode on bf16 MFMA, 1 = GEMM,
+                       // 3 = decode with x in registers
   DecodeConfig dq;     // path 0
+  XsConfig xs;         // path 3
   int splits;          // K splits of the decode kernel (1 = none)
   int lora_parts;      // K slices of the LoRA down-projection (0 = no LoRA)
   size_t off_t;        // workspace offset of t partials: [lora_parts][m][r] fp32

@@ -552,11 +552,21 @@ static int decode_splits_for(int64_t m, int64_t n, int64_t k) {
 
 LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
   LinearPlan p{};
-  p.path = m > 16 ? 1 : decode_f8f4_supports(FMT_NVFP4, m) ? 0 : 2;
+  if (m > 16) p.path = 1;
+  else if (m >= 2 && decode_xs_supports(m, n, k, r)) p.path = 3;
+  else p.path = decode_f8f4_supports(FMT_NVFP4, m) ? 0 : 2;
+  if (p.path == 3) {
+    p.xs = plan_decode_xs(m, n, k, r);
+    if (p.xs.splits > 1 && (p.xs.ntiles + 7) / 8 > kTileSlots) p.path = 1;     // counters would not fit
+  }
   // decode path: per-chunk LoRA partials, summed by the decode kernel
-  p.lora_parts = r <= 0 ? 0 : p.path == 0 ? lora_part_count(k) : lora_parts_for(m, k);
+  const bool xs_fused = p.path == 3 && r <= decode_xs_fused_rank();     // the kernel forms t itself
+  p.lora_parts = r <= 0 || xs_fused ? 0 : p.path == 0 ? lora_part_count(k) : lora_parts_for(m, k);
   size_t part_floats = 0;
-  if (p.path == 0) {
+  if (p.path == 3) {
+    p.splits = p.xs.splits;
+    part_floats = (size_t)p.xs.splits * p.xs.ntiles * 16 * m;
+  } else if (p.path == 0) {
     // one plan for both formats: the NVFP4 layout is never smaller
     p.dq = plan_decode_f8f4(FMT_NVFP4, m, n, k, r);
     p.splits = p.dq.splits;
@@ -573,7 +583,7 @@ LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
   p.off_count = off;
   off += sizeof(uint32_t) * kCounterSlots;
   p.off_t = off;
-  if (r > 0) {
+  if (r > 0 && !xs_fused) {
     off += align256(sizeof(float) * (size_t)m * (size_t)r);                           // t
     if (p.lora_parts > 1 || p.path == 0)
       off += align256(sizeof(float) * (size_t)p.lora_parts * m * r);                  // partials
@@ -654,7 +664,7 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
       case 3: hipLaunchKernelGGL(lora_part_kernel<3>, dim3(P), dim3(256), 0, stream, xx, (int)m, k, aa, r, tp); break;
       default: hipLaunchKernelGGL(lora_part_kernel<4>, dim3(P), dim3(256), 0, stream, xx, (int)m, k, aa, r, tp); break;
     }
-  } else if (has_lora) {
+  } else if (has_lora && !(plan.path == 3 && r <= decode_xs_fused_rank())) {
     const int64_t nsteps = (k + 31) / 32;
     const int P = plan.lora_parts;
     const int spp = (int)((nsteps + P - 1) / P);
@@ -666,6 +676,12 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
   if (plan.path == 0) {
     hipError_t e = launch_decode_f8f4(fmt, plan.dq, x, m, k, codes, scales, tensor_scale, n, tp, plan.lora_parts,
                                       lora_b, r, y, part, cnt_n, stream);
+    if (e != hipSuccess) return e;
+  } else if (plan.path == 3) {
+    const bool fused = r <= decode_xs_fused_rank();
+    hipError_t e = launch_decode_xs(fmt, plan.xs, x, m, k, codes, scales, tensor_scale, n,
+                                    has_lora && fused ? lora_a : nullptr, has_lora && !fused ? t : nullptr, lora_b,
+                                    r, y, part, cnt_n, stream);
     if (e != hipSuccess) return e;
   } else if (plan.path == 2) {
     if (fmt == FMT_NVFP4)

@@ -1,11 +1,16 @@
-"""Edge cases of the decode path (m <= 8), which feeds x to the block-scaled
-matrix core as two E4M3 terms per element under an E8M0 scale per 32 elements:
+"""Edge cases of the decode paths (m <= 16).  One row of x goes to the
+block-scaled matrix core as two E4M3 terms per element under an E8M0 scale per
+32 elements; 2 to 16 rows go to the fp16 (NVFP4) or bf16 (MXFP4) matrix core
+with x scaled by a power of two per row and wave (NVFP4) and the weights
+decoded exactly in registers:
 
 - activations spanning many binades inside one block, bf16 subnormals, zero
   blocks and rows far below 1 stay within |err| <= 2e-3 ||x_m|| ||w_n^eff||;
 - a non-finite activation turns every output of its row NaN and leaves the other
   rows untouched;
-- scale bytes that start at an odd 2-byte offset (staged byte by byte).
+- a NaN block scale turns every output of its weight row (output column) NaN;
+- scale bytes that start at an odd 2-byte or an odd byte offset, and LoRA B rows
+  that are not 16-byte aligned.
 """
 import numpy as np
 import pytest
@@ -47,7 +52,7 @@ def _wide_range_x(seed: int, m: int, k: int) -> np.ndarray:
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("m", [1, 3, 8, 16])
 def test_wide_dynamic_range_activations(fp4w, fmt, m):
     n, k = 300, 2080
     say(f"[decode-edges] wide-range x fmt={fmt} m={m}")
@@ -94,6 +99,65 @@ def test_nvfp4_scales_at_odd_two_byte_offset(fp4w):
     view.copy_(u8_dev(scales))
     q2 = fp4w.QWeight(0, q.codes, view, q.tensor_scale, n, k)
     y_off = fp4w.linear(bf16_dev(x), q2, bf16_dev(a), bf16_dev(b))
+    y_ref = fp4w.linear(bf16_dev(x), q, bf16_dev(a), bf16_dev(b))
+    torch.cuda.synchronize()
+    assert torch.equal(y_off.view(torch.int16), y_ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("m", [1, 5])
+def test_nan_block_scale_poisons_its_column_only(fp4w, fmt, m):
+    n, k = 70, 640
+    say(f"[decode-edges] NaN block scale fmt={fmt} m={m}")
+    w, x, a, b = W.linear_inputs(91 + m, n, k, m, rank=16)
+    codes, scales, st = O.quantize(fmt, w)
+    scales = scales.copy()
+    scales[33, 3] = 0x7F if fmt == 0 else 0xFF          # the format's NaN scale code
+    q = qweight_dev(fp4w, fmt, codes, scales, st)
+    y = fp4w.linear(bf16_dev(x), q, bf16_dev(a), bf16_dev(b)).float().cpu().numpy()
+    assert np.isnan(y[:, 33]).all()
+    keep = np.array([c for c in range(n) if c != 33])
+    y64 = O.linear(fmt, x, codes, scales, st, a, b)[:, keep]
+    xn = np.sqrt((f64_of_bf16(x) ** 2).sum(axis=1))[:, None]
+    wn = weff_norms(fmt, codes[keep], scales[keep], st, a, b[keep])[None, :]
+    check_bound(y[:, keep].astype(np.float64), y64, xn, wn, "columns without the NaN scale")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_scales_at_odd_byte_offset(fp4w, fmt):
+    """MXFP4 scales may start at any byte; NVFP4 scales must be 2-byte aligned
+    and an odd address is refused before anything is launched."""
+    m, n, k = 3, 130, 1056
+    say(f"[decode-edges] scales at a 1-byte offset fmt={fmt}")
+    w, x, a, b = W.linear_inputs(83, n, k, m, rank=8)
+    codes, scales, st = O.quantize(fmt, w)
+    q = qweight_dev(fp4w, fmt, codes, scales, st)
+    buf = torch.zeros(scales.size + 64, dtype=torch.uint8, device=DEV)
+    view = buf[1:1 + scales.size].view(scales.shape)
+    view.copy_(u8_dev(scales))
+    q2 = fp4w.QWeight(fmt, q.codes, view, q.tensor_scale, n, k)
+    if fmt == 0:
+        with pytest.raises(fp4w.Fp4wError) as ei:
+            fp4w.linear(bf16_dev(x), q2, bf16_dev(a), bf16_dev(b))
+        assert ei.value.status == -3
+        return
+    y_off = fp4w.linear(bf16_dev(x), q2, bf16_dev(a), bf16_dev(b))
+    y_ref = fp4w.linear(bf16_dev(x), q, bf16_dev(a), bf16_dev(b))
+    torch.cuda.synchronize()
+    assert torch.equal(y_off.view(torch.int16), y_ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("m", [1, 6])
+def test_lora_b_not_16_byte_aligned(fp4w, m):
+    n, k, r = 150, 512, 16
+    say(f"[decode-edges] LoRA B at a 2-byte offset m={m}")
+    w, x, a, b = W.linear_inputs(87, n, k, m, rank=r)
+    codes, scales, st = O.quantize(0, w)
+    q = qweight_dev(fp4w, 0, codes, scales, st)
+    buf = torch.zeros(b.size + 8, dtype=torch.bfloat16, device=DEV)
+    bv = buf[1:1 + b.size].view(n, r)
+    bv.copy_(bf16_dev(b))
+    y_off = fp4w.linear(bf16_dev(x), q, bf16_dev(a), bv)
     y_ref = fp4w.linear(bf16_dev(x), q, bf16_dev(a), bf16_dev(b))
     torch.cuda.synchronize()
     assert torch.equal(y_off.view(torch.int16), y_ref.view(torch.int16))

@@ -366,34 +366,38 @@ __device__ __forceinline__ void gemm_store_lds(const GemmStage<FMT>& st, uint16_
     *reinterpret_cast<u32x4_t*>(sa + rr * G_LDA + c) = st.xv[i];
   }
   const int rr = tid >> 1, c = 32 * (tid & 1);
-  u32x4_t o[4];
+  uint16_t* const dst = sb + rr * G_LDA + c;
   if (FMT == FMT_NVFP4) {
     const float d0 = e4m3_to_f32(st.sv & 0xFFu), d1 = e4m3_to_f32((st.sv >> 8) & 0xFFu);
+    // one 16-byte piece at a time (few live registers: two stages of loads are in flight)
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const float d = q < 2 ? d0 : d1;
       const uint32_t dw = st.cv[q];
-      f32x2_t a0 = fp4x2_to_f32x2<0>(dw, 1.0f), a1 = fp4x2_to_f32x2<1>(dw, 1.0f);
-      f32x2_t a2 = fp4x2_to_f32x2<2>(dw, 1.0f), a3 = fp4x2_to_f32x2<3>(dw, 1.0f);
+      const f32x2_t a0 = fp4x2_to_f32x2<0>(dw, 1.0f), a1 = fp4x2_to_f32x2<1>(dw, 1.0f);
+      const f32x2_t a2 = fp4x2_to_f32x2<2>(dw, 1.0f), a3 = fp4x2_to_f32x2<3>(dw, 1.0f);
       // e2m1 * dec(sb) has at most 6 significant bits: exact in fp32 and in bf16
-      o[q].x = (__float_as_uint(a0.x * d) >> 16) | (__float_as_uint(a0.y * d) & 0xFFFF0000u);
-      o[q].y = (__float_as_uint(a1.x * d) >> 16) | (__float_as_uint(a1.y * d) & 0xFFFF0000u);
-      o[q].z = (__float_as_uint(a2.x * d) >> 16) | (__float_as_uint(a2.y * d) & 0xFFFF0000u);
-      o[q].w = (__float_as_uint(a3.x * d) >> 16) | (__float_as_uint(a3.y * d) & 0xFFFF0000u);
+      u32x4_t o;
+      o.x = (__float_as_uint(a0.x * d) >> 16) | (__float_as_uint(a0.y * d) & 0xFFFF0000u);
+      o.y = (__float_as_uint(a1.x * d) >> 16) | (__float_as_uint(a1.y * d) & 0xFFFF0000u);
+      o.z = (__float_as_uint(a2.x * d) >> 16) | (__float_as_uint(a2.y * d) & 0xFFFF0000u);
+      o.w = (__float_as_uint(a3.x * d) >> 16) | (__float_as_uint(a3.y * d) & 0xFFFF0000u);
+      *reinterpret_cast<u32x4_t*>(dst + 8 * q) = o;
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     const float sc = e8m0_scale_operand(st.sv);
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const uint32_t dw = st.cv[q];
-      o[q].x = fp4x2_to_bf16x2_scaled<0>(dw, sc);
-      o[q].y = fp4x2_to_bf16x2_scaled<1>(dw, sc);
-      o[q].z = fp4x2_to_bf16x2_scaled<2>(dw, sc);
-      o[q].w = fp4x2_to_bf16x2_scaled<3>(dw, sc);
+      u32x4_t o;
+      o.x = fp4x2_to_bf16x2_scaled<0>(dw, sc);
+      o.y = fp4x2_to_bf16x2_scaled<1>(dw, sc);
+      o.z = fp4x2_to_bf16x2_scaled<2>(dw, sc);
+      o.w = fp4x2_to_bf16x2_scaled<3>(dw, sc);
+      *reinterpret_cast<u32x4_t*>(dst + 8 * q) = o;
     }
   }
-#pragma unroll
-  for (int q = 0; q < 4; q++) *reinterpret_cast<u32x4_t*>(sb + rr * G_LDA + c + 8 * q) = o[q];
 }
 
 template <int FMT>
@@ -419,13 +423,16 @@ __global__ __launch_bounds__(G_THREADS, 2) void linear_gemm_kernel(
     for (int j = 0; j < TJ; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (int)((K + G_BK - 1) / G_BK);
-  GemmStage<FMT> stage;
-  gemm_load<FMT>(stage, x, M, K, codes, scales, N, m0, n0, 0);
-  gemm_store_lds<FMT>(stage, sA0, sB0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt++) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gemm_load<FMT>(stage, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 1) * G_BK);
+  // Global loads run two K tiles ahead (two register stages, used alternately):
+  // a K tile's MFMAs take well under the latency of a load from HBM.  The
+  // barrier waits for LDS work only; the loads of the tile after next stay in
+  // flight across it.
+  auto lds_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mfma_tile = [&](int cur) __attribute__((always_inline)) {
     const uint16_t* a = sA0 + cur * (G_BM * G_LDA);
     const uint16_t* b = sB0 + cur * (G_BN * G_LDA);
 #pragma unroll
@@ -442,19 +449,31 @@ __global__ __launch_bounds__(G_THREADS, 2) void linear_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < TJ; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) gemm_store_lds<FMT>(stage, sA0 + (cur ^ 1) * (G_BM * G_LDA), sB0 + (cur ^ 1) * (G_BN * G_LDA));
-    __syncthreads();
+  };
+  GemmStage<FMT> st0, st1;
+  gemm_load<FMT>(st0, x, M, K, codes, scales, N, m0, n0, 0);
+  if (nk > 1) gemm_load<FMT>(st1, x, M, K, codes, scales, N, m0, n0, (int64_t)G_BK);
+  gemm_store_lds<FMT>(st0, sA0, sB0);
+  lds_barrier();
+  // iteration kt: tile kt is in LDS buffer kt & 1, tile kt + 1 in the other stage's
+  // registers; the freed stage loads tile kt + 2
+  for (int kt = 0; kt < nk; kt += 2) {
+    if (kt + 2 < nk) gemm_load<FMT>(st0, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 2) * G_BK);
+    mfma_tile(0);
+    if (kt + 1 < nk) gemm_store_lds<FMT>(st1, sA0 + (G_BM * G_LDA), sB0 + (G_BN * G_LDA));
+    lds_barrier();
+    if (kt + 1 >= nk) break;
+    if (kt + 3 < nk) gemm_load<FMT>(st1, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 3) * G_BK);
+    mfma_tile(1);
+    if (kt + 2 < nk) gemm_store_lds<FMT>(st0, sA0, sB0);
+    lds_barrier();
   }
 
   // epilogue: y = s_t * acc + LoRA, with the LoRA as extra MFMA steps over
   // K' = [t_hi | t_lo] (t split into two bf16 parts) against [B | B].
+  // (s_t is applied in the first LoRA step, or at the store without LoRA: a
+  // separate pass over the accumulators costs registers two load stages need)
   const float st = (FMT == FMT_NVFP4) ? *tensor_scale : 1.0f;
-#pragma unroll
-  for (int i = 0; i < TI; i++)
-#pragma unroll
-    for (int j = 0; j < TJ; j++)
-#pragma unroll
-      for (int e = 0; e < 4; e++) acc[i][j][e] *= st;
   if (t) {
     const int rpad = ((r + 15) / 16) * 16;
     for (int jb = 0; jb < rpad; jb += 16) {
@@ -500,7 +519,13 @@ __global__ __launch_bounds__(G_THREADS, 2) void linear_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < TI; i++)
 #pragma unroll
-        for (int j2 = 0; j2 < TJ; j2++) acc[i][j2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf[i], bfv[j2], acc[i][j2], 0, 0, 0);
+        for (int j2 = 0; j2 < TJ; j2++) {
+          if (FMT == FMT_NVFP4 && jb == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[i][j2][e] *= st;
+          }
+          acc[i][j2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf[i], bfv[j2], acc[i][j2], 0, 0, 0);
+        }
     }
   }
   // store: lane holds rows 4 g + e, column li of each 16 x 16 sub-tile
@@ -512,7 +537,8 @@ __global__ __launch_bounds__(G_THREADS, 2) void linear_gemm_kernel(
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const int64_t mr = m0 + wm * 64 + i * 16 + 4 * g + e;
-        if (mr < M && nc < N) y[mr * N + nc] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
+        const float v = (FMT == FMT_NVFP4 && !t) ? acc[i][j][e] * st : acc[i][j][e];
+        if (mr < M && nc < N) y[mr * N + nc] = (uint16_t)f32_to_bf16_rne(v);
       }
     }
 }

@@ -25,21 +25,47 @@ __global__ void nvfp4_amax_zero_kernel(uint32_t* word) { *word = 0u; }
 
 // |w| of a bf16 is its bit pattern without the sign; as unsigned integers these
 // order like the values (NaN patterns above +inf above every finite value).
-__global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint4* __restrict__ w, int64_t n16,
-                                                         uint32_t* __restrict__ word) {
+// A workgroup reads one contiguous chunk with AMAX_UNROLL loads in flight per
+// thread, reduces across its waves in LDS and offers its maximum with a single
+// atomic, skipped when the word already holds as much (atomics on one address
+// are serialized, so their number, not the reads, would otherwise set the time).
+constexpr int AMAX_THREADS = 256;
+constexpr int AMAX_UNROLL = 8;
+
+__global__ __launch_bounds__(AMAX_THREADS) void nvfp4_amax_kernel(const uint4* __restrict__ w, int64_t n16,
+                                                                  uint32_t* __restrict__ word) {
+  __shared__ uint32_t wmax[AMAX_THREADS / 64];
+  const int64_t chunk = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * chunk;
+  const int64_t i1 = i0 + chunk < n16 ? i0 + chunk : n16;
   uint32_t m = 0;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
-    uint4 v = w[i];
-    uint32_t a[4] = {v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu};
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += (int64_t)AMAX_THREADS * AMAX_UNROLL) {
+    uint4 v[AMAX_UNROLL];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      uint32_t lo = a[j] & 0xFFFFu, hi = a[j] >> 16;
-      m = lo > m ? lo : m;
-      m = hi > m ? hi : m;
+    for (int u = 0; u < AMAX_UNROLL; u++) {
+      const int64_t j = i + (int64_t)u * AMAX_THREADS;
+      v[u] = j < i1 ? w[j] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < AMAX_UNROLL; u++) {
+      const uint32_t a[4] = {v[u].x & 0x7FFF7FFFu, v[u].y & 0x7FFF7FFFu, v[u].z & 0x7FFF7FFFu, v[u].w & 0x7FFF7FFFu};
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const uint32_t lo = a[q] & 0xFFFFu, hi = a[q] >> 16;
+        m = lo > m ? lo : m;
+        m = hi > m ? hi : m;
+      }
     }
   }
   m = wave_max_u32(m);
-  if ((threadIdx.x & 63) == 0 && m != 0u) atomicMax(word, m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int q = 1; q < AMAX_THREADS / 64; q++) m = wmax[q] > m ? wmax[q] : m;
+    const uint32_t cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (m > cur) atomicMax(word, m);
+  }
 }
 
 __device__ __forceinline__ float tensor_scale_from_amax_word(uint32_t word) {
@@ -211,8 +237,9 @@ hipError_t launch_quantize(int fmt, const void* w, int64_t n, int64_t k, uint8_t
     uint32_t* word = reinterpret_cast<uint32_t*>(tensor_scale);
     if (!frozen) {
       hipLaunchKernelGGL(nvfp4_amax_zero_kernel, dim3(1), dim3(1), 0, stream, word);
-      hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(grid_for(count / 8, 256 * 8, 2048)), dim3(256), 0, stream,
-                         reinterpret_cast<const uint4*>(w), count / 8, word);
+      // about 4 workgroups per CU, each at least 32 KiB of the tensor
+      hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(grid_for(count / 8, AMAX_THREADS * AMAX_UNROLL, 1024)),
+                         dim3(AMAX_THREADS), 0, stream, reinterpret_cast<const uint4*>(w), count / 8, word);
       hipLaunchKernelGGL(nvfp4_encode_kernel<false>, dim3(grid_for(nblocks, 256, 16384)), dim3(256), 0, stream,
                          reinterpret_cast<const uint4*>(w), nblocks, word, scales,
                          reinterpret_cast<uint2*>(codes));

@@ -124,15 +124,22 @@ size_t fp4w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
  *   y_bf16     (m, n) bf16, rounded once from the fp32 result
  *   workspace  >= fp4w_linear_workspace_bytes(m, n, k, r) bytes, see above
  * Launches (all on `stream`):
- *  - m <= 8: with a LoRA, a kernel writing per-chunk
- *    partials of t = x A^T; then the decode kernel on gfx950's block-scaled
- *    MFMA, which feeds the codes to the matrix core as stored and x as two E4M3
- *    terms per element under an E8M0 scale per 32 elements.  That split is exact
- *    for every element within 2^13 of its block's largest magnitude; smaller
- *    ones are off by at most 2^-21 of that maximum.  A non-finite x element
- *    makes every output of its row NaN.
- *  - 8 < m <= 16: the LoRA down-projection, then a decode kernel on the
- *    bf16 MFMA (codes dequantized exactly to bf16 in registers).
+ *  - m == 1: with a LoRA, a kernel writing per-chunk partials of t = x A^T;
+ *    then the decode kernel on gfx950's block-scaled MFMA, which feeds the
+ *    codes to the matrix core as stored and x as two E4M3 terms per element
+ *    under an E8M0 scale per 32 elements.  That split is exact for every element
+ *    within 2^13 of its block's largest magnitude; smaller ones are off by at
+ *    most 2^-21 of that maximum.
+ *  - 2 <= m <= 16: one decode kernel holding x in registers (it also forms
+ *    t = x A^T when r <= 16; larger ranks get a LoRA down-projection launch
+ *    first): the weights are decoded exactly to fp16 (NVFP4, with x scaled to
+ *    fp16 by a power of two per row and K range: exact for every element within
+ *    2^28 of that range's largest magnitude) or bf16 (MXFP4) in registers and
+ *    fed to the 16-bit MFMA.  MXFP4 weights whose decoded value exceeds bf16's
+ *    range (scale codes 253, 254 only) give infinite products, as dequantizing
+ *    to bf16 does.
+ *    On both decode paths a non-finite x element makes every output of its row
+ *    NaN, and a NaN block scale every output of its weight row.
  *  - m > 16: the LoRA down-projection, then the LDS-staged bf16 MFMA GEMM.
  * The LoRA product is added in fp32 (GEMM: t split into two bf16 parts for the
  * matrix cores).

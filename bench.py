@@ -193,7 +193,7 @@ def main():
     per_launch_ms, _ = time_graph(gemv_only, launches, args.warmup)
     gemv_bytes = linear_bytes(0, 1, n, k, 0)
     achieved = gemv_bytes / (per_launch_ms * 1e-3) / 1e9
-    roofline = {"kernel": "decode_f8f4_kernel<NVFP4, 1 row, 4 waves, ring 8> on W (18944, 3584), M=1",
+    roofline = {"kernel": "decode_f8f4_kernel<NVFP4, 1 row, 4 waves, ring 8, no LoRA> on W (18944, 3584), M=1",
                 "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(),
                 "avg_launch_us": round(per_launch_ms * 1e3, 3), "launches_timed": launches,

@@ -106,10 +106,11 @@ int fp4w_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
  * Workspace for fp4w_linear, in bytes, for x (m, k), W (n, k) and LoRA rank r
  * (0 when there is no LoRA); 0 for invalid arguments.  It holds the LoRA
  * intermediate t = x A^T (fp32) or its per-chunk partials, split-K partial sums
- * and, in its first 8 KiB at fixed offsets, arrival counters.  The counters
- * must be zero before the first call: zero-fill a new workspace once; every call
- * returns its counters to zero when it completes, so one workspace serves calls
- * of any shape in stream order.
+ * and, in its first 28800 bytes at fixed offsets, arrival counters and the words
+ * through which one kernel's workgroups hand t to each other.  That area must be
+ * zero before the first call: zero-fill a new workspace once; every call returns
+ * it to zero when it completes, so one workspace serves calls of any shape in
+ * stream order (calls that overlap on one workspace race).
  */
 size_t fp4w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
 
@@ -124,12 +125,14 @@ size_t fp4w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
  *   y_bf16     (m, n) bf16, rounded once from the fp32 result
  *   workspace  >= fp4w_linear_workspace_bytes(m, n, k, r) bytes, see above
  * Launches (all on `stream`):
- *  - m == 1: with a LoRA, a kernel writing per-chunk partials of t = x A^T;
- *    then the decode kernel on gfx950's block-scaled MFMA, which feeds the
- *    codes to the matrix core as stored and x as two E4M3 terms per element
- *    under an E8M0 scale per 32 elements.  That split is exact for every element
- *    within 2^13 of its block's largest magnitude; smaller ones are off by at
- *    most 2^-21 of that maximum.
+ *  - m == 1: one launch of the decode kernel on gfx950's block-scaled MFMA,
+ *    which feeds the codes to the matrix core as stored and x as two E4M3 terms
+ *    per element under an E8M0 scale per 32 elements.  That split is exact for
+ *    every element within 2^13 of its block's largest magnitude; smaller ones
+ *    are off by at most 2^-21 of that maximum.  With a LoRA, the kernel's first
+ *    workgroups form t = x A^T on the bf16 matrix core, one K chunk each, and
+ *    hand it to the workgroups that write the outputs (chunks added in a fixed
+ *    order: the result does not depend on scheduling).
  *  - 2 <= m <= 16: one decode kernel holding x in registers (it also forms
  *    t = x A^T when r <= 16; larger ranks get a LoRA down-projection launch
  *    first): the weights are decoded exactly to fp16 (NVFP4, with x scaled to
@@ -187,6 +190,17 @@ int fp4w_merge_scales(int fmt, const uint8_t *scales_in, const float *deltas,
                       int64_t num_blocks, uint8_t *scales_out,
                       const uint8_t *codes_in, uint8_t *codes_out, int64_t code_bytes,
                       void *stream);
+
+/*
+ * Test hook (not part of the method): the longest time, in ticks of the
+ * device's 100 MHz clock, that a workgroup of the m == 1 decode kernel waits
+ * for the t = x A^T that other workgroups publish before it forms t itself by
+ * the same steps in the same order (the outputs are the same either way).
+ * Default 100000 (1 ms); 0 makes most workgroups form t themselves.  Applies to
+ * later launches of this process; ticks < 0 only queries.  Returns the value
+ * in force before the call.
+ */
+int64_t fp4w_debug_lora_wait(int64_t ticks);
 
 /* Human-readable name of a status code (static string). */
 const char *fp4w_status_string(int status);

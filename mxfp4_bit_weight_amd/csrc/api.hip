@@ -32,7 +32,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP4W_OK : FP4W_ERR_HIP; 
 
 extern "C" {
 
-int fp4w_version(void) { return 2; }
+int fp4w_version(void) { return 3; }
 
 const char* fp4w_status_string(int status) {
   switch (status) {
@@ -77,6 +77,10 @@ int fp4w_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, const 
 size_t fp4w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
   if (m < 0 || n < 0 || k < 0 || r < 0 || r > FP4W_MAX_LORA_RANK) return 0;
   return fp4w::plan_linear(m, n, k, r).bytes;
+}
+
+int64_t fp4w_debug_lora_wait(int64_t ticks) {
+  return ticks < 0 ? fp4w::lora_wait_ticks() : fp4w::set_lora_wait_ticks(ticks);
 }
 
 int fp4w_linear(int fmt, const void* x_bf16, int64_t m, int64_t k, const uint8_t* codes, const uint8_t* scales,

@@ -38,10 +38,27 @@
 // Wave partials are added in LDS in wave order; with several slices the last
 // workgroup of a tile to arrive adds the slices' partials in slice order, so
 // the result never depends on scheduling.
+//
+// LoRA (t = x A^T, then t B^T added to every output row): t is needed only
+// when a tile's outputs are written, after its codes have streamed, so the
+// down-projection runs inside the same launch.  The grid's first workgroups
+// stream no codes: workgroup p forms the partial of K chunk p on the bf16
+// matrix core (each wave a run of 32-wide steps, waves added in order) and
+// stores it, complemented so that a zero word reads as "not yet written".  A
+// workgroup writing outputs waits for every chunk word with a bounded poll and
+// adds the chunks in chunk order; were the wait ever to run out, it forms the
+// chunks itself by the same steps in the same order, so the value is the same
+// either way.  The chunk workgroups wait on nothing, so the wait ends.  The
+// hand-over words return to zero before the kernel ends: the readers arrive on
+// 32 counters a cache line apart, the completed groups and the chunk
+// workgroups (after their stores have landed) on one more, and the arrival
+// that completes it clears the words.
 #include "fp4w_device.hpp"
 #include "fp4w_internal.hpp"
 #include "sync.hpp"
 #include "xenc.hpp"
+
+#include <atomic>
 
 namespace fp4w {
 
@@ -50,6 +67,7 @@ typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 constexpr int DQ_STEP = 128;       // K per step: one block-scaled MFMA
 constexpr int DQ_ROWS = 16;        // weight rows per tile
 constexpr int DQ_MAX_R = 64;       // LoRA rank staged in LDS
+constexpr int DQ_LSPW = 4;         // 32-wide K steps per wave of a LoRA chunk
 
 // LDS layout of one workgroup (byte offsets):
 //   zeros   128 (spw + 1)          A lanes that carry no x read here (spw: steps per wave)
@@ -59,9 +77,10 @@ constexpr int DQ_MAX_R = 64;       // LoRA rank staged in LDS
 //   lb      16 x r bf16            the tile rows of the LoRA B
 //   lt      m x r fp32             t = x A^T
 //   red     nw x m x 16 fp32       wave partials
+//   lr      nw x m x r fp32        wave partials of a LoRA chunk
 struct DqLayout {
   int kslice, xrow, nblkp, srow, spw;
-  int zero_off, xh_off, xl_off, sc_off, ws_off, lb_off, lt_off, red_off, bytes;
+  int zero_off, xh_off, xl_off, sc_off, ws_off, lb_off, lt_off, red_off, lr_off, bytes;
 };
 
 __host__ __device__ inline DqLayout dq_layout(int fmt, int m, int kslice, int nw, int r) {
@@ -82,17 +101,64 @@ __host__ __device__ inline DqLayout dq_layout(int fmt, int m, int kslice, int nw
   L.lb_off = off;   off += (DQ_ROWS * r * 2 + 15) & ~15;
   L.lt_off = off;   off += m * r * 4;
   L.red_off = off;  off += nw * m * DQ_ROWS * 4;
+  L.lr_off = off;   off += nw * m * r * 4;
   L.bytes = off;
   return L;
 }
 
-template <int FMT, int NQ, int NW, int DEPTH>
+// ---------------------------------------------------------------------------------
+// LoRA hand-over between the workgroups of one launch (words of the counter area).
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lsync_load(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void lsync_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t lsync_add(uint32_t* p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One wave: an arrival on the top counter, which expects one arrival per reader
+// group and per chunk; the arrival that completes it clears the `words` chunk
+// words and the counter.
+__device__ __forceinline__ void lsync_top_arrive(uint32_t* ls, uint32_t expected, int words, int lane) {
+  uint32_t old = 0;
+  if (lane == 0) old = lsync_add(&ls[kLsyncTop]);
+  old = (uint32_t)__shfl((int)old, 0, 64);
+  if (old == expected - 1u) {
+    for (int e = lane; e < words; e += 64) lsync_store(&ls[e], 0u);
+    if (lane == 0) lsync_store(&ls[kLsyncTop], 0u);
+  }
+}
+
+__device__ __forceinline__ uint32_t lsync_top_expected(int ntiles, int lparts) {
+  return (uint32_t)((ntiles < kLsyncSubs ? ntiles : kLsyncSubs) + lparts);
+}
+
+// One wave of the workgroup that writes the outputs of `tile`, after its loads of
+// the chunk words have returned.
+__device__ __forceinline__ void lsync_reader_arrive(uint32_t* ls, int tile, int ntiles, int lparts, int words,
+                                                    int lane) {
+  const int c = tile % kLsyncSubs;
+  const uint32_t quota = (uint32_t)(ntiles / kLsyncSubs + (c < ntiles % kLsyncSubs ? 1 : 0));
+  uint32_t old = 0;
+  if (lane == 0) {
+    old = lsync_add(&ls[kLsyncSub + 32 * c]);
+    if (old == quota - 1u) lsync_store(&ls[kLsyncSub + 32 * c], 0u);
+  }
+  old = (uint32_t)__shfl((int)old, 0, 64);
+  if (old == quota - 1u) lsync_top_arrive(ls, lsync_top_expected(ntiles, lparts), words, lane);
+}
+
+template <int FMT, int NQ, int NW, int DEPTH, bool LORA>
 __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
     const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t N,
-    const float* __restrict__ tp, int parts, const uint16_t* __restrict__ lora_b, int r,
-    uint16_t* __restrict__ y, float* __restrict__ part, uint32_t* __restrict__ cnt, int S, int sps,
-    int nsteps_total, int ntiles, int scales16) {
+    const uint16_t* __restrict__ lora_a, const uint16_t* __restrict__ lora_b, int r,
+    int lparts, int lsw, uint32_t* __restrict__ lsync, uint16_t* __restrict__ y, float* __restrict__ part,
+    uint32_t* __restrict__ cnt, int S, int sps, int nsteps_total, int ntiles, int scales16,
+    uint64_t wait_ticks) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int flag;
   constexpr int NT = 64 * NW;
@@ -101,11 +167,69 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
   // if any, load after it): x units of 8 elements, 16-byte scale units
   constexpr int DQ_XPRE = NW >= 16 ? 3 : 2;
   constexpr int DQ_SPRE = NW >= 16 ? 2 : 1;
-  const int s = blockIdx.x % S, tile = blockIdx.x / S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // uniform: keeps the buffer descriptor scalar
-  const int rr = tp ? r : 0;
+  const int rr = LORA ? r : 0;                                   // LORA: lora_a, lora_b given, r > 0
+  const int mr = M * rr;
+  const int words = lparts * mr;                                  // chunk words of the hand-over
   const DqLayout L = dq_layout(FMT, M, sps * DQ_STEP, NW, rr);
+  const int bid = (int)blockIdx.x - lparts;                       // < 0: a LoRA chunk workgroup
+  const int s = bid % S, tile = bid / S;
+  // ---- LoRA chunk p: wave w takes the lsw 32-wide K steps from (p NW + w) lsw
+  //      on v_mfma_f32_16x16x32_bf16, x rows as A (row = lane % 16), A's rows as B
+  //      (column j = 16 b + lane % 16); lane (j, g) gets rows m = 4 g + i.  Loads
+  //      go out LSPW steps at a time. --------------------------------------------------
+  float* lr = reinterpret_cast<float*>(lds + L.lr_off);            // [wave][m][j]
+  auto lora_chunk = [&](int p) __attribute__((always_inline)) {
+    const int li = lane & 15, lg = lane >> 4;
+    const int64_t st0 = ((int64_t)p * NW + wave) * lsw;
+    for (int b = 0; b < (rr + 15) / 16; b++) {
+      const int j = 16 * b + li;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int i0 = 0; i0 < lsw; i0 += DQ_LSPW) {
+        u32x4_t xa[DQ_LSPW], av[DQ_LSPW];
+#pragma unroll
+        for (int i = 0; i < DQ_LSPW; i++) {
+          const int64_t kk = (st0 + i0 + i) * 32 + 8 * lg;
+          const bool okx = li < M && kk < K, oka = j < rr && kk < K;
+          xa[i] = load16(x + (okx ? (int64_t)li * K + kk : 0));
+          av[i] = load16(lora_a + (oka ? (int64_t)j * K + kk : 0));
+          if (!okx) xa[i] = (u32x4_t){0u, 0u, 0u, 0u};
+          if (!oka) av[i] = (u32x4_t){0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < DQ_LSPW; i++)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[i]), as_bf16x8(av[i]), acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int m = 4 * lg + i;
+        if (m < M && j < rr) lr[(wave * M + m) * rr + j] = acc[i];
+      }
+    }
+  };
+  // wave 0, after a barrier that follows lora_chunk(p): the chunk's value at
+  // e = m r + j, its waves added in order
+  auto chunk_value = [&](int e) __attribute__((always_inline)) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; w++) v += lr[w * mr + e];
+    return v;
+  };
+  if (LORA && bid < 0) {
+    // ---- 0. a chunk workgroup: its partial, complemented, then its arrival ------
+    const int p = (int)blockIdx.x;
+    lora_chunk(p);
+    __syncthreads();
+    if (wave == 0) {
+      for (int e = lane; e < mr; e += 64) lsync_store(&lsync[p * mr + e], ~__float_as_uint(chunk_value(e)));
+      wait_stores_complete();
+      lsync_top_arrive(lsync, lsync_top_expected(ntiles, lparts), words, lane);
+    }
+    return;
+  }
+
+
   const int kslice = L.kslice;
   const int step0 = s * sps;
   const int nss = min(sps, nsteps_total - step0);          // steps in this slice
@@ -138,7 +262,7 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
     grow = grow < N ? grow : N - 1;
     sv[c] = load16(scales + (u < us ? grow * srow_g + k0 / BLK + 16 * q : 0));
   }
-  // first LoRA B element of this thread; the rest, and t, load later
+  // first LoRA B element of this thread; the rest load later
   uint32_t lbv = 0;
   if (rr > 0) {
     const int rw = tid / rr, j = tid - rw * rr;
@@ -225,25 +349,10 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
   }
   if (rr > 0) {
     uint16_t* lb = reinterpret_cast<uint16_t*>(lds + L.lb_off);
-    float* lt = reinterpret_cast<float*>(lds + L.lt_off);
     if (tid < DQ_ROWS * rr) lb[tid] = (uint16_t)lbv;
     for (int e = tid + NT; e < DQ_ROWS * rr; e += NT) {
       const int rw = e / rr, j = e - rw * rr;
       lb[e] = row_base + rw < N ? lora_b[(row_base + rw) * rr + j] : (uint16_t)0;
-    }
-    // t = sum of the chunk partials, in chunk order (8 loads in flight at a time)
-    const int mr = M * rr;
-    for (int e = tid; e < mr; e += NT) {
-      float sum = 0.f;
-      for (int p0 = 0; p0 < parts; p0 += 8) {
-        float pv[8];
-#pragma unroll
-        for (int q = 0; q < 8; q++) pv[q] = p0 + q < parts ? tp[(int64_t)(p0 + q) * mr + e] : 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; q++)
-          if (p0 + q < parts) sum += pv[q];
-      }
-      lt[e] = sum;
     }
   }
   __syncthreads();
@@ -398,6 +507,49 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
       o = sum;
     }
   }
+  if (LORA) {
+    // ---- 6. t: the published chunks added in chunk order (bounded wait), else
+    //      the chunks formed here by the same steps ------------------------------
+    __shared__ int have_t;
+    float* lt = reinterpret_cast<float*>(lds + L.lt_off);
+    if (wave == 0) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      int ok;
+      for (;;) {
+        int mine = 1;
+        for (int q = lane; q < mr; q += 64) {
+          float t = 0.f;
+          for (int p0 = 0; p0 < lparts; p0 += 8) {
+            uint32_t w[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) w[i] = p0 + i < lparts ? lsync_load(&lsync[(p0 + i) * mr + q]) : ~0u;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+              if (w[i] == 0u) mine = 0;
+              if (p0 + i < lparts) t += __uint_as_float(~w[i]);
+            }
+          }
+          lt[q] = t;
+        }
+        ok = __all(mine);
+        if (ok || __builtin_amdgcn_s_memrealtime() - t0 >= wait_ticks) break;
+        __builtin_amdgcn_s_sleep(8);
+      }
+      if (lane == 0) have_t = ok;
+    }
+    __syncthreads();
+    if (__builtin_expect(!have_t, 0)) {
+      if (wave == 0)
+        for (int q = lane; q < mr; q += 64) lt[q] = 0.f;
+      for (int p = 0; p < lparts; p++) {
+        lora_chunk(p);
+        __syncthreads();
+        if (wave == 0)
+          for (int q = lane; q < mr; q += 64) lt[q] += chunk_value(q);
+        __syncthreads();
+      }
+    }
+  }
   if (e < nout) {
     const int m = e / DQ_ROWS, nn = e - m * DQ_ROWS;
     const int64_t row = row_base + nn;
@@ -414,6 +566,8 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
       y[(int64_t)m * N + row] = (uint16_t)f32_to_bf16_rne(out);
     }
   }
+  // the chunk words have been read (or were not needed): arrive
+  if (LORA && wave == 0) lsync_reader_arrive(lsync, tile, ntiles, lparts, words, lane);
 }
 
 // ---------------------------------------------------------------------------------
@@ -459,14 +613,35 @@ DecodeConfig plan_decode_f8f4(int fmt, int64_t m, int64_t n, int64_t k, int r) {
   return c;
 }
 
+static std::atomic<int64_t> g_lora_wait{100000};          // 1 ms
+int64_t lora_wait_ticks() { return g_lora_wait.load(std::memory_order_relaxed); }
+int64_t set_lora_wait_ticks(int64_t ticks) { return g_lora_wait.exchange(ticks, std::memory_order_relaxed); }
+
+// Steps per wave of a LoRA chunk: DQ_LSPW (one round of loads per column block),
+// or a multiple of it when the chunk words would not fit the hand-over area.
+static int dq_lora_steps(int nw, int64_t k, int mr) {
+  const int64_t nsteps = (k + 31) / 32;
+  int64_t lsw = DQ_LSPW;
+  while ((nsteps + lsw * nw - 1) / (lsw * nw) * mr > kLsyncWords) lsw += DQ_LSPW;
+  return (int)lsw;
+}
+
 template <int FMT, int NQ>
 static void launch_nq(const DecodeConfig& c, dim3 grid, size_t lds, hipStream_t stream, const uint16_t* x, int m,
                       int64_t k, const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t n,
-                      const float* tp, int parts, const uint16_t* lb, int r, uint16_t* y, float* part,
-                      uint32_t* cnt, int nsteps, int ntiles, int scales16) {
-#define FP4W_DQ(W, D)                                                                                      \
-  hipLaunchKernelGGL((decode_f8f4_kernel<FMT, NQ, W, D>), grid, dim3(64 * W), lds, stream, x, m, k, codes, \
-                     scales, ts, n, tp, parts, lb, r, y, part, cnt, c.splits, c.sps, nsteps, ntiles, scales16)
+                      const uint16_t* la, const uint16_t* lb, int r, int lparts, int lsw, uint32_t* lsync, uint16_t* y, float* part, uint32_t* cnt, int nsteps, int ntiles,
+                      int scales16) {
+#define FP4W_DQ(W, D)                                                                                        \
+  do {                                                                                                       \
+    if (r > 0)                                                                                               \
+      hipLaunchKernelGGL((decode_f8f4_kernel<FMT, NQ, W, D, true>), grid, dim3(64 * W), lds, stream, x, m, k,  \
+                         codes, scales, ts, n, la, lb, r, lparts, lsw, lsync, y, part, cnt, c.splits, c.sps, nsteps, \
+                         ntiles, scales16, (uint64_t)lora_wait_ticks());                                     \
+    else                                                                                                     \
+      hipLaunchKernelGGL((decode_f8f4_kernel<FMT, NQ, W, D, false>), grid, dim3(64 * W), lds, stream, x, m, k, \
+                         codes, scales, ts, n, la, lb, r, lparts, lsw, lsync, y, part, cnt, c.splits, c.sps, nsteps, \
+                         ntiles, scales16, (uint64_t)0);                                                     \
+  } while (0)
   if (c.nw == 4) {
     if (c.depth <= 8) FP4W_DQ(4, 8); else FP4W_DQ(4, 16);
   } else if (c.nw == 8 || (FMT == FMT_NVFP4 && NQ > 1)) {
@@ -479,7 +654,7 @@ static void launch_nq(const DecodeConfig& c, dim3 grid, size_t lds, hipStream_t 
 
 hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c0, const void* x, int64_t m, int64_t k,
                               const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t n,
-                              const float* tp, int parts, const void* lb, int r, void* y, float* part,
+                              const void* la, const void* lb, int r, uint32_t* lsync, void* y, float* part,
                               uint32_t* cnt, hipStream_t stream) {
   DecodeConfig c = c0;
   const int nq = fmt == FMT_NVFP4 ? (int)m : (int)((m + 7) / 8);
@@ -488,13 +663,17 @@ hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c0, const void* x, in
   const int ntiles = (int)((n + DQ_ROWS - 1) / DQ_ROWS);
   const int nsteps = (int)((k + DQ_STEP - 1) / DQ_STEP);
   const int kslice = c.sps * DQ_STEP;
-  const int rr = tp ? r : 0;
+  const int rr = la && lb && k > 0 ? r : 0;        // k = 0: t = x A^T is zero
   const size_t lds = decode_f8f4_lds_bytes(fmt, m, kslice, c.nw, rr);
-  if (lds > 64 * 1024 || rr > DQ_MAX_R) return hipErrorInvalidValue;
+  if (lds > 64 * 1024 || rr > DQ_MAX_R || m * rr > 1024) return hipErrorInvalidValue;
+  // chunk workgroups of the LoRA down-projection go first in the grid
+  const int lsw = rr > 0 ? dq_lora_steps(c.nw, k, (int)m * rr) : DQ_LSPW;
+  const int lparts = rr > 0 ? (int)(((k + 31) / 32 + (int64_t)lsw * c.nw - 1) / ((int64_t)lsw * c.nw)) : 0;
+  const dim3 grid((unsigned)(lparts + (int64_t)ntiles * c.splits));
   const int scales16 = ((reinterpret_cast<uintptr_t>(scales) & 15u) == 0 && (k / blk) % 16 == 0 &&
                         (kslice / blk) % 16 == 0) ? 1 : 0;
-  const dim3 grid((unsigned)((int64_t)ntiles * c.splits));
   const uint16_t* xx = reinterpret_cast<const uint16_t*>(x);
+  const uint16_t* aa = rr > 0 ? reinterpret_cast<const uint16_t*>(la) : nullptr;
   const uint16_t* bb = reinterpret_cast<const uint16_t*>(lb);
   uint16_t* yy = reinterpret_cast<uint16_t*>(y);
   const int mm = (int)m;
@@ -502,8 +681,8 @@ hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c0, const void* x, in
     switch (mm) {
 #define FP4W_NQ(Q_)                                                                                        \
   case Q_:                                                                                                 \
-    launch_nq<FMT_NVFP4, Q_>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, tp, parts, bb, rr, yy, part, cnt, \
-                             nsteps, ntiles, scales16);                                                    \
+    launch_nq<FMT_NVFP4, Q_>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, aa, bb, rr, lparts, lsw, lsync, \
+                             yy, part, cnt, nsteps, ntiles, scales16);                                     \
     break;
       FP4W_NQ(1) FP4W_NQ(2) FP4W_NQ(3) FP4W_NQ(4) FP4W_NQ(5) FP4W_NQ(6) FP4W_NQ(7) FP4W_NQ(8)
 #undef FP4W_NQ
@@ -511,11 +690,11 @@ hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c0, const void* x, in
     }
   } else {
     if (mm <= 8)
-      launch_nq<FMT_MXFP4, 1>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, tp, parts, bb, rr, yy, part, cnt,
-                              nsteps, ntiles, scales16);
+      launch_nq<FMT_MXFP4, 1>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, aa, bb, rr, lparts, lsw, lsync, yy,
+                              part, cnt, nsteps, ntiles, scales16);
     else
-      launch_nq<FMT_MXFP4, 2>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, tp, parts, bb, rr, yy, part, cnt,
-                              nsteps, ntiles, scales16);
+      launch_nq<FMT_MXFP4, 2>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, aa, bb, rr, lparts, lsw, lsync, yy,
+                              part, cnt, nsteps, ntiles, scales16);
   }
   return hipSuccess;
 }

@@ -19,13 +19,25 @@ hipError_t launch_merge_scales(int fmt, const uint8_t* scales_in, const float* d
 
 // Linear (dense).  The plan fixes the kernel shape and the workspace layout:
 //   [counters: kCounterSlots u32, fixed][t: m x r fp32][t partials][split-K partials]
-// The arrival counters sit at fixed offsets for every shape, so a counter a call
-// returns to zero is zero for the next call whatever its shape.  Slots
-// [0, kLoraSlots) serve the LoRA down-projection's m-tiles, the rest the
-// decode kernel's weight tiles; the planner only splits when the tiles fit.
-constexpr int kCounterSlots = 2048;
+// The counter area sits at a fixed offset for every shape and every word of it
+// is zero between calls (a call returns what it used to zero), so whatever the
+// previous call's shape, the next one finds it cleared.  Slots:
+//   [0, kLoraSlots)            arrival counters of the LoRA down-projection's m-tiles
+//   [kLoraSlots, kTileBase + kTileSlots)  the decode kernels' weight tiles
+//   [kLsyncBase, kCounterSlots) the block-scaled decode kernel's LoRA hand-over:
+//       the chunk partials of t (up to kLsyncWords, stored complemented so that
+//       zero means "not yet written"), and arrival counters: one per 128-byte
+//       line for the workgroups that read them (kLsyncSubs), one on top.
 constexpr int kLoraSlots = 16;
-constexpr int kTileSlots = kCounterSlots - kLoraSlots;
+constexpr int kTileBase = kLoraSlots;
+constexpr int kTileSlots = 2048 - kLoraSlots;
+constexpr int kLsyncBase = 2048;
+constexpr int kLsyncWords = 4096;       // chunk partials: chunks x m x r
+constexpr int kLsyncTop = kLsyncWords;  // completed reader groups, then producers
+constexpr int kLsyncSub = kLsyncTop + 32;
+constexpr int kLsyncSubs = 32;          // reader arrivals, group c at kLsyncSub + 32 c
+constexpr int kLsyncSlots = kLsyncSub + 32 * kLsyncSubs;
+constexpr int kCounterSlots = kLsyncBase + kLsyncSlots;
 
 // Decode kernel on the block-scaled matrix core (decode.hip): a workgroup of
 // `nw` waves per tile of 16 weight rows, `splits` slices of K of `sps`
@@ -39,12 +51,16 @@ struct DecodeConfig {
 bool decode_f8f4_supports(int fmt, int64_t m);
 DecodeConfig plan_decode_f8f4(int fmt, int64_t m, int64_t n, int64_t k, int r);
 size_t decode_f8f4_lds_bytes(int fmt, int64_t m, int kslice, int nw, int r);
-// tp: LoRA partials [parts][m][r] fp32 (x A^T per K chunk), or nullptr
+// bound on the decode kernel's wait for the published t (ticks of the 100 MHz clock)
+int64_t lora_wait_ticks();
+int64_t set_lora_wait_ticks(int64_t ticks);      // returns the previous bound
+// la / lb: LoRA A (r x k bf16) and B (n x r bf16), or nullptr (no LoRA); the
+// kernel forms t = x A^T itself (K chunks in workgroups of their own, handed
+// over through lsync: the kLsyncSlots words of the counter area from kLsyncBase)
 hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c, const void* x, int64_t m, int64_t k,
                               const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t n,
-                              const float* tp, int parts, const void* lb, int r, void* y, float* part,
+                              const void* la, const void* lb, int r, uint32_t* lsync, void* y, float* part,
                               uint32_t* cnt, hipStream_t stream);
-int lora_part_count(int64_t k);
 
 // Decode kernel with x held in registers (decode_xs.hip): K in `splits` spans of
 // `qspan` 32-wide groups, `nw` waves per workgroup, weight tiles of 16 rows.

@@ -5,11 +5,15 @@
 // memory-bound (same post, "Eksperimenty"); the product runs on 16-bit values
 // (QATFactory page, section on how training repeats the engine's arithmetic).
 //
-// Launches per call:
-//   1. lora_down_kernel      t = x A^T (fp32, M x r), split over K, ordered sum
-//   2. m <= 16: linear_decode_kernel (decode-shaped, HBM-bound; skinny.hpp)
-//      m >  16: linear_gemm_kernel   (LDS-staged bf16 MFMA GEMM, dequantizing
-//                                      each weight tile once into LDS)
+// Launches per call (plan_linear picks the path):
+//   m = 1:       decode_f8f4_kernel (decode.hip; forms t = x A^T itself)
+//   2 <= m <= 16: decode_xs_kernel  (decode_xs.hip; forms t itself for r <= 16,
+//                                    after lora_down_kernel for larger ranks)
+//   m > 16:      lora_down_kernel, then linear_gemm_kernel (LDS-staged bf16 MFMA
+//                GEMM, dequantizing each weight tile once into LDS)
+//   shapes the decode kernels do not take: lora_down_kernel, then
+//                linear_decode_kernel (skinny.hpp)
+// lora_down_kernel: t = x A^T (fp32, M x r), split over K, ordered sum.
 // Split-K partial sums are combined by the last workgroup to arrive, in a fixed
 // order, so results do not depend on scheduling.  Its arrival counters live in
 // the caller's workspace and are returned to zero by that last workgroup.
@@ -93,68 +97,6 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restri
   }
 }
 
-// ---------------------------------------------------------------------------------
-// LoRA down-projection for the decode path (m <= 16): partials only.  Workgroup p
-// owns 4 * SPW consecutive 32-wide K steps (each wave SPW of them, every load in
-// flight at once) and writes tp[p] = x[:, chunk p] A[:, chunk p]^T (m x r fp32).
-// The decode kernel adds the partials in chunk order while it stages, so no
-// arrival counter and no second pass are needed here.
-// ---------------------------------------------------------------------------------
-constexpr int LP_SPW = 8;
-constexpr int LP_STEPS = 4 * LP_SPW;      // 32-wide K steps per workgroup
-
-template <int RB>
-__global__ __launch_bounds__(256) void lora_part_kernel(const uint16_t* __restrict__ x, int M, int64_t K,
-                                                        const uint16_t* __restrict__ a, int r,
-                                                        float* __restrict__ tp) {
-  __shared__ float red[4 * RB * 4 * 64];
-  const int p = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 15, g = lane >> 4;
-  const int64_t step0 = ((int64_t)p * 4 + wave) * LP_SPW;
-  const bool xrow_ok = li < M;
-  u32x4_t xa[LP_SPW], av[LP_SPW][RB];
-#pragma unroll
-  for (int s = 0; s < LP_SPW; s++) {
-    const int64_t k = (step0 + s) * 32 + 8 * g;
-    const bool kin = k < K;
-    const int64_t kc = kin ? k : 0;
-    xa[s] = load16(x + (xrow_ok ? (int64_t)li * K : 0) + kc);
-    if (!(kin && xrow_ok)) xa[s] = (u32x4_t){0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int b = 0; b < RB; b++) {
-      const int j = b * 16 + li;
-      av[s][b] = load16(a + (j < r ? (int64_t)j * K : 0) + kc);
-      if (!(kin && j < r)) av[s][b] = (u32x4_t){0u, 0u, 0u, 0u};
-    }
-  }
-  f32x4_t acc[RB];
-#pragma unroll
-  for (int b = 0; b < RB; b++) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < LP_SPW; s++)
-#pragma unroll
-    for (int b = 0; b < RB; b++)
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[s]), as_bf16x8(av[s][b]), acc[b], 0, 0, 0);
-  // D row 4 g + i = m, column li = j within block b
-#pragma unroll
-  for (int b = 0; b < RB; b++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) red[((wave * RB + b) * 4 + i) * 64 + lane] = acc[b][i];
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int b = 0; b < RB; b++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float v = ((red[((0 * RB + b) * 4 + i) * 64 + lane] + red[((1 * RB + b) * 4 + i) * 64 + lane]) +
-                         red[((2 * RB + b) * 4 + i) * 64 + lane]) + red[((3 * RB + b) * 4 + i) * 64 + lane];
-        const int m = 4 * g + i, j = b * 16 + li;
-        if (m < M && j < r) tp[((int64_t)p * M + m) * r + j] = v;
-      }
-  }
-}
-
-int lora_part_count(int64_t k) { return (int)(((k + 31) / 32 + LP_STEPS - 1) / LP_STEPS); }
 
 // ---------------------------------------------------------------------------------
 // Decode-shaped linear (m <= 16).
@@ -585,9 +527,7 @@ LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
     p.xs = plan_decode_xs(m, n, k, r);
     if (p.xs.splits > 1 && (p.xs.ntiles + 7) / 8 > kTileSlots) p.path = 1;     // counters would not fit
   }
-  // decode path: per-chunk LoRA partials, summed by the decode kernel
   const bool xs_fused = p.path == 3 && r <= decode_xs_fused_rank();     // the kernel forms t itself
-  p.lora_parts = r <= 0 || xs_fused ? 0 : p.path == 0 ? lora_part_count(k) : lora_parts_for(m, k);
   size_t part_floats = 0;
   if (p.path == 3) {
     p.splits = p.xs.splits;
@@ -605,14 +545,19 @@ LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
     part_floats = (size_t)p.splits * n * m;
   }
   if (p.path == 1) p.splits = 1;
+  // LoRA down-projection: formed inside the block-scaled decode kernel (path 0)
+  // or the x-in-registers kernel (path 3, r <= its fused rank), without
+  // workspace beyond the counter area; else by lora_down_kernel (K slices,
+  // ordered sum) into t
+  const bool lora_inside = xs_fused || p.path == 0;
+  p.lora_parts = r <= 0 || lora_inside ? 0 : lora_parts_for(m, k);
   size_t off = 0;
   p.off_count = off;
   off += sizeof(uint32_t) * kCounterSlots;
   p.off_t = off;
-  if (r > 0 && !xs_fused) {
+  if (r > 0 && !lora_inside) {
     off += align256(sizeof(float) * (size_t)m * (size_t)r);                           // t
-    if (p.lora_parts > 1 || p.path == 0)
-      off += align256(sizeof(float) * (size_t)p.lora_parts * m * r);                  // partials
+    if (p.lora_parts > 1) off += align256(sizeof(float) * (size_t)p.lora_parts * m * r);   // partials
   }
   p.off_part = off;
   if (p.splits > 1) off += align256(sizeof(float) * part_floats);
@@ -674,23 +619,14 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   const bool has_lora = r > 0 && lora_a && lora_b;
   float* t = has_lora ? reinterpret_cast<float*>(ws + plan.off_t) : nullptr;
-  float* tp = (has_lora && (plan.lora_parts > 1 || plan.path == 0))
+  float* tp = (has_lora && plan.lora_parts > 1)
                   ? reinterpret_cast<float*>(ws + plan.off_t + align256(sizeof(float) * (size_t)m * r))
                   : nullptr;
   float* part = reinterpret_cast<float*>(ws + plan.off_part);
   uint32_t* cnt_m = reinterpret_cast<uint32_t*>(ws + plan.off_count);
   uint32_t* cnt_n = cnt_m + kLoraSlots;
-  if (has_lora && plan.path == 0) {
-    const int P = plan.lora_parts;
-    const uint16_t* xx = reinterpret_cast<const uint16_t*>(x);
-    const uint16_t* aa = reinterpret_cast<const uint16_t*>(lora_a);
-    switch ((r + 15) / 16) {
-      case 1: hipLaunchKernelGGL(lora_part_kernel<1>, dim3(P), dim3(256), 0, stream, xx, (int)m, k, aa, r, tp); break;
-      case 2: hipLaunchKernelGGL(lora_part_kernel<2>, dim3(P), dim3(256), 0, stream, xx, (int)m, k, aa, r, tp); break;
-      case 3: hipLaunchKernelGGL(lora_part_kernel<3>, dim3(P), dim3(256), 0, stream, xx, (int)m, k, aa, r, tp); break;
-      default: hipLaunchKernelGGL(lora_part_kernel<4>, dim3(P), dim3(256), 0, stream, xx, (int)m, k, aa, r, tp); break;
-    }
-  } else if (has_lora && !(plan.path == 3 && r <= decode_xs_fused_rank())) {
+  // t = x A^T for the paths that do not form it inside their decode kernel
+  if (has_lora && plan.path != 0 && !(plan.path == 3 && r <= decode_xs_fused_rank())) {
     const int64_t nsteps = (k + 31) / 32;
     const int P = plan.lora_parts;
     const int spp = (int)((nsteps + P - 1) / P);
@@ -700,8 +636,9 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
                        spp, tp, t, cnt_m);
   }
   if (plan.path == 0) {
-    hipError_t e = launch_decode_f8f4(fmt, plan.dq, x, m, k, codes, scales, tensor_scale, n, tp, plan.lora_parts,
-                                      lora_b, r, y, part, cnt_n, stream);
+    hipError_t e = launch_decode_f8f4(fmt, plan.dq, x, m, k, codes, scales, tensor_scale, n,
+                                      has_lora ? lora_a : nullptr, has_lora ? lora_b : nullptr, r,
+                                      cnt_m + kLsyncBase, y, part, cnt_n, stream);
     if (e != hipSuccess) return e;
   } else if (plan.path == 3) {
     const bool fused = r <= decode_xs_fused_rank();

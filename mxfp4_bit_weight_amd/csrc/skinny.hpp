@@ -34,8 +34,6 @@ constexpr int SK_THREADS = 64 * SK_WAVES;
 constexpr int SK_TILE_N = 16;
 constexpr int SK_STEP_K = 128;
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
-
 // 8 codes (one dword) -> 8 bf16 B-operand values, scaled by the power of two `pow2`.
 __device__ __forceinline__ bf16x8_t codes8_to_bf16(uint32_t dw, float pow2) {
   u32x4_t r;

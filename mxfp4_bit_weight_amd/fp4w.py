@@ -19,6 +19,8 @@ BLOCK = {NVFP4: 16, MXFP4: 32}
 FROZEN_SCALES = 0x1
 OUT_FP32 = 0x2
 MAX_LORA_RANK = 64
+# the workspace's first bytes: arrival counters and LoRA hand-over words, zero between calls
+WORKSPACE_COUNTER_BYTES = 28800
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp4w.so")
@@ -46,9 +48,11 @@ _grouped = _sig("fp4w_grouped_linear", _int, _int, _p, _i64, _p, _p, _i64, _i64,
 _merge = _sig("fp4w_merge_scales", _int, _int, _p, _p, _i64, _p, _p, _p, _i64, _p)
 _status = _sig("fp4w_status_string", ctypes.c_char_p, _int)
 _version = _sig("fp4w_version", _int)
+_debug_lora_wait = _sig("fp4w_debug_lora_wait", _i64, _i64)
 
 EXPORTED = ["fp4w_quantize", "fp4w_dequantize", "fp4w_linear_workspace_bytes", "fp4w_linear",
-            "fp4w_grouped_linear", "fp4w_merge_scales", "fp4w_status_string", "fp4w_version"]
+            "fp4w_grouped_linear", "fp4w_merge_scales", "fp4w_status_string", "fp4w_version",
+            "fp4w_debug_lora_wait"]
 
 
 class Fp4wError(RuntimeError):
@@ -68,6 +72,13 @@ def status_string(status: int) -> str:
 
 def version() -> int:
     return _version()
+
+
+def debug_lora_wait(ticks: int = -1) -> int:
+    """Test hook: bound (100 MHz ticks) on the m = 1 decode kernel's wait for a
+    published LoRA product before it forms the product itself; < 0 only queries.
+    Returns the previous bound."""
+    return int(_debug_lora_wait(int(ticks)))
 
 
 def _ptr(t: Optional[torch.Tensor]):

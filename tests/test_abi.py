@@ -52,6 +52,21 @@ def test_workspace_bytes(lib):
     assert lib.linear_workspace_bytes(-1, 10, 64, 0) == 0
 
 
+def test_workspace_covers_the_counter_area(lib):
+    # arrival counters and the LoRA hand-over words sit in the first 28800 bytes
+    assert lib.WORKSPACE_COUNTER_BYTES == 28800
+    assert lib.linear_workspace_bytes(1, 16, 32, 0) == lib.WORKSPACE_COUNTER_BYTES
+
+
+def test_lora_wait_hook(lib):
+    prev = lib.debug_lora_wait()
+    assert prev == 100000                                       # 1 ms of the 100 MHz clock
+    assert lib.debug_lora_wait(0) == prev
+    assert lib.debug_lora_wait() == 0
+    assert lib.debug_lora_wait(prev) == 0
+    assert lib.debug_lora_wait() == prev
+
+
 def _fake(addr):
     return ctypes.c_void_p(addr)
 

@@ -58,7 +58,7 @@ def test_linear_graph_replays(fp4w, fmt):
         torch.cuda.synchronize()
         for i, (y, yr) in enumerate(zip(outs, ref)):
             assert torch.equal(y.view(torch.int16), yr.view(torch.int16)), f"replay {rep} case {cases[i]}"
-    assert int(ws[:8192].view(torch.int32).abs().sum().item()) == 0
+    assert int(ws[:fp4w.WORKSPACE_COUNTER_BYTES].view(torch.int32).abs().sum().item()) == 0
 
 
 @pytest.mark.parametrize("fmt", [0, 1])

@@ -115,8 +115,8 @@ def test_workspace_counters_return_to_zero_and_determinism(fp4w):
     y2 = fp4w.linear(xd, q, ad, bd, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
-    # the first 8 KiB hold the arrival counters; all must be zero again
-    counters = ws[:8192].view(torch.int32)
+    # the counter area (arrival counters, LoRA hand-over words) must be zero again
+    counters = ws[:fp4w.WORKSPACE_COUNTER_BYTES].view(torch.int32)
     assert int(counters.abs().sum().item()) == 0
 
 
@@ -136,7 +136,7 @@ def test_workspace_reuse_across_shapes(fp4w):
         xn = np.sqrt((f64_of_bf16(x) ** 2).sum(axis=1))[:, None]
         wn = weff_norms(0, codes, scales, st, a, b)[None, :]
         check_bound(f64_of_bf16(bits_host(y)), y64, xn, wn, f"reuse m={m} n={n} k={k}")
-        assert int(ws[:8192].view(torch.int32).abs().sum().item()) == 0
+        assert int(ws[:fp4w.WORKSPACE_COUNTER_BYTES].view(torch.int32).abs().sum().item()) == 0
 
 
 def test_empty_and_tiny(fp4w):

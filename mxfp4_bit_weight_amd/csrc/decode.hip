@@ -44,11 +44,12 @@
 // down-projection runs inside the same launch.  The grid's first workgroups
 // stream no codes: workgroup p forms the partial of K chunk p on the bf16
 // matrix core (each wave a run of 32-wide steps, waves added in order) and
-// stores it, complemented so that a zero word reads as "not yet written".  A
-// workgroup writing outputs waits for every chunk word with a bounded poll and
-// adds the chunks in chunk order; were the wait ever to run out, it forms the
-// chunks itself by the same steps in the same order, so the value is the same
-// either way.  The chunk workgroups wait on nothing, so the wait ends.  The
+// stores it, complemented so that a zero word reads as "not yet written".  In
+// every other workgroup, the first wave done with its share of the codes waits
+// for every chunk word with a bounded poll (its sibling waves still stream) and
+// adds the chunks in chunk order; were the wait ever to run out, the
+// workgroup forms the chunks itself by the same steps in the same order, so
+// the value is the same either way.  The chunk workgroups wait on nothing, so the wait ends.  The
 // hand-over words return to zero before the kernel ends: the readers arrive on
 // 32 counters a cache line apart, the completed groups and the chunk
 // workgroups (after their stores have landed) on one more, and the arrival
@@ -132,23 +133,23 @@ __device__ __forceinline__ void lsync_top_arrive(uint32_t* ls, uint32_t expected
   }
 }
 
-__device__ __forceinline__ uint32_t lsync_top_expected(int ntiles, int lparts) {
-  return (uint32_t)((ntiles < kLsyncSubs ? ntiles : kLsyncSubs) + lparts);
+__device__ __forceinline__ uint32_t lsync_top_expected(int nread, int lparts) {
+  return (uint32_t)((nread < kLsyncSubs ? nread : kLsyncSubs) + lparts);
 }
 
-// One wave of the workgroup that writes the outputs of `tile`, after its loads of
-// the chunk words have returned.
-__device__ __forceinline__ void lsync_reader_arrive(uint32_t* ls, int tile, int ntiles, int lparts, int words,
+// One wave of reader workgroup `rd` of `nread`, after its loads of the chunk
+// words have returned.
+__device__ __forceinline__ void lsync_reader_arrive(uint32_t* ls, int rd, int nread, int lparts, int words,
                                                     int lane) {
-  const int c = tile % kLsyncSubs;
-  const uint32_t quota = (uint32_t)(ntiles / kLsyncSubs + (c < ntiles % kLsyncSubs ? 1 : 0));
+  const int c = rd % kLsyncSubs;
+  const uint32_t quota = (uint32_t)(nread / kLsyncSubs + (c < nread % kLsyncSubs ? 1 : 0));
   uint32_t old = 0;
   if (lane == 0) {
     old = lsync_add(&ls[kLsyncSub + 32 * c]);
     if (old == quota - 1u) lsync_store(&ls[kLsyncSub + 32 * c], 0u);
   }
   old = (uint32_t)__shfl((int)old, 0, 64);
-  if (old == quota - 1u) lsync_top_arrive(ls, lsync_top_expected(ntiles, lparts), words, lane);
+  if (old == quota - 1u) lsync_top_arrive(ls, lsync_top_expected(nread, lparts), words, lane);
 }
 
 template <int FMT, int NQ, int NW, int DEPTH, bool LORA>
@@ -161,6 +162,7 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
     uint64_t wait_ticks) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int flag;
+  __shared__ int lfin, have_t;                                    // LoRA: waves done streaming; t published
   constexpr int NT = 64 * NW;
   constexpr int BLK = FMT == FMT_NVFP4 ? 16 : 32;
   // staging units per thread whose loads are issued before the ring (the rest,
@@ -175,6 +177,7 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
   const DqLayout L = dq_layout(FMT, M, sps * DQ_STEP, NW, rr);
   const int bid = (int)blockIdx.x - lparts;                       // < 0: a LoRA chunk workgroup
   const int s = bid % S, tile = bid / S;
+  const int nread = ntiles * S;                                   // LoRA: every tile workgroup reads t
   // ---- LoRA chunk p: wave w takes the lsw 32-wide K steps from (p NW + w) lsw
   //      on v_mfma_f32_16x16x32_bf16, x rows as A (row = lane % 16), A's rows as B
   //      (column j = 16 b + lane % 16); lane (j, g) gets rows m = 4 g + i.  Loads
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
     if (wave == 0) {
       for (int e = lane; e < mr; e += 64) lsync_store(&lsync[p * mr + e], ~__float_as_uint(chunk_value(e)));
       wait_stores_complete();
-      lsync_top_arrive(lsync, lsync_top_expected(ntiles, lparts), words, lane);
+      lsync_top_arrive(lsync, lsync_top_expected(nread, lparts), words, lane);
     }
     return;
   }
@@ -349,6 +352,7 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
   }
   if (rr > 0) {
     uint16_t* lb = reinterpret_cast<uint16_t*>(lds + L.lb_off);
+    if (tid == 0) lfin = 0;
     if (tid < DQ_ROWS * rr) lb[tid] = (uint16_t)lbv;
     for (int e = tid + NT; e < DQ_ROWS * rr; e += NT) {
       const int rw = e / rr, j = e - rw * rr;
@@ -473,6 +477,42 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
       for (int i = 0; i < 4; i++) v[q][i] = acc[q][i] + __shfl_xor(acc[q][i], 32, 64);
   }
 
+  if (LORA) {
+    // ---- 4b. the first wave done with its part fetches the chunk words of t
+    //      (bounded wait) and adds them in chunk order while the others stream;
+    //      then it arrives ------------------------------------------------------
+    int first = 0;
+    if (lane == 0) first = atomicAdd(&lfin, 1) == 0;
+    first = __shfl(first, 0, 64);
+    if (first) {
+      float* lt = reinterpret_cast<float*>(lds + L.lt_off);
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      int ok;
+      for (;;) {
+        int mine = 1;
+        for (int q = lane; q < mr; q += 64) {
+          float t = 0.f;
+          for (int p0 = 0; p0 < lparts; p0 += 8) {
+            uint32_t w[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) w[i] = p0 + i < lparts ? lsync_load(&lsync[(p0 + i) * mr + q]) : ~0u;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+              if (w[i] == 0u) mine = 0;
+              if (p0 + i < lparts) t += __uint_as_float(~w[i]);
+            }
+          }
+          lt[q] = t;
+        }
+        ok = __all(mine);
+        if (ok || __builtin_amdgcn_s_memrealtime() - t0 >= wait_ticks) break;
+        __builtin_amdgcn_s_sleep(8);
+      }
+      if (lane == 0) have_t = ok;
+      lsync_reader_arrive(lsync, bid, nread, lparts, words, lane);
+    }
+  }
+
   // ---- 5. wave partials -> LDS, tile sums in wave order --------------------------
   float* red = reinterpret_cast<float*>(lds + L.red_off);      // [wave][m][16]
   if (FMT == FMT_NVFP4) {
@@ -507,47 +547,18 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
       o = sum;
     }
   }
-  if (LORA) {
-    // ---- 6. t: the published chunks added in chunk order (bounded wait), else
-    //      the chunks formed here by the same steps ------------------------------
-    __shared__ int have_t;
+  if (LORA && __builtin_expect(!have_t, 0)) {
+    // ---- 6. the wait for t ran out: the chunks formed here, by the same steps in
+    //      the same order -----------------------------------------------------------
     float* lt = reinterpret_cast<float*>(lds + L.lt_off);
-    if (wave == 0) {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      int ok;
-      for (;;) {
-        int mine = 1;
-        for (int q = lane; q < mr; q += 64) {
-          float t = 0.f;
-          for (int p0 = 0; p0 < lparts; p0 += 8) {
-            uint32_t w[8];
-#pragma unroll
-            for (int i = 0; i < 8; i++) w[i] = p0 + i < lparts ? lsync_load(&lsync[(p0 + i) * mr + q]) : ~0u;
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-              if (w[i] == 0u) mine = 0;
-              if (p0 + i < lparts) t += __uint_as_float(~w[i]);
-            }
-          }
-          lt[q] = t;
-        }
-        ok = __all(mine);
-        if (ok || __builtin_amdgcn_s_memrealtime() - t0 >= wait_ticks) break;
-        __builtin_amdgcn_s_sleep(8);
-      }
-      if (lane == 0) have_t = ok;
-    }
-    __syncthreads();
-    if (__builtin_expect(!have_t, 0)) {
+    if (wave == 0)
+      for (int q = lane; q < mr; q += 64) lt[q] = 0.f;
+    for (int p = 0; p < lparts; p++) {
+      lora_chunk(p);
+      __syncthreads();
       if (wave == 0)
-        for (int q = lane; q < mr; q += 64) lt[q] = 0.f;
-      for (int p = 0; p < lparts; p++) {
-        lora_chunk(p);
-        __syncthreads();
-        if (wave == 0)
-          for (int q = lane; q < mr; q += 64) lt[q] += chunk_value(q);
-        __syncthreads();
-      }
+        for (int q = lane; q < mr; q += 64) lt[q] += chunk_value(q);
+      __syncthreads();
     }
   }
   if (e < nout) {
@@ -566,8 +577,6 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
       y[(int64_t)m * N + row] = (uint16_t)f32_to_bf16_rne(out);
     }
   }
-  // the chunk words have been read (or were not needed): arrive
-  if (LORA && wave == 0) lsync_reader_arrive(lsync, tile, ntiles, lparts, words, lane);
 }
 
 // ---------------------------------------------------------------------------------

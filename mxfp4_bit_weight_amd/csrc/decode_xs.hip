@@ -100,24 +100,25 @@ __device__ __forceinline__ bf16x8_t codes8_to_bf16_pow2(uint32_t dw, float pow2)
   return bits_as_bf16x8(r);
 }
 
+// The product of one workgroup: span s of K, tile run gi, M <= 16 rows of x.
 // SC: 1 = the block scales of the tiles are staged in LDS by the whole workgroup with
 // 16-byte loads (each scale line is fetched once); 0 = every lane loads its own
-// bytes (any alignment).
+// bytes (any alignment).  xrow: nullptr = row m of x is x[m]; otherwise row m is
+// x[xrow[m]] of xrows rows, and a row index outside [0, xrows) makes the output
+// row NaN (the routed rows of an expert).
 template <int FMT, int TG, int SC>
-__global__ __launch_bounds__(64 * XS_MAX_WAVES) void decode_xs_kernel(
-    const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ codes,
+__device__ __forceinline__ void xs_body(
+    uint8_t* __restrict__ lds, int* flag, const uint16_t* __restrict__ x, const int32_t* __restrict__ xrow,
+    int64_t xrows, int M, int64_t K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t N,
     const uint16_t* __restrict__ lora_a, const float* __restrict__ t_lora, const uint16_t* __restrict__ lora_b,
     int r, uint16_t* __restrict__ y, float* __restrict__ part, uint32_t* __restrict__ cnt, int S, int qspan,
-    int ntiles, int G, int tg, int lb16) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int flag;
+    int ntiles, int G, int tg, int lb16, int s, int gi) {
   constexpr int CPW = XS_CPW;
   const int nt = (int)blockDim.x;
   const int nw = nt >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // uniform: buffer descriptors stay scalar
-  const int s = (int)(blockIdx.x % (unsigned)S), gi = (int)(blockIdx.x / (unsigned)S);
   // tiles gi, gi + G, gi + 2 G, ...: at each step the G runs read one contiguous
   // stretch of the weight matrix
   const int ntg = (ntiles - gi + G - 1) / G;                         // 1 .. tg <= TG
@@ -144,12 +145,15 @@ __global__ __launch_bounds__(64 * XS_MAX_WAVES) void decode_xs_kernel(
   // Every load below is issued unconditionally (a lane or tile with nothing to
   // read gets an offset past its buffer), so the compiler's wait counts stay
   // exact and no wait drains loads that are not needed yet.
-  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (uint32_t)((int64_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (uint32_t)(xrows * K * 2));
+  int64_t xr = n;                                // the row of x lane row n reads
+  if (xrow) xr = n < M ? (int64_t)xrow[n] : -1;
+  const bool xr_ok = n < M && xr >= 0 && xr < xrows;
   u32x4_t xa[CPW][4];
 #pragma unroll
   for (int u = 0; u < CPW; u++) {
-    const bool ok = (n < M) & qok[u];
-    const uint32_t base = (uint32_t)(n * K + 32 * (int64_t)qv[u]) * 2u;
+    const bool ok = xr_ok & qok[u];
+    const uint32_t base = (uint32_t)((xr_ok ? xr : 0) * K + 32 * (int64_t)qv[u]) * 2u;
 #pragma unroll
     for (int sub = 0; sub < 4; sub++) xa[u][sub] = buffer_load16(xrs, ok ? base + 16u * sub : kBufferOob);
   }
@@ -248,6 +252,7 @@ __global__ __launch_bounds__(64 * XS_MAX_WAVES) void decode_xs_kernel(
         const uint32_t m2 = a > b ? a : b;
         mx = m2 > mx ? m2 : mx;
       }
+  if (xrow && n < M && !xr_ok) mx = 0x7F80u;     // a routed row without a valid token: NaN outputs
   {
     uint32_t o = (uint32_t)__shfl_xor((int)mx, 16, 64);
     mx = o > mx ? o : mx;
@@ -427,7 +432,7 @@ __global__ __launch_bounds__(64 * XS_MAX_WAVES) void decode_xs_kernel(
     }
   }
   if (S > 1) {
-    if (!arrive_last(&cnt[gi], (uint32_t)S, &flag)) return;
+    if (!arrive_last(&cnt[gi], (uint32_t)S, flag)) return;
     for (int e = tid; e < nout; e += nt) {
       float v = 0.f;
       const int ti = e / per_tile, rem = e - ti * per_tile;
@@ -437,6 +442,51 @@ __global__ __launch_bounds__(64 * XS_MAX_WAVES) void decode_xs_kernel(
       out_index(e, m, row);
       if (row < N) y[(int64_t)m * N + row] = (uint16_t)f32_to_bf16_rne(v);
     }
+  }
+}
+
+template <int FMT, int TG, int SC>
+__global__ __launch_bounds__(64 * XS_MAX_WAVES) void decode_xs_kernel(
+    const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t N,
+    const uint16_t* __restrict__ lora_a, const float* __restrict__ t_lora, const uint16_t* __restrict__ lora_b,
+    int r, uint16_t* __restrict__ y, float* __restrict__ part, uint32_t* __restrict__ cnt, int S, int qspan,
+    int ntiles, int G, int tg, int lb16) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int flag;
+  const int s = (int)(blockIdx.x % (unsigned)S), gi = (int)(blockIdx.x / (unsigned)S);
+  xs_body<FMT, TG, SC>(lds, &flag, x, nullptr, M, M, K, codes, scales, tensor_scale, N, lora_a, t_lora, lora_b, r, y,
+                       part, cnt, S, qspan, ntiles, G, tg, lb16, s, gi);
+}
+
+// ---------------------------------------------------------------------------------
+// Grouped (mixture of experts): workgroup (expert e, tile run gi) takes the
+// expert's routed rows [offsets[e], offsets[e+1]) 16 at a time, each chunk
+// against the run's tiles of W_e, K in one span.  The routing stays on the
+// device: an expert with no rows returns at once.
+// ---------------------------------------------------------------------------------
+template <int FMT, int TG, int SC>
+__global__ __launch_bounds__(64 * XS_MAX_WAVES) void grouped_xs_kernel(
+    const uint16_t* __restrict__ x, int64_t num_tokens, const int32_t* __restrict__ row_index,
+    const int32_t* __restrict__ offsets, int64_t total_rows, int64_t N, int64_t K,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const float* __restrict__ tscales,
+    uint16_t* __restrict__ y, int qspan, int ntiles, int G, int tg) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int flag;
+  const int64_t e = blockIdx.x / (unsigned)G;
+  const int gi = (int)(blockIdx.x % (unsigned)G);
+  int64_t q0 = offsets[e], q1 = offsets[e + 1];
+  q0 = q0 < 0 ? 0 : (q0 > total_rows ? total_rows : q0);
+  q1 = q1 > total_rows ? total_rows : q1;
+  constexpr int64_t BLK = FMT == FMT_NVFP4 ? 16 : 32;
+  const uint8_t* ce = codes + e * N * (K / 2);
+  const uint8_t* se = scales + e * N * (K / BLK);
+  const float* te = FMT == FMT_NVFP4 ? tscales + e : nullptr;
+  for (; q0 < q1; q0 += XS_MAX_M) {
+    const int mc = (int)(q1 - q0 < XS_MAX_M ? q1 - q0 : XS_MAX_M);
+    xs_body<FMT, TG, SC>(lds, &flag, x, row_index + q0, num_tokens, mc, K, ce, se, te, N, nullptr, nullptr, nullptr,
+                         0, y + q0 * N, nullptr, nullptr, 1, qspan, ntiles, G, tg, 0, 0, gi);
+    __syncthreads();                             // LDS is reused by the next chunk
   }
 }
 
@@ -566,6 +616,82 @@ hipError_t launch_decode_xs(int fmt, const XsConfig& c, const void* x, int64_t m
                                     cnt, c, (int)G, (int)tg, lb16, sc);
   return launch_xs_fmt<FMT_MXFP4>(grid, block, lds, stream, xx, (int)m, k, codes, scales, ts, n, aa, tt, bb, rr, yy, part,
                                   cnt, c, (int)G, (int)tg, lb16, sc);
+}
+
+// ---- grouped ------------------------------------------------------------------------
+bool grouped_xs_supports(int64_t num_tokens, int64_t n, int64_t k) {
+  const int64_t nq = k / 32;
+  return k % 32 == 0 && nq > 0 && nq <= (int64_t)4 * XS_CPW * XS_MAX_WAVES &&     // K in one span
+         n * (k / 2) < ((int64_t)1 << 31) && num_tokens * k * 2 < ((int64_t)1 << 31);
+}
+
+template <int FMT, int TG, int SC>
+static hipError_t launch_gxs_tg(dim3 grid, dim3 block, size_t lds, hipStream_t stream, const uint16_t* x,
+                                int64_t num_tokens, const int32_t* row_index, const int32_t* offsets,
+                                int64_t total_rows, int64_t n, int64_t k, const uint8_t* codes, const uint8_t* scales,
+                                const float* ts, uint16_t* y, int qspan, int ntiles, int G, int tg) {
+  static bool lds_set = false;
+  if (!lds_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_xs_kernel<FMT, TG, SC>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kXsMaxLds);
+    if (e != hipSuccess) return e;
+    lds_set = true;
+  }
+  hipLaunchKernelGGL((grouped_xs_kernel<FMT, TG, SC>), grid, block, lds, stream, x, num_tokens, row_index, offsets,
+                     total_rows, n, k, codes, scales, ts, y, qspan, ntiles, G, tg);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_gxs_fmt(int tg, int sc, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                                 const uint16_t* x, int64_t num_tokens, const int32_t* row_index,
+                                 const int32_t* offsets, int64_t total_rows, int64_t n, int64_t k,
+                                 const uint8_t* codes, const uint8_t* scales, const float* ts, uint16_t* y, int qspan,
+                                 int ntiles, int G) {
+#define FP4W_GXS(TGv, SCv)                                                                                    \
+  launch_gxs_tg<FMT, TGv, SCv>(grid, block, lds, stream, x, num_tokens, row_index, offsets, total_rows, n, k, \
+                               codes, scales, ts, y, qspan, ntiles, G, tg)
+  if (sc) {
+    if (tg <= 1) return FP4W_GXS(1, 1);
+    if (tg <= 2) return FP4W_GXS(2, 1);
+    if (tg <= 4) return FP4W_GXS(4, 1);
+    return FP4W_GXS(6, 1);
+  }
+  if (tg <= 1) return FP4W_GXS(1, 0);
+  if (tg <= 2) return FP4W_GXS(2, 0);
+  if (tg <= 4) return FP4W_GXS(4, 0);
+  return FP4W_GXS(6, 0);
+#undef FP4W_GXS
+}
+
+hipError_t launch_grouped_xs(int fmt, const void* x, int64_t num_tokens, const int32_t* row_index,
+                             const int32_t* expert_offsets, int64_t num_experts, int64_t total_rows, int64_t n,
+                             int64_t k, const uint8_t* codes, const uint8_t* scales, const float* tensor_scales,
+                             void* y, hipStream_t stream) {
+  const XsConfig c = plan_decode_xs(XS_MAX_M, n, k, 0);
+  if (c.splits != 1) return hipErrorInvalidValue;
+  // runs of at most kXsMaxTilesPerGroup tiles per expert
+  const int64_t tg = c.ntiles < kXsMaxTilesPerGroup ? c.ntiles : kXsMaxTilesPerGroup;
+  const int64_t G = (c.ntiles + tg - 1) / tg;
+  if (num_experts * G > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int sb = fmt == FMT_NVFP4 ? 2 : 1;
+  const int64_t span_bytes = (int64_t)sb * c.qspan;
+  int sc = (reinterpret_cast<uintptr_t>(scales) & 15u) == 0 && ((k / 32) * sb) % 16 == 0 && span_bytes % 16 == 0 &&
+           tg * XS_ROWS * (span_bytes / 16) <= (int64_t)XS_SC_UNITS * 64 * c.nw ? 1 : 0;
+  size_t lds = (size_t)xs_layout(XS_MAX_M, c.nw, (int)tg, 0, sc ? (int)span_bytes : 0).bytes;
+  if (lds > (size_t)kXsMaxLds && sc) {
+    sc = 0;
+    lds = (size_t)xs_layout(XS_MAX_M, c.nw, (int)tg, 0, 0).bytes;
+  }
+  if (lds > (size_t)kXsMaxLds) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(num_experts * G)), block((unsigned)(64 * c.nw));
+  const uint16_t* xx = reinterpret_cast<const uint16_t*>(x);
+  uint16_t* yy = reinterpret_cast<uint16_t*>(y);
+  if (fmt == FMT_NVFP4)
+    return launch_gxs_fmt<FMT_NVFP4>((int)tg, sc, grid, block, lds, stream, xx, num_tokens, row_index, expert_offsets,
+                                     total_rows, n, k, codes, scales, tensor_scales, yy, c.qspan, c.ntiles, (int)G);
+  return launch_gxs_fmt<FMT_MXFP4>((int)tg, sc, grid, block, lds, stream, xx, num_tokens, row_index, expert_offsets,
+                                   total_rows, n, k, codes, scales, tensor_scales, yy, c.qspan, c.ntiles, (int)G);
 }
 
 }  // namespace fp4w

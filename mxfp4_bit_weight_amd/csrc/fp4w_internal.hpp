@@ -99,6 +99,13 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
                          const void* lora_b, int r, void* y, void* workspace, const LinearPlan& plan,
                          hipStream_t stream);
 
+// Grouped linear on the x-in-registers kernel (decode_xs.hip): K in one span.
+bool grouped_xs_supports(int64_t num_tokens, int64_t n, int64_t k);
+hipError_t launch_grouped_xs(int fmt, const void* x, int64_t num_tokens, const int32_t* row_index,
+                             const int32_t* expert_offsets, int64_t num_experts, int64_t total_rows, int64_t n,
+                             int64_t k, const uint8_t* codes, const uint8_t* scales, const float* tensor_scales,
+                             void* y, hipStream_t stream);
+
 hipError_t launch_grouped_linear(int fmt, const void* x, int64_t num_tokens, const int32_t* row_index,
                                  const int32_t* expert_offsets, int64_t num_experts, int64_t total_rows,
                                  int64_t n, int64_t k, const uint8_t* codes, const uint8_t* scales,

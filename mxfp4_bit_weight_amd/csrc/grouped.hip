@@ -6,8 +6,10 @@
 // section 02).  Routed rows are sorted by expert; expert e owns rows
 // [offsets[e], offsets[e+1]) and row q reads token x[row_index[q]].
 //
-// One workgroup per (expert, 16-row weight tile) runs the decode tile of
-// skinny.hpp over the whole K for each chunk of up to 16 of its routed rows.
+// K up to 4096 (every shape of the pages' MoE model) runs on the x-in-registers
+// kernel of decode_xs.hip, a workgroup per (expert, run of weight tiles).
+// Otherwise one workgroup per (expert, 16-row weight tile) runs the decode tile
+// of skinny.hpp over the whole K for each chunk of up to 16 of its routed rows.
 // The routing never leaves the device: a workgroup whose expert received no
 // rows exits at once, and the number of m-groups is chosen per chunk (uniform
 // branch).  Rows with a token index outside [0, num_tokens) are written as NaN.
@@ -90,6 +92,9 @@ hipError_t launch_grouped_linear(int fmt, const void* x, int64_t num_tokens, con
                                  int64_t n, int64_t k, const uint8_t* codes, const uint8_t* scales,
                                  const float* tensor_scales, void* y, hipStream_t stream) {
   if (num_experts == 0 || total_rows == 0 || n == 0) return hipSuccess;
+  if (grouped_xs_supports(num_tokens, n, k))
+    return launch_grouped_xs(fmt, x, num_tokens, row_index, expert_offsets, num_experts, total_rows, n, k, codes,
+                             scales, tensor_scales, y, stream);
   const int64_t tiles = (n + SK_TILE_N - 1) / SK_TILE_N;
   const dim3 grid((unsigned)(num_experts * tiles)), block(SK_THREADS);
   const uint16_t* xx = reinterpret_cast<const uint16_t*>(x);

@@ -1,7 +1,9 @@
 """GPU parity of the grouped (MoE) W4A16 linear against the binary64 oracle:
 128 experts with gate/up (768, 2048) and down (2048, 768) weights, 64 tokens
 routed top-8; plus empty experts, experts with more than 16 rows, a single
-expert, and out-of-range token indices (NaN rows)."""
+expert, out-of-range token indices (NaN rows), offsets outside [0, total rows]
+(clamped; rows no expert covers keep their contents) and a K above 4096 (the
+per-tile kernel instead of the x-in-registers one)."""
 import numpy as np
 import pytest
 import torch
@@ -68,13 +70,51 @@ def test_uneven_routing(fp4w, fmt):
     _case(fp4w, fmt, x, row_index, offsets, codes, scales, ts, "uneven routing")
 
 
-def test_bad_token_index_gives_nan_rows(fp4w):
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_long_k_uses_the_per_tile_kernel(fp4w, fmt):
+    # K = 4160: 130 groups of 32, more than one span of the x-in-registers kernel holds
+    offsets = np.array([0, 5, 5, 22], np.int32)
+    rng = np.random.default_rng(12)
+    row_index = rng.integers(0, 9, offsets[-1]).astype(np.int32)
+    x = W.normal_bf16(4, W.TID_X, (9, 4160), 1.0)
+    codes, scales, ts = _experts(fmt, 4, 3, 40, 4160)
+    _case(fp4w, fmt, x, row_index, offsets, codes, scales, ts, "K 4160")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_offsets_are_clamped(fp4w, fmt):
+    """Offsets [-3, 2, 9] over 5 rows act as [0, 2, 5]; offsets [0, 2, 3] leave
+    rows 3 and 4 as they were."""
+    rng = np.random.default_rng(13)
+    row_index = rng.integers(0, 6, 5).astype(np.int32)
+    x = W.normal_bf16(5, W.TID_X, (6, 256), 1.0)
+    codes, scales, ts = _experts(fmt, 5, 2, 24, 256)
+    args = (u8_dev(codes), u8_dev(scales), f32_dev(ts) if fmt == 0 else None)
+    y = fp4w.grouped_linear(bf16_dev(x), i32_dev(row_index), i32_dev(np.array([-3, 2, 9], np.int32)), fmt, *args)
+    torch.cuda.synchronize()
+    y64 = O.grouped_linear(fmt, x, row_index, np.array([0, 2, 5], np.int32), codes, scales, ts)
+    xn = np.sqrt((f64_of_bf16(x) ** 2).sum(axis=1))[row_index][:, None]
+    wn = np.zeros((5, 24))
+    for e, (a, b) in enumerate([(0, 2), (2, 5)]):
+        d = O.dequantize(fmt, codes[e], scales[e], ts[e], "f64")
+        wn[a:b] = np.sqrt((d * d).sum(axis=1))[None, :]
+    check_bound(f64_of_bf16(bits_host(y)), y64, xn, wn, "clamped offsets")
+    out = torch.full((5, 24), 7.0, dtype=torch.bfloat16, device=DEV)
+    fp4w.grouped_linear(bf16_dev(x), i32_dev(row_index), i32_dev(np.array([0, 2, 3], np.int32)), fmt, *args, out=out)
+    torch.cuda.synchronize()
+    assert bool((out[3:] == 7.0).all().item())
+    y64 = O.grouped_linear(fmt, x, row_index[:3], np.array([0, 2, 3], np.int32), codes, scales, ts)
+    check_bound(f64_of_bf16(bits_host(out[:3])), y64, xn[:3], wn[:3], "rows 0-2 of the short offsets")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_bad_token_index_gives_nan_rows(fp4w, fmt):
     offsets = np.array([0, 3, 5], np.int32)
     row_index = np.array([0, 99, 1, -1, 2], np.int32)
     x = W.normal_bf16(3, W.TID_X, (4, 64), 1.0)
-    codes, scales, ts = _experts(0, 3, 2, 16, 64)
-    y = fp4w.grouped_linear(bf16_dev(x), i32_dev(row_index), i32_dev(offsets), 0, u8_dev(codes), u8_dev(scales),
-                            f32_dev(ts))
+    codes, scales, ts = _experts(fmt, 3, 2, 16, 64)
+    y = fp4w.grouped_linear(bf16_dev(x), i32_dev(row_index), i32_dev(offsets), fmt, u8_dev(codes), u8_dev(scales),
+                            f32_dev(ts) if fmt == 0 else None)
     torch.cuda.synchronize()
     yh = y.float().cpu().numpy()
     assert np.isnan(yh[1]).all() and np.isnan(yh[3]).all()

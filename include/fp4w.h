@@ -125,7 +125,8 @@ size_t fp4w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
  *   y_bf16     (m, n) bf16, rounded once from the fp32 result
  *   workspace  >= fp4w_linear_workspace_bytes(m, n, k, r) bytes, see above
  * Launches (all on `stream`):
- *  - m == 1: one launch of the decode kernel on gfx950's block-scaled MFMA,
+ *  - m <= 2, and m <= 4 when n * k <= 2^24: one launch of the decode kernel
+ *    on gfx950's block-scaled MFMA,
  *    which feeds the codes to the matrix core as stored and x as two E4M3 terms
  *    per element under an E8M0 scale per 32 elements.  That split is exact for
  *    every element within 2^13 of its block's largest magnitude; smaller ones
@@ -133,7 +134,7 @@ size_t fp4w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
  *    workgroups form t = x A^T on the bf16 matrix core, one K chunk each, and
  *    hand it to the workgroups that write the outputs (chunks added in a fixed
  *    order: the result does not depend on scheduling).
- *  - 2 <= m <= 16: one decode kernel holding x in registers (it also forms
+ *  - other m <= 16: one decode kernel holding x in registers (it also forms
  *    t = x A^T when r <= 16; larger ranks get a LoRA down-projection launch
  *    first): the weights are decoded exactly to fp16 (NVFP4, with x scaled to
  *    fp16 by a power of two per row and K range: exact for every element within

@@ -518,10 +518,20 @@ static int decode_splits_for(int64_t m, int64_t n, int64_t k) {
   return (int)s;
 }
 
+// Decode-shaped calls (m <= 16) run on the block-scaled kernel when its cost per
+// row of x is small against a launch (m <= 2, or m <= 4 on a matrix of at most
+// 2^24 weights), else on the x-in-registers kernel.  Measured on MI355X for the
+// Qwen-2.5-7B shapes in both formats, with and without LoRA: at m = 2 the
+// block-scaled kernel is faster on every shape, at m = 4 only on 3584 x 3584,
+// at m = 8 on none.
+static bool decode_prefers_f8f4(int64_t m, int64_t n, int64_t k) {
+  return m <= 2 || (m <= 4 && n * k <= ((int64_t)1 << 24));
+}
+
 LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
   LinearPlan p{};
   if (m > 16) p.path = 1;
-  else if (m >= 2 && decode_xs_supports(m, n, k, r)) p.path = 3;
+  else if (m >= 2 && decode_xs_supports(m, n, k, r) && !decode_prefers_f8f4(m, n, k)) p.path = 3;
   else p.path = decode_f8f4_supports(FMT_NVFP4, m) ? 0 : 2;
   if (p.path == 3) {
     p.xs = plan_decode_xs(m, n, k, r);

@@ -1,5 +1,6 @@
-"""m = 1 linear with a LoRA: inside the one decode launch, the first workgroups
-form t = x A^T (one K chunk each) and hand it to the workgroups that write the
+"""Decode-shaped linear on the block-scaled kernel (m = 1; m = 2; m <= 4 on small
+matrices) with a LoRA: inside the one decode launch, the first workgroups form
+t = x A^T (one K chunk each) and hand it to the workgroups that write the
 outputs through words of the workspace.
 
 Checked here, against the binary64 oracle within |err| <= 2e-3 ||x|| ||w_n^eff||:
@@ -83,6 +84,39 @@ def test_handover_matches_oracle_and_own_t(fp4w, restore_wait, fmt, n, k, r, sam
         torch.cuda.synchronize()
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), f"own t differs ({what}, rep {rep})"
         assert _counters_zero(fp4w, ws), "hand-over words left non-zero (wait bound 0)"
+
+
+# m = 2 to 4 on the block-scaled kernel (m = 2 always; m = 3, 4 on matrices of
+# at most 2^24 weights): several rows of x per chunk word
+MROWS = [(2, 200, 544, 16), (2, 3584, 18944, 16), (3, 1000, 1056, 64), (4, 33, 640, 17), (4, 3584, 3584, 16)]
+
+
+@pytest.mark.parametrize("m,n,k,r", MROWS)
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_handover_several_rows(fp4w, restore_wait, fmt, m, n, k, r):
+    what = f"fmt={fmt} m={m} n={n} k={k} r={r}"
+    say(f"[lora handover] {what}")
+    w, x, a, b = W.linear_inputs(400 + m + r, n, k, m, rank=r, wkind="outlier")
+    codes, scales, st = O.quantize(fmt, w)
+    q = qweight_dev(fp4w, fmt, codes, scales, st)
+    xd, ad, bd = bf16_dev(x), bf16_dev(a), bf16_dev(b)
+    ws = torch.zeros(fp4w.linear_workspace_bytes(m, n, k, r), dtype=torch.uint8, device=DEV)
+    y1 = fp4w.linear(xd, q, ad, bd, workspace=ws)
+    torch.cuda.synchronize()
+    assert _counters_zero(fp4w, ws)
+    rng = np.random.default_rng(m * 1000 + n)
+    rows = rng.integers(0, m, 384)
+    cols = rng.integers(0, n, 384)
+    ys = f64_of_bf16(bits_host(y1[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)]))
+    y64 = O.linear_sampled(fmt, x, codes, scales, st, rows, cols, a, b)
+    xn = np.sqrt((f64_of_bf16(x[rows]) ** 2).sum(axis=1))
+    wn = weff_norms(fmt, codes, scales, st, a, b, rows=cols)
+    check_bound(ys, y64, xn, wn, what)
+    fp4w.debug_lora_wait(0)
+    y2 = fp4w.linear(xd, q, ad, bd, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), f"own t differs ({what})"
+    assert _counters_zero(fp4w, ws)
 
 
 def test_handover_then_other_shapes_on_one_workspace(fp4w):

@@ -39,23 +39,14 @@
 // workgroup of a tile to arrive adds the slices' partials in slice order, so
 // the result never depends on scheduling.
 //
-// LoRA (t = x A^T, then t B^T added to every output row): t is needed only
-// when a tile's outputs are written, after its codes have streamed, so the
-// down-projection runs inside the same launch.  The grid's first workgroups
-// stream no codes: workgroup p forms the partial of K chunk p on the bf16
-// matrix core (each wave a run of 32-wide steps, waves added in order) and
-// stores it, complemented so that a zero word reads as "not yet written".  In
-// every other workgroup, the first wave done with its share of the codes waits
-// for every chunk word with a bounded poll (its sibling waves still stream) and
-// adds the chunks in chunk order; were the wait ever to run out, the
-// workgroup forms the chunks itself by the same steps in the same order, so
-// the value is the same either way.  The chunk workgroups wait on nothing, so the wait ends.  The
-// hand-over words return to zero before the kernel ends: the readers arrive on
-// 32 counters a cache line apart, the completed groups and the chunk
-// workgroups (after their stores have landed) on one more, and the arrival
-// that completes it clears the words.
+// LoRA (t = x A^T, then t B^T added to every output row): formed inside the
+// same launch by the grid's first workgroups and handed over through the
+// workspace (lora_handover.hpp).  In the workgroups that write outputs, the
+// first wave done with its share of the codes polls for t while its sibling
+// waves still stream.
 #include "fp4w_device.hpp"
 #include "fp4w_internal.hpp"
+#include "lora_handover.hpp"
 #include "sync.hpp"
 #include "xenc.hpp"
 
@@ -68,7 +59,6 @@ typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 constexpr int DQ_STEP = 128;       // K per step: one block-scaled MFMA
 constexpr int DQ_ROWS = 16;        // weight rows per tile
 constexpr int DQ_MAX_R = 64;       // LoRA rank staged in LDS
-constexpr int DQ_LSPW = 4;         // 32-wide K steps per wave of a LoRA chunk
 
 // LDS layout of one workgroup (byte offsets):
 //   zeros   128 (spw + 1)          A lanes that carry no x read here (spw: steps per wave)
@@ -107,51 +97,6 @@ __host__ __device__ inline DqLayout dq_layout(int fmt, int m, int kslice, int nw
   return L;
 }
 
-// ---------------------------------------------------------------------------------
-// LoRA hand-over between the workgroups of one launch (words of the counter area).
-// ---------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t lsync_load(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void lsync_store(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t lsync_add(uint32_t* p) {
-  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// One wave: an arrival on the top counter, which expects one arrival per reader
-// group and per chunk; the arrival that completes it clears the `words` chunk
-// words and the counter.
-__device__ __forceinline__ void lsync_top_arrive(uint32_t* ls, uint32_t expected, int words, int lane) {
-  uint32_t old = 0;
-  if (lane == 0) old = lsync_add(&ls[kLsyncTop]);
-  old = (uint32_t)__shfl((int)old, 0, 64);
-  if (old == expected - 1u) {
-    for (int e = lane; e < words; e += 64) lsync_store(&ls[e], 0u);
-    if (lane == 0) lsync_store(&ls[kLsyncTop], 0u);
-  }
-}
-
-__device__ __forceinline__ uint32_t lsync_top_expected(int nread, int lparts) {
-  return (uint32_t)((nread < kLsyncSubs ? nread : kLsyncSubs) + lparts);
-}
-
-// One wave of reader workgroup `rd` of `nread`, after its loads of the chunk
-// words have returned.
-__device__ __forceinline__ void lsync_reader_arrive(uint32_t* ls, int rd, int nread, int lparts, int words,
-                                                    int lane) {
-  const int c = rd % kLsyncSubs;
-  const uint32_t quota = (uint32_t)(nread / kLsyncSubs + (c < nread % kLsyncSubs ? 1 : 0));
-  uint32_t old = 0;
-  if (lane == 0) {
-    old = lsync_add(&ls[kLsyncSub + 32 * c]);
-    if (old == quota - 1u) lsync_store(&ls[kLsyncSub + 32 * c], 0u);
-  }
-  old = (uint32_t)__shfl((int)old, 0, 64);
-  if (old == quota - 1u) lsync_top_arrive(ls, lsync_top_expected(nread, lparts), words, lane);
-}
-
 template <int FMT, int NQ, int NW, int DEPTH, bool LORA>
 __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
     const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ codes,
@@ -178,57 +123,10 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
   const int bid = (int)blockIdx.x - lparts;                       // < 0: a LoRA chunk workgroup
   const int s = bid % S, tile = bid / S;
   const int nread = ntiles * S;                                   // LoRA: every tile workgroup reads t
-  // ---- LoRA chunk p: wave w takes the lsw 32-wide K steps from (p NW + w) lsw
-  //      on v_mfma_f32_16x16x32_bf16, x rows as A (row = lane % 16), A's rows as B
-  //      (column j = 16 b + lane % 16); lane (j, g) gets rows m = 4 g + i.  Loads
-  //      go out LSPW steps at a time. --------------------------------------------------
-  float* lr = reinterpret_cast<float*>(lds + L.lr_off);            // [wave][m][j]
-  auto lora_chunk = [&](int p) __attribute__((always_inline)) {
-    const int li = lane & 15, lg = lane >> 4;
-    const int64_t st0 = ((int64_t)p * NW + wave) * lsw;
-    for (int b = 0; b < (rr + 15) / 16; b++) {
-      const int j = 16 * b + li;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      for (int i0 = 0; i0 < lsw; i0 += DQ_LSPW) {
-        u32x4_t xa[DQ_LSPW], av[DQ_LSPW];
-#pragma unroll
-        for (int i = 0; i < DQ_LSPW; i++) {
-          const int64_t kk = (st0 + i0 + i) * 32 + 8 * lg;
-          const bool okx = li < M && kk < K, oka = j < rr && kk < K;
-          xa[i] = load16(x + (okx ? (int64_t)li * K + kk : 0));
-          av[i] = load16(lora_a + (oka ? (int64_t)j * K + kk : 0));
-          if (!okx) xa[i] = (u32x4_t){0u, 0u, 0u, 0u};
-          if (!oka) av[i] = (u32x4_t){0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int i = 0; i < DQ_LSPW; i++)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[i]), as_bf16x8(av[i]), acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int m = 4 * lg + i;
-        if (m < M && j < rr) lr[(wave * M + m) * rr + j] = acc[i];
-      }
-    }
-  };
-  // wave 0, after a barrier that follows lora_chunk(p): the chunk's value at
-  // e = m r + j, its waves added in order
-  auto chunk_value = [&](int e) __attribute__((always_inline)) {
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; w++) v += lr[w * mr + e];
-    return v;
-  };
+  float* lr = reinterpret_cast<float*>(lds + L.lr_off);            // [wave][m][j]: a LoRA chunk
   if (LORA && bid < 0) {
-    // ---- 0. a chunk workgroup: its partial, complemented, then its arrival ------
-    const int p = (int)blockIdx.x;
-    lora_chunk(p);
-    __syncthreads();
-    if (wave == 0) {
-      for (int e = lane; e < mr; e += 64) lsync_store(&lsync[p * mr + e], ~__float_as_uint(chunk_value(e)));
-      wait_stores_complete();
-      lsync_top_arrive(lsync, lsync_top_expected(nread, lparts), words, lane);
-    }
+    // ---- 0. a chunk workgroup: its partial of t, complemented, then its arrival --
+    lora_chunk_publish(lr, x, M, K, lora_a, rr, (int)blockIdx.x, NW, lsw, lsync, nread, lparts);
     return;
   }
 
@@ -486,28 +384,7 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
     first = __shfl(first, 0, 64);
     if (first) {
       float* lt = reinterpret_cast<float*>(lds + L.lt_off);
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      int ok;
-      for (;;) {
-        int mine = 1;
-        for (int q = lane; q < mr; q += 64) {
-          float t = 0.f;
-          for (int p0 = 0; p0 < lparts; p0 += 8) {
-            uint32_t w[8];
-#pragma unroll
-            for (int i = 0; i < 8; i++) w[i] = p0 + i < lparts ? lsync_load(&lsync[(p0 + i) * mr + q]) : ~0u;
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-              if (w[i] == 0u) mine = 0;
-              if (p0 + i < lparts) t += __uint_as_float(~w[i]);
-            }
-          }
-          lt[q] = t;
-        }
-        ok = __all(mine);
-        if (ok || __builtin_amdgcn_s_memrealtime() - t0 >= wait_ticks) break;
-        __builtin_amdgcn_s_sleep(8);
-      }
+      const int ok = lora_poll(lsync, lparts, mr, lt, wait_ticks, lane);
       if (lane == 0) have_t = ok;
       lsync_reader_arrive(lsync, bid, nread, lparts, words, lane);
     }
@@ -550,16 +427,7 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
   if (LORA && __builtin_expect(!have_t, 0)) {
     // ---- 6. the wait for t ran out: the chunks formed here, by the same steps in
     //      the same order -----------------------------------------------------------
-    float* lt = reinterpret_cast<float*>(lds + L.lt_off);
-    if (wave == 0)
-      for (int q = lane; q < mr; q += 64) lt[q] = 0.f;
-    for (int p = 0; p < lparts; p++) {
-      lora_chunk(p);
-      __syncthreads();
-      if (wave == 0)
-        for (int q = lane; q < mr; q += 64) lt[q] += chunk_value(q);
-      __syncthreads();
-    }
+    lora_form_all(lr, reinterpret_cast<float*>(lds + L.lt_off), x, M, K, lora_a, rr, NW, lsw, lparts);
   }
   if (e < nout) {
     const int m = e / DQ_ROWS, nn = e - m * DQ_ROWS;
@@ -626,14 +494,6 @@ static std::atomic<int64_t> g_lora_wait{100000};          // 1 ms
 int64_t lora_wait_ticks() { return g_lora_wait.load(std::memory_order_relaxed); }
 int64_t set_lora_wait_ticks(int64_t ticks) { return g_lora_wait.exchange(ticks, std::memory_order_relaxed); }
 
-// Steps per wave of a LoRA chunk: DQ_LSPW (one round of loads per column block),
-// or a multiple of it when the chunk words would not fit the hand-over area.
-static int dq_lora_steps(int nw, int64_t k, int mr) {
-  const int64_t nsteps = (k + 31) / 32;
-  int64_t lsw = DQ_LSPW;
-  while ((nsteps + lsw * nw - 1) / (lsw * nw) * mr > kLsyncWords) lsw += DQ_LSPW;
-  return (int)lsw;
-}
 
 template <int FMT, int NQ>
 static void launch_nq(const DecodeConfig& c, dim3 grid, size_t lds, hipStream_t stream, const uint16_t* x, int m,
@@ -676,8 +536,8 @@ hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c0, const void* x, in
   const size_t lds = decode_f8f4_lds_bytes(fmt, m, kslice, c.nw, rr);
   if (lds > 64 * 1024 || rr > DQ_MAX_R || m * rr > 1024) return hipErrorInvalidValue;
   // chunk workgroups of the LoRA down-projection go first in the grid
-  const int lsw = rr > 0 ? dq_lora_steps(c.nw, k, (int)m * rr) : DQ_LSPW;
-  const int lparts = rr > 0 ? (int)(((k + 31) / 32 + (int64_t)lsw * c.nw - 1) / ((int64_t)lsw * c.nw)) : 0;
+  const int lsw = rr > 0 ? lora_chunk_steps(c.nw, k, (int)m * rr) : kLoraStepsPerLoad;
+  const int lparts = rr > 0 ? lora_chunk_count(c.nw, k, lsw) : 0;
   const dim3 grid((unsigned)(lparts + (int64_t)ntiles * c.splits));
   const int scales16 = ((reinterpret_cast<uintptr_t>(scales) & 15u) == 0 && (k / blk) % 16 == 0 &&
                         (kslice / blk) % 16 == 0) ? 1 : 0;

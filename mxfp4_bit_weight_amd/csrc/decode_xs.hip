@@ -39,6 +39,7 @@
 // partials in span order, so results never depend on scheduling.
 #include "fp4w_device.hpp"
 #include "fp4w_internal.hpp"
+#include "lora_handover.hpp"
 #include "sync.hpp"
 
 namespace fp4w {
@@ -51,13 +52,12 @@ constexpr int XS_MAX_M = 16;         // rows of x (MFMA rows)
 constexpr int XS_MAX_R = 64;         // LoRA rank
 constexpr int XS_MAX_WAVES = 16;
 constexpr int XS_CPW = 2;            // 32-wide K groups per lane
-constexpr int XS_FUSED_R = 16;       // LoRA ranks up to this are formed in the kernel
 constexpr int XS_SC_UNITS = 4;       // staged scale units per thread at most
 constexpr int XS_RING = 2;           // tiles of code loads in flight per wave
 
 // LDS of one workgroup (byte offsets):
 //   red   [nw][tg][m][16] fp32   wave partials of each tile
-//   tred  [nw][m][r] fp32        wave partials of t = x A^T over the span
+//   tred  [nw][m][r] fp32        LoRA: wave partials of one K chunk of t = x A^T
 //   lb    [tg * 16][r] bf16      the LoRA B rows of the tiles
 //   lt    [m][r] fp32            t over the span
 //   ssc   [tg * 16][span_bytes]   block-scale bytes of the tiles' rows over the span
@@ -106,14 +106,18 @@ __device__ __forceinline__ bf16x8_t codes8_to_bf16_pow2(uint32_t dw, float pow2)
 // bytes (any alignment).  xrow: nullptr = row m of x is x[m]; otherwise row m is
 // x[xrow[m]] of xrows rows, and a row index outside [0, xrows) makes the output
 // row NaN (the routed rows of an expert).
-template <int FMT, int TG, int SC>
+// LORA: t = x A^T comes from the launch's chunk workgroups (lora_handover.hpp):
+// wave 0 waits for it in the epilogue, reader `rd` of `nread`, and span 0 adds
+// t B^T to its outputs.
+template <int FMT, int TG, int SC, bool LORA>
 __device__ __forceinline__ void xs_body(
-    uint8_t* __restrict__ lds, int* flag, const uint16_t* __restrict__ x, const int32_t* __restrict__ xrow,
-    int64_t xrows, int M, int64_t K, const uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ lds, int* flag, int* have_t, const uint16_t* __restrict__ x,
+    const int32_t* __restrict__ xrow, int64_t xrows, int M, int64_t K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t N,
-    const uint16_t* __restrict__ lora_a, const float* __restrict__ t_lora, const uint16_t* __restrict__ lora_b,
-    int r, uint16_t* __restrict__ y, float* __restrict__ part, uint32_t* __restrict__ cnt, int S, int qspan,
-    int ntiles, int G, int tg, int lb16, int s, int gi) {
+    const uint16_t* __restrict__ lora_a, const uint16_t* __restrict__ lora_b, int r, int lparts, int lsw,
+    uint32_t* __restrict__ lsync, uint64_t wait_ticks, uint16_t* __restrict__ y, float* __restrict__ part,
+    uint32_t* __restrict__ cnt, int S, int qspan, int ntiles, int G, int tg, int lb16, int s, int gi, int rd,
+    int nread) {
   constexpr int CPW = XS_CPW;
   const int nt = (int)blockDim.x;
   const int nw = nt >> 6;
@@ -127,7 +131,7 @@ __device__ __forceinline__ void xs_body(
   const int qs1 = min((s + 1) * qspan, nq);
   const int qw0 = s * qspan + wave * 4 * CPW;
   const int n = lane & 15, g = lane >> 4;
-  const int rr = (lora_a || t_lora) ? r : 0;       // LoRA rank (0: none)
+  const int rr = LORA ? r : 0;                     // LoRA rank (0: none)
   constexpr uint32_t SB = FMT == FMT_NVFP4 ? 2u : 1u;              // scale bytes per 32-wide group
   const int span_bytes = SC ? (int)SB * qspan : 0;
   const XsLayout L = xs_layout(M, nw, tg, rr, span_bytes);
@@ -156,17 +160,6 @@ __device__ __forceinline__ void xs_body(
     const uint32_t base = (uint32_t)((xr_ok ? xr : 0) * K + 32 * (int64_t)qv[u]) * 2u;
 #pragma unroll
     for (int sub = 0; sub < 4; sub++) xa[u][sub] = buffer_load16(xrs, ok ? base + 16u * sub : kBufferOob);
-  }
-  // fused LoRA (r <= 16): A rows j = n as B operands over the same K groups
-  const int ra = lora_a ? r : 0;
-  const __amdgpu_buffer_rsrc_t ars = make_rsrc(lora_a, (uint32_t)((int64_t)ra * K * 2));
-  u32x4_t av[CPW][4];
-#pragma unroll
-  for (int u = 0; u < CPW; u++) {
-    const bool ok = (n < ra) & qok[u];
-    const uint32_t base = (uint32_t)(n * K + 32 * (int64_t)qv[u]) * 2u;
-#pragma unroll
-    for (int sub = 0; sub < 4; sub++) av[u][sub] = buffer_load16(ars, ok ? base + 16u * sub : kBufferOob);
   }
   // first 16-byte unit of the LoRA B rows of the tiles (B 16-byte aligned, r % 8 == 0)
   // (unit e: tile e / (2 r), 16-byte unit e % (2 r) of its 16 rows; rows >= N not read)
@@ -217,24 +210,6 @@ __device__ __forceinline__ void xs_body(
   const uint32_t span_b0 = SB * (uint32_t)(s * qspan);
   const uint32_t span_blen = SB * (uint32_t)(qs1 - s * qspan);
   u32x4_t scv[XS_SC_UNITS];
-
-  // ---- 3. fused LoRA: t = x A^T over the wave's K groups (bf16 products, fp32 sums) ----
-  // D layout: lane (j = n, g) holds rows m = 4 g + i of column j.
-  // (run without LoRA too, on zeros: the A loads then stay where they are issued)
-  float* tred = reinterpret_cast<float*>(lds + L.tred_off);
-  {
-    f32x4_t tacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < CPW; u++)
-#pragma unroll
-      for (int sub = 0; sub < 4; sub++)
-        tacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_as_bf16x8(xa[u][sub]), bits_as_bf16x8(av[u][sub]), tacc, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int m = 4 * g + i;
-      if (m < M && n < ra) tred[(wave * M + m) * ra + n] = tacc[i];
-    }
-  }
 
   // ---- 4. x to the operand format -------------------------------------------------
   // Largest |x| of each row over this wave's K groups, as the 15 magnitude bits
@@ -387,19 +362,16 @@ __device__ __forceinline__ void xs_body(
         lbe[e] = el < N * rr ? lora_b[el] : (uint16_t)0;
       }
     }
-    // t given (r > 16): the whole of it, added by the first span only
-    if (ra == 0)
-      for (int e = tid; e < M * rr; e += nt) lt[e] = s == 0 ? t_lora[e] : 0.f;
+    // t: the chunk words of the launch (bounded wait), read by wave 0 of the
+    // span-0 workgroups while the other waves stage B
+    if (wave == 0) {
+      const int ok = s == 0 ? lora_poll(lsync, lparts, M * rr, lt, wait_ticks, lane) : 1;
+      if (lane == 0) *have_t = ok;
+    }
   }
   __syncthreads();
-  if (ra > 0) {                                  // the span's t: wave partials in wave order
-    for (int e = tid; e < M * ra; e += nt) {
-      float v = 0.f;
-      for (int w = 0; w < nw; w++) v += tred[w * M * ra + e];
-      lt[e] = v;
-    }
-    __syncthreads();
-  }
+  if (LORA && __builtin_expect(!*have_t, 0))      // the wait ran out (span 0): the chunks formed here
+    lora_form_all(reinterpret_cast<float*>(lds + L.tred_off), lt, x, M, K, lora_a, rr, nw, lsw, lparts);
 
   // ---- 7. tile sums in wave order (+ the span's LoRA term); spans in span order --------
   const float st = (FMT == FMT_NVFP4) ? *tensor_scale : 1.0f;
@@ -415,7 +387,7 @@ __device__ __forceinline__ void xs_body(
     float o = 0.f;
     for (int w = 0; w < nw; w++) o += red[(w * tg + ti) * per_tile + rem];
     float v = st * o;
-    if (rr > 0) {
+    if (rr > 0 && s == 0) {                      // t B^T once per output: span 0
       const int m = rem / XS_ROWS, nn = rem - m * XS_ROWS;
       const uint16_t* b = lbs + (ti * XS_ROWS + nn) * rr;
       float l = 0.f;
@@ -431,6 +403,8 @@ __device__ __forceinline__ void xs_body(
       if (row < N) y[(int64_t)m * N + row] = (uint16_t)f32_to_bf16_rne(v);
     }
   }
+  // the chunk words have been read (span 0): arrive
+  if (LORA && s == 0 && wave == 0) lsync_reader_arrive(lsync, rd, nread, lparts, lparts * M * rr, lane);
   if (S > 1) {
     if (!arrive_last(&cnt[gi], (uint32_t)S, flag)) return;
     for (int e = tid; e < nout; e += nt) {
@@ -445,18 +419,28 @@ __device__ __forceinline__ void xs_body(
   }
 }
 
-template <int FMT, int TG, int SC>
+// Dense: LORA workgroups below lparts form the chunks of t (and stream no codes);
+// workgroup lparts + bid takes span bid % S of tile run bid / S.
+template <int FMT, int TG, int SC, bool LORA>
 __global__ __launch_bounds__(64 * XS_MAX_WAVES) void decode_xs_kernel(
     const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t N,
-    const uint16_t* __restrict__ lora_a, const float* __restrict__ t_lora, const uint16_t* __restrict__ lora_b,
-    int r, uint16_t* __restrict__ y, float* __restrict__ part, uint32_t* __restrict__ cnt, int S, int qspan,
-    int ntiles, int G, int tg, int lb16) {
+    const uint16_t* __restrict__ lora_a, const uint16_t* __restrict__ lora_b, int r, int lparts, int lsw,
+    uint32_t* __restrict__ lsync, uint64_t wait_ticks, uint16_t* __restrict__ y, float* __restrict__ part,
+    uint32_t* __restrict__ cnt, int S, int qspan, int ntiles, int G, int tg, int lb16) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int flag;
-  const int s = (int)(blockIdx.x % (unsigned)S), gi = (int)(blockIdx.x / (unsigned)S);
-  xs_body<FMT, TG, SC>(lds, &flag, x, nullptr, M, M, K, codes, scales, tensor_scale, N, lora_a, t_lora, lora_b, r, y,
-                       part, cnt, S, qspan, ntiles, G, tg, lb16, s, gi);
+  __shared__ int flag, have_t;
+  if (LORA && (int)blockIdx.x < lparts) {
+    const XsLayout L = xs_layout(M, (int)blockDim.x >> 6, tg, r, 0);
+    lora_chunk_publish(reinterpret_cast<float*>(lds + L.tred_off), x, M, K, lora_a, r, (int)blockIdx.x,
+                       (int)blockDim.x >> 6, lsw, lsync, G, lparts);
+    return;
+  }
+  const int bid = (int)blockIdx.x - (LORA ? lparts : 0);
+  const int s = bid % S, gi = bid / S;
+  xs_body<FMT, TG, SC, LORA>(lds, &flag, &have_t, x, nullptr, M, M, K, codes, scales, tensor_scale, N, lora_a,
+                             lora_b, r, lparts, lsw, lsync, wait_ticks, y, part, cnt, S, qspan, ntiles, G, tg, lb16,
+                             s, gi, gi, G);
 }
 
 // ---------------------------------------------------------------------------------
@@ -472,7 +456,7 @@ __global__ __launch_bounds__(64 * XS_MAX_WAVES) void grouped_xs_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const float* __restrict__ tscales,
     uint16_t* __restrict__ y, int qspan, int ntiles, int G, int tg) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int flag;
+  __shared__ int flag, have_t;
   const int64_t e = blockIdx.x / (unsigned)G;
   const int gi = (int)(blockIdx.x % (unsigned)G);
   int64_t q0 = offsets[e], q1 = offsets[e + 1];
@@ -484,8 +468,9 @@ __global__ __launch_bounds__(64 * XS_MAX_WAVES) void grouped_xs_kernel(
   const float* te = FMT == FMT_NVFP4 ? tscales + e : nullptr;
   for (; q0 < q1; q0 += XS_MAX_M) {
     const int mc = (int)(q1 - q0 < XS_MAX_M ? q1 - q0 : XS_MAX_M);
-    xs_body<FMT, TG, SC>(lds, &flag, x, row_index + q0, num_tokens, mc, K, ce, se, te, N, nullptr, nullptr, nullptr,
-                         0, y + q0 * N, nullptr, nullptr, 1, qspan, ntiles, G, tg, 0, 0, gi);
+    xs_body<FMT, TG, SC, false>(lds, &flag, &have_t, x, row_index + q0, num_tokens, mc, K, ce, se, te, N, nullptr,
+                                nullptr, 0, 0, 0, nullptr, 0, y + q0 * N, nullptr, nullptr, 1, qspan, ntiles, G, tg, 0,
+                                0, gi, 0, 0);
     __syncthreads();                             // LDS is reused by the next chunk
   }
 }
@@ -497,8 +482,6 @@ bool decode_xs_supports(int64_t m, int64_t n, int64_t k, int r) {
   return m >= 1 && m <= XS_MAX_M && k % 32 == 0 && r <= XS_MAX_R &&
          n * (k / 2) < ((int64_t)1 << 31) && m * k * 2 < ((int64_t)1 << 31) && (int64_t)r * k * 2 < ((int64_t)1 << 31);
 }
-
-int decode_xs_fused_rank() { return XS_FUSED_R; }
 
 // Spans: the fewest with at most XS_MAX_WAVES waves each; waves: just enough for
 // the span.  The tile runs (G) are chosen at launch from the device's CU count.
@@ -526,30 +509,45 @@ constexpr int kXsGroupsPerCu = 1;
 constexpr int kXsMaxTilesPerGroup = 6;
 constexpr int kXsMaxLds = 160 * 1024 - 64;      // dynamic LDS bytes a workgroup may take
 
-template <int FMT, int TG, int SC>
-static hipError_t launch_xs_tg(dim3 grid, dim3 block, size_t lds, hipStream_t stream, const uint16_t* x, int m,
-                               int64_t k, const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t n,
-                               const uint16_t* la, const float* t, const uint16_t* lb, int r, uint16_t* y, float* part,
-                               uint32_t* cnt, const XsConfig& c, int G, int tg, int lb16) {
+struct XsLaunch {
+  const uint16_t* x;
+  int m;
+  int64_t k;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* ts;
+  int64_t n;
+  const uint16_t* la;
+  const uint16_t* lb;
+  int r, lparts, lsw;
+  uint32_t* lsync;
+  uint16_t* y;
+  float* part;
+  uint32_t* cnt;
+  int G, tg, lb16;
+};
+
+template <int FMT, int TG, int SC, bool LORA>
+static hipError_t launch_xs_tg(dim3 grid, dim3 block, size_t lds, hipStream_t stream, const XsLaunch& a,
+                               const XsConfig& c) {
   static bool lds_set = false;
   if (!lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_xs_kernel<FMT, TG, SC>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_xs_kernel<FMT, TG, SC, LORA>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kXsMaxLds);
     if (e != hipSuccess) return e;
     lds_set = true;
   }
-  hipLaunchKernelGGL((decode_xs_kernel<FMT, TG, SC>), grid, block, lds, stream, x, m, k, codes, scales, ts, n, la, t,
-                     lb, r, y, part, cnt, c.splits, c.qspan, c.ntiles, G, tg, lb16);
+  hipLaunchKernelGGL((decode_xs_kernel<FMT, TG, SC, LORA>), grid, block, lds, stream, a.x, a.m, a.k, a.codes, a.scales,
+                     a.ts, a.n, a.la, a.lb, a.r, a.lparts, a.lsw, a.lsync, (uint64_t)(LORA ? lora_wait_ticks() : 0),
+                     a.y, a.part, a.cnt, c.splits, c.qspan, c.ntiles, a.G, a.tg, a.lb16);
   return hipGetLastError();
 }
 
-template <int FMT>
-static hipError_t launch_xs_fmt(dim3 grid, dim3 block, size_t lds, hipStream_t stream, const uint16_t* x, int m,
-                                int64_t k, const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t n,
-                                const uint16_t* la, const float* t, const uint16_t* lb, int r, uint16_t* y,
-                                float* part, uint32_t* cnt, const XsConfig& c, int G, int tg, int lb16, int sc) {
-#define FP4W_XS(TGv, SCv) \
-  launch_xs_tg<FMT, TGv, SCv>(grid, block, lds, stream, x, m, k, codes, scales, ts, n, la, t, lb, r, y, part, cnt, c, G, tg, lb16)
+template <int FMT, bool LORA>
+static hipError_t launch_xs_fmt(dim3 grid, dim3 block, size_t lds, hipStream_t stream, const XsLaunch& a,
+                                const XsConfig& c, int sc) {
+#define FP4W_XS(TGv, SCv) launch_xs_tg<FMT, TGv, SCv, LORA>(grid, block, lds, stream, a, c)
+  const int tg = a.tg;
   if (sc) {
     if (tg <= 1) return FP4W_XS(1, 1);
     if (tg <= 2) return FP4W_XS(2, 1);
@@ -576,11 +574,10 @@ static int device_cu_count() {
 }
 
 hipError_t launch_decode_xs(int fmt, const XsConfig& c, const void* x, int64_t m, int64_t k, const uint8_t* codes,
-                            const uint8_t* scales, const float* ts, int64_t n, const void* la, const float* t,
-                            const void* lb, int r, void* y, float* part, uint32_t* cnt, hipStream_t stream) {
-  // LoRA: A (r <= 16, formed in the kernel) or t = x A^T given; neither: none
-  if (la && r > XS_FUSED_R) return hipErrorInvalidValue;
-  const int rr = (la || t) ? r : 0;
+                            const uint8_t* scales, const float* ts, int64_t n, const void* la, const void* lb, int r,
+                            uint32_t* lsync, void* y, float* part, uint32_t* cnt, hipStream_t stream) {
+  const int rr = la && lb && k > 0 ? r : 0;      // k = 0: t = x A^T is zero
+  if (rr > XS_MAX_R || m * rr > 1024) return hipErrorInvalidValue;
   // tile runs: about kXsGroupsPerCu workgroups per CU over all spans, at most
   // kXsMaxTilesPerGroup tiles each, never more runs than tiles
   int64_t G = (int64_t)device_cu_count() * kXsGroupsPerCu / c.splits;
@@ -604,18 +601,33 @@ hipError_t launch_decode_xs(int fmt, const XsConfig& c, const void* x, int64_t m
     lds = (size_t)xs_layout((int)m, c.nw, (int)tg, rr, 0).bytes;
   }
   if (lds > (size_t)kXsMaxLds) return hipErrorInvalidValue;
-  const int lb16 = (reinterpret_cast<uintptr_t>(lb) & 15u) == 0 && rr % 8 == 0 ? 1 : 0;
-  const dim3 grid((unsigned)(G * c.splits)), block((unsigned)(64 * c.nw));
-  const uint16_t* xx = reinterpret_cast<const uint16_t*>(x);
-  const uint16_t* aa = rr > 0 && la ? reinterpret_cast<const uint16_t*>(la) : nullptr;
-  const float* tt = rr > 0 && !la ? t : nullptr;
-  const uint16_t* bb = reinterpret_cast<const uint16_t*>(lb);
-  uint16_t* yy = reinterpret_cast<uint16_t*>(y);
+  XsLaunch a{};
+  a.x = reinterpret_cast<const uint16_t*>(x);
+  a.m = (int)m;
+  a.k = k;
+  a.codes = codes;
+  a.scales = scales;
+  a.ts = ts;
+  a.n = n;
+  a.la = rr > 0 ? reinterpret_cast<const uint16_t*>(la) : nullptr;
+  a.lb = reinterpret_cast<const uint16_t*>(lb);
+  a.r = rr;
+  // chunk workgroups of the LoRA down-projection go first in the grid
+  a.lsw = rr > 0 ? lora_chunk_steps(c.nw, k, (int)m * rr) : kLoraStepsPerLoad;
+  a.lparts = rr > 0 ? lora_chunk_count(c.nw, k, a.lsw) : 0;
+  a.lsync = lsync;
+  a.y = reinterpret_cast<uint16_t*>(y);
+  a.part = part;
+  a.cnt = cnt;
+  a.G = (int)G;
+  a.tg = (int)tg;
+  a.lb16 = (reinterpret_cast<uintptr_t>(lb) & 15u) == 0 && rr % 8 == 0 ? 1 : 0;
+  const dim3 grid((unsigned)(a.lparts + G * c.splits)), block((unsigned)(64 * c.nw));
   if (fmt == FMT_NVFP4)
-    return launch_xs_fmt<FMT_NVFP4>(grid, block, lds, stream, xx, (int)m, k, codes, scales, ts, n, aa, tt, bb, rr, yy, part,
-                                    cnt, c, (int)G, (int)tg, lb16, sc);
-  return launch_xs_fmt<FMT_MXFP4>(grid, block, lds, stream, xx, (int)m, k, codes, scales, ts, n, aa, tt, bb, rr, yy, part,
-                                  cnt, c, (int)G, (int)tg, lb16, sc);
+    return rr > 0 ? launch_xs_fmt<FMT_NVFP4, true>(grid, block, lds, stream, a, c, sc)
+                  : launch_xs_fmt<FMT_NVFP4, false>(grid, block, lds, stream, a, c, sc);
+  return rr > 0 ? launch_xs_fmt<FMT_MXFP4, true>(grid, block, lds, stream, a, c, sc)
+                : launch_xs_fmt<FMT_MXFP4, false>(grid, block, lds, stream, a, c, sc);
 }
 
 // ---- grouped ------------------------------------------------------------------------

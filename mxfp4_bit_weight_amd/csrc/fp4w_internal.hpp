@@ -72,13 +72,11 @@ struct XsConfig {
 };
 bool decode_xs_supports(int64_t m, int64_t n, int64_t k, int r);
 XsConfig plan_decode_xs(int64_t m, int64_t n, int64_t k, int r);
-// LoRA operands: la = A (r x k bf16, r <= decode_xs_fused_rank(): the kernel forms
-// t = x A^T itself) or t = x A^T (m x r fp32, complete), and lb = B (n x r bf16);
-// la and t both nullptr: no LoRA.
-int decode_xs_fused_rank();
+// LoRA operands: la = A (r x k bf16) and lb = B (n x r bf16), or nullptr (no
+// LoRA); the kernel forms t = x A^T itself (lora_handover.hpp, through lsync).
 hipError_t launch_decode_xs(int fmt, const XsConfig& c, const void* x, int64_t m, int64_t k, const uint8_t* codes,
-                            const uint8_t* scales, const float* ts, int64_t n, const void* la, const float* t,
-                            const void* lb, int r, void* y, float* part, uint32_t* cnt, hipStream_t stream);
+                            const uint8_t* scales, const float* ts, int64_t n, const void* la, const void* lb, int r,
+                            uint32_t* lsync, void* y, float* part, uint32_t* cnt, hipStream_t stream);
 
 struct LinearPlan {
   int path;            // 0 = decode on the block-scaled MFMA, 2 = decode on bf16 MFMA, 1 = GEMM,

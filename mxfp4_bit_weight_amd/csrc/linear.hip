@@ -6,9 +6,9 @@
 // (QATFactory page, section on how training repeats the engine's arithmetic).
 //
 // Launches per call (plan_linear picks the path):
-//   m = 1:       decode_f8f4_kernel (decode.hip; forms t = x A^T itself)
-//   2 <= m <= 16: decode_xs_kernel  (decode_xs.hip; forms t itself for r <= 16,
-//                                    after lora_down_kernel for larger ranks)
+//   m <= 2 (m <= 4 on small matrices): decode_f8f4_kernel (decode.hip; forms
+//                t = x A^T itself)
+//   other m <= 16: decode_xs_kernel (decode_xs.hip; forms t itself)
 //   m > 16:      lora_down_kernel, then linear_gemm_kernel (LDS-staged bf16 MFMA
 //                GEMM, dequantizing each weight tile once into LDS)
 //   shapes the decode kernels do not take: lora_down_kernel, then
@@ -537,7 +537,6 @@ LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
     p.xs = plan_decode_xs(m, n, k, r);
     if (p.xs.splits > 1 && (p.xs.ntiles + 7) / 8 > kTileSlots) p.path = 1;     // counters would not fit
   }
-  const bool xs_fused = p.path == 3 && r <= decode_xs_fused_rank();     // the kernel forms t itself
   size_t part_floats = 0;
   if (p.path == 3) {
     p.splits = p.xs.splits;
@@ -555,11 +554,10 @@ LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
     part_floats = (size_t)p.splits * n * m;
   }
   if (p.path == 1) p.splits = 1;
-  // LoRA down-projection: formed inside the block-scaled decode kernel (path 0)
-  // or the x-in-registers kernel (path 3, r <= its fused rank), without
-  // workspace beyond the counter area; else by lora_down_kernel (K slices,
-  // ordered sum) into t
-  const bool lora_inside = xs_fused || p.path == 0;
+  // LoRA down-projection: formed inside the decode kernels (paths 0 and 3, chunk
+  // workgroups handing t over through the counter area); else by
+  // lora_down_kernel (K slices, ordered sum) into t
+  const bool lora_inside = p.path == 0 || p.path == 3;
   p.lora_parts = r <= 0 || lora_inside ? 0 : lora_parts_for(m, k);
   size_t off = 0;
   p.off_count = off;
@@ -636,7 +634,7 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
   uint32_t* cnt_m = reinterpret_cast<uint32_t*>(ws + plan.off_count);
   uint32_t* cnt_n = cnt_m + kLoraSlots;
   // t = x A^T for the paths that do not form it inside their decode kernel
-  if (has_lora && plan.path != 0 && !(plan.path == 3 && r <= decode_xs_fused_rank())) {
+  if (has_lora && plan.path != 0 && plan.path != 3) {
     const int64_t nsteps = (k + 31) / 32;
     const int P = plan.lora_parts;
     const int spp = (int)((nsteps + P - 1) / P);
@@ -651,10 +649,9 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
                                       cnt_m + kLsyncBase, y, part, cnt_n, stream);
     if (e != hipSuccess) return e;
   } else if (plan.path == 3) {
-    const bool fused = r <= decode_xs_fused_rank();
     hipError_t e = launch_decode_xs(fmt, plan.xs, x, m, k, codes, scales, tensor_scale, n,
-                                    has_lora && fused ? lora_a : nullptr, has_lora && !fused ? t : nullptr, lora_b,
-                                    r, y, part, cnt_n, stream);
+                                    has_lora ? lora_a : nullptr, has_lora ? lora_b : nullptr, r, cnt_m + kLsyncBase,
+                                    y, part, cnt_n, stream);
     if (e != hipSuccess) return e;
   } else if (plan.path == 2) {
     if (fmt == FMT_NVFP4)

@@ -272,11 +272,18 @@ struct GemmStage {
   uint32_t sv;       // their scale bytes (NVFP4: two, MXFP4: one)
 };
 
-template <int FMT>
+// BUF: buffer loads through descriptors over x, the codes and the scales; a
+// chunk outside the matrices gets an offset past its buffer and reads zeros
+// without touching memory, so no select on the loaded data follows the load
+// (such a select would make the wave wait for the data at once, not when the
+// stage is stored a K tile later).  Needs x and the codes below 2 GiB.
+// Otherwise plain loads of a clamped address, zeroed after the load.
+template <int FMT, bool BUF>
 __device__ __forceinline__ void gemm_load(GemmStage<FMT>& st, const uint16_t* __restrict__ x, int64_t M,
                                           int64_t K, const uint8_t* __restrict__ codes,
                                           const uint8_t* __restrict__ scales, int64_t N, int64_t m0, int64_t n0,
-                                          int64_t k0) {
+                                          int64_t k0, __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t cr,
+                                          __amdgpu_buffer_rsrc_t sr) {
   const int tid = threadIdx.x;
   // x: 256 rows x 64 bf16 = 2048 chunks of 16 B; thread handles rows tid/8 + 64 i, chunk tid % 8
 #pragma unroll
@@ -284,19 +291,30 @@ __device__ __forceinline__ void gemm_load(GemmStage<FMT>& st, const uint16_t* __
     const int64_t mr = m0 + (tid >> 3) + 64 * i;
     const int64_t k = k0 + 8 * (tid & 7);
     const bool ok = mr < M && k < K;
-    st.xv[i] = load16(x + (ok ? mr * K + k : 0));
-    if (!ok) st.xv[i] = (u32x4_t){0u, 0u, 0u, 0u};
+    if (BUF) {
+      st.xv[i] = buffer_load16(xr, ok ? (uint32_t)((mr * K + k) * 2) : kBufferOob);
+    } else {
+      st.xv[i] = load16(x + (ok ? mr * K + k : 0));
+      if (!ok) st.xv[i] = (u32x4_t){0u, 0u, 0u, 0u};
+    }
   }
   // W: 256 rows x 64 codes = 512 chunks of 32 codes; thread handles row tid/2, half tid % 2
   const int64_t blk = (FMT == FMT_NVFP4) ? 16 : 32;
   const int64_t nr = n0 + (tid >> 1);
   const int64_t k = k0 + 32 * (tid & 1);
   const bool ok = nr < N && k < K;
-  const int64_t nrc = ok ? nr : 0, kc = ok ? k : 0;
-  st.cv = load16(codes + nrc * (K / 2) + kc / 2);
-  if (FMT == FMT_NVFP4) st.sv = *reinterpret_cast<const uint16_t*>(scales + nrc * (K / blk) + kc / blk);
-  else st.sv = scales[nrc * (K / blk) + kc / blk];
-  if (!ok) { st.cv = (u32x4_t){0u, 0u, 0u, 0u}; st.sv = 0u; }
+  if (BUF) {
+    st.cv = buffer_load16(cr, ok ? (uint32_t)(nr * (K / 2) + k / 2) : kBufferOob);
+    const uint32_t so = ok ? (uint32_t)(nr * (K / blk) + k / blk) : kBufferOob;
+    if (FMT == FMT_NVFP4) st.sv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(sr, so, 0, 0);
+    else st.sv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sr, so, 0, 0);
+  } else {
+    const int64_t nrc = ok ? nr : 0, kc = ok ? k : 0;
+    st.cv = load16(codes + nrc * (K / 2) + kc / 2);
+    if (FMT == FMT_NVFP4) st.sv = *reinterpret_cast<const uint16_t*>(scales + nrc * (K / blk) + kc / blk);
+    else st.sv = scales[nrc * (K / blk) + kc / blk];
+    if (!ok) { st.cv = (u32x4_t){0u, 0u, 0u, 0u}; st.sv = 0u; }
+  }
 }
 
 template <int FMT>
@@ -342,7 +360,7 @@ __device__ __forceinline__ void gemm_store_lds(const GemmStage<FMT>& st, uint16_
   }
 }
 
-template <int FMT>
+template <int FMT, bool BUF>
 __global__ __launch_bounds__(G_THREADS, 2) void linear_gemm_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t N,
@@ -365,6 +383,10 @@ __global__ __launch_bounds__(G_THREADS, 2) void linear_gemm_kernel(
     for (int j = 0; j < TJ; j++) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (int)((K + G_BK - 1) / G_BK);
+  const int64_t blk = (FMT == FMT_NVFP4) ? 16 : 32;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, BUF ? (uint32_t)(M * K * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes, BUF ? (uint32_t)(N * (K / 2)) : 0u);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, BUF ? (uint32_t)(N * (K / blk)) : 0u);
   // Global loads run two K tiles ahead (two register stages, used alternately):
   // a K tile's MFMAs take well under the latency of a load from HBM.  The
   // barrier waits for LDS work only; the loads of the tile after next stay in
@@ -393,19 +415,19 @@ __global__ __launch_bounds__(G_THREADS, 2) void linear_gemm_kernel(
     }
   };
   GemmStage<FMT> st0, st1;
-  gemm_load<FMT>(st0, x, M, K, codes, scales, N, m0, n0, 0);
-  if (nk > 1) gemm_load<FMT>(st1, x, M, K, codes, scales, N, m0, n0, (int64_t)G_BK);
+  gemm_load<FMT, BUF>(st0, x, M, K, codes, scales, N, m0, n0, 0, xr, cr, sr);
+  if (nk > 1) gemm_load<FMT, BUF>(st1, x, M, K, codes, scales, N, m0, n0, (int64_t)G_BK, xr, cr, sr);
   gemm_store_lds<FMT>(st0, sA0, sB0);
   lds_barrier();
   // iteration kt: tile kt is in LDS buffer kt & 1, tile kt + 1 in the other stage's
   // registers; the freed stage loads tile kt + 2
   for (int kt = 0; kt < nk; kt += 2) {
-    if (kt + 2 < nk) gemm_load<FMT>(st0, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 2) * G_BK);
+    if (kt + 2 < nk) gemm_load<FMT, BUF>(st0, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 2) * G_BK, xr, cr, sr);
     mfma_tile(0);
     if (kt + 1 < nk) gemm_store_lds<FMT>(st1, sA0 + (G_BM * G_LDA), sB0 + (G_BN * G_LDA));
     lds_barrier();
     if (kt + 1 >= nk) break;
-    if (kt + 3 < nk) gemm_load<FMT>(st1, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 3) * G_BK);
+    if (kt + 3 < nk) gemm_load<FMT, BUF>(st1, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 3) * G_BK, xr, cr, sr);
     mfma_tile(1);
     if (kt + 2 < nk) gemm_store_lds<FMT>(st0, sA0, sB0);
     lds_barrier();
@@ -666,22 +688,25 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
     const uint16_t* xx = reinterpret_cast<const uint16_t*>(x);
     const uint16_t* bb = reinterpret_cast<const uint16_t*>(lora_b);
     uint16_t* yy = reinterpret_cast<uint16_t*>(y);
-    static bool lds_set[2] = {false, false};
-    if (!lds_set[fmt]) {
-      hipError_t e = fmt == FMT_NVFP4
-                         ? hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_gemm_kernel<FMT_NVFP4>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
-                         : hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_gemm_kernel<FMT_MXFP4>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      lds_set[fmt] = true;
+    const bool buf = m * k * 2 < ((int64_t)1 << 31) && n * (k / 2) < ((int64_t)1 << 31);
+#define FP4W_GEMM(FMTv, BUFv)                                                                                \
+  do {                                                                                                       \
+    static bool lds_set = false;                                                                             \
+    if (!lds_set) {                                                                                          \
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_gemm_kernel<FMTv, BUFv>),     \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);             \
+      if (e != hipSuccess) return e;                                                                         \
+      lds_set = true;                                                                                        \
+    }                                                                                                        \
+    hipLaunchKernelGGL((linear_gemm_kernel<FMTv, BUFv>), dim3((unsigned)tiles), dim3(G_THREADS), lds, stream, \
+                       xx, m, k, codes, scales, tensor_scale, n, t, bb, has_lora ? r : 0, yy);              \
+  } while (0)
+    if (fmt == FMT_NVFP4) {
+      if (buf) FP4W_GEMM(FMT_NVFP4, true); else FP4W_GEMM(FMT_NVFP4, false);
+    } else {
+      if (buf) FP4W_GEMM(FMT_MXFP4, true); else FP4W_GEMM(FMT_MXFP4, false);
     }
-    if (fmt == FMT_NVFP4)
-      hipLaunchKernelGGL(linear_gemm_kernel<FMT_NVFP4>, dim3((unsigned)tiles), dim3(G_THREADS), lds, stream, xx, m, k,
-                         codes, scales, tensor_scale, n, t, bb, has_lora ? r : 0, yy);
-    else
-      hipLaunchKernelGGL(linear_gemm_kernel<FMT_MXFP4>, dim3((unsigned)tiles), dim3(G_THREADS), lds, stream, xx, m, k,
-                         codes, scales, tensor_scale, n, t, bb, has_lora ? r : 0, yy);
+#undef FP4W_GEMM
   }
   return hipGetLastError();
 }

@@ -259,7 +259,8 @@ __global__ __launch_bounds__(64 * WPW) void linear_decode_kernel(
 // K tile of x is copied to LDS, each K tile of W is loaded as codes and
 // dequantized once into LDS as exact bf16 (e2m1 * dec(sb) has at most 6
 // significant bits; the tensor scale is applied at the end).  The next tile's
-// global loads are in flight while the current one is used.
+// global loads (buffer loads: chunks outside the matrices read zeros) are in
+// flight while the current one is used.
 // ---------------------------------------------------------------------------------
 constexpr int G_BM = 256, G_BN = 256, G_BK = 64;
 constexpr int G_LDA = G_BK + 8;   // bf16 elements per LDS row (16 bytes of padding)
@@ -291,8 +292,9 @@ __device__ __forceinline__ void gemm_load(GemmStage<FMT>& st, const uint16_t* __
     const int64_t mr = m0 + (tid >> 3) + 64 * i;
     const int64_t k = k0 + 8 * (tid & 7);
     const bool ok = mr < M && k < K;
-    if (BUF) {
-      st.xv[i] = buffer_load16(xr, ok ? (uint32_t)((mr * K + k) * 2) : kBufferOob);
+    if (BUF) {                                   // 32-bit offsets: x below 2 GiB
+      const uint32_t xo = ((uint32_t)mr * (uint32_t)K + (uint32_t)k) * 2u;
+      st.xv[i] = buffer_load16(xr, ok ? xo : kBufferOob);
     } else {
       st.xv[i] = load16(x + (ok ? mr * K + k : 0));
       if (!ok) st.xv[i] = (u32x4_t){0u, 0u, 0u, 0u};
@@ -303,9 +305,11 @@ __device__ __forceinline__ void gemm_load(GemmStage<FMT>& st, const uint16_t* __
   const int64_t nr = n0 + (tid >> 1);
   const int64_t k = k0 + 32 * (tid & 1);
   const bool ok = nr < N && k < K;
-  if (BUF) {
-    st.cv = buffer_load16(cr, ok ? (uint32_t)(nr * (K / 2) + k / 2) : kBufferOob);
-    const uint32_t so = ok ? (uint32_t)(nr * (K / blk) + k / blk) : kBufferOob;
+  if (BUF) {                                     // 32-bit offsets: the codes below 2 GiB
+    const uint32_t co = (uint32_t)nr * (uint32_t)(K >> 1) + ((uint32_t)k >> 1);
+    st.cv = buffer_load16(cr, ok ? co : kBufferOob);
+    const uint32_t so0 = (uint32_t)nr * (uint32_t)(K / blk) + (uint32_t)k / (uint32_t)blk;
+    const uint32_t so = ok ? so0 : kBufferOob;
     if (FMT == FMT_NVFP4) st.sv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(sr, so, 0, 0);
     else st.sv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sr, so, 0, 0);
   } else {
@@ -387,10 +391,8 @@ __global__ __launch_bounds__(G_THREADS, 2) void linear_gemm_kernel(
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, BUF ? (uint32_t)(M * K * 2) : 0u);
   const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes, BUF ? (uint32_t)(N * (K / 2)) : 0u);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, BUF ? (uint32_t)(N * (K / blk)) : 0u);
-  // Global loads run two K tiles ahead (two register stages, used alternately):
-  // a K tile's MFMAs take well under the latency of a load from HBM.  The
-  // barrier waits for LDS work only; the loads of the tile after next stay in
-  // flight across it.
+  // The barrier waits for LDS work only; the global loads of the next tile stay
+  // in flight across it.
   auto lds_barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
@@ -414,22 +416,29 @@ __global__ __launch_bounds__(G_THREADS, 2) void linear_gemm_kernel(
         for (int j = 0; j < TJ; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   };
-  GemmStage<FMT> st0, st1;
-  gemm_load<FMT, BUF>(st0, x, M, K, codes, scales, N, m0, n0, 0, xr, cr, sr);
-  if (nk > 1) gemm_load<FMT, BUF>(st1, x, M, K, codes, scales, N, m0, n0, (int64_t)G_BK, xr, cr, sr);
-  gemm_store_lds<FMT>(st0, sA0, sB0);
+  // One register stage: after a tile's MFMAs the stage (the next tile) goes to
+  // the other LDS buffer and is refilled with the tile after that, so its loads
+  // run under the next tile's MFMAs.  (Two stages, loads two tiles ahead, were
+  // no faster: the compiler's wait counting lost the order of the stages'
+  // loads across the unrolled loop and waited for all of them.)
+  GemmStage<FMT> sg;
+  gemm_load<FMT, BUF>(sg, x, M, K, codes, scales, N, m0, n0, 0, xr, cr, sr);
+  gemm_store_lds<FMT>(sg, sA0, sB0);
+  if (nk > 1) gemm_load<FMT, BUF>(sg, x, M, K, codes, scales, N, m0, n0, (int64_t)G_BK, xr, cr, sr);
   lds_barrier();
-  // iteration kt: tile kt is in LDS buffer kt & 1, tile kt + 1 in the other stage's
-  // registers; the freed stage loads tile kt + 2
   for (int kt = 0; kt < nk; kt += 2) {
-    if (kt + 2 < nk) gemm_load<FMT, BUF>(st0, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 2) * G_BK, xr, cr, sr);
     mfma_tile(0);
-    if (kt + 1 < nk) gemm_store_lds<FMT>(st1, sA0 + (G_BM * G_LDA), sB0 + (G_BN * G_LDA));
+    if (kt + 1 < nk) {
+      gemm_store_lds<FMT>(sg, sA0 + (G_BM * G_LDA), sB0 + (G_BN * G_LDA));
+      if (kt + 2 < nk) gemm_load<FMT, BUF>(sg, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 2) * G_BK, xr, cr, sr);
+    }
     lds_barrier();
     if (kt + 1 >= nk) break;
-    if (kt + 3 < nk) gemm_load<FMT, BUF>(st1, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 3) * G_BK, xr, cr, sr);
     mfma_tile(1);
-    if (kt + 2 < nk) gemm_store_lds<FMT>(st0, sA0, sB0);
+    if (kt + 2 < nk) {
+      gemm_store_lds<FMT>(sg, sA0, sB0);
+      if (kt + 3 < nk) gemm_load<FMT, BUF>(sg, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 3) * G_BK, xr, cr, sr);
+    }
     lds_barrier();
   }
 

@@ -134,9 +134,8 @@ size_t fp4w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
  *    workgroups form t = x A^T on the bf16 matrix core, one K chunk each, and
  *    hand it to the workgroups that write the outputs (chunks added in a fixed
  *    order: the result does not depend on scheduling).
- *  - other m <= 16: one decode kernel holding x in registers (it also forms
- *    t = x A^T when r <= 16; larger ranks get a LoRA down-projection launch
- *    first): the weights are decoded exactly to fp16 (NVFP4, with x scaled to
+ *  - other m <= 16: one launch of a decode kernel holding x in registers (with
+ *    a LoRA, t = x A^T is formed and handed over inside it as above): the weights are decoded exactly to fp16 (NVFP4, with x scaled to
  *    fp16 by a power of two per row and K range: exact for every element within
  *    2^28 of that range's largest magnitude) or bf16 (MXFP4) in registers and
  *    fed to the 16-bit MFMA.  MXFP4 weights whose decoded value exceeds bf16's

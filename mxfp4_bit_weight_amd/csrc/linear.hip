@@ -416,29 +416,75 @@ __global__ __launch_bounds__(G_THREADS, 2) void linear_gemm_kernel(
         for (int j = 0; j < TJ; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   };
-  // One register stage: after a tile's MFMAs the stage (the next tile) goes to
-  // the other LDS buffer and is refilled with the tile after that, so its loads
-  // run under the next tile's MFMAs.  (Two stages, loads two tiles ahead, were
-  // no faster: the compiler's wait counting lost the order of the stages'
-  // loads across the unrolled loop and waited for all of them.)
+  // One register stage holds the next K tile.  During the second half of a
+  // tile's MFMAs the stage is dequantized and stored into the other LDS buffer,
+  // one piece after each MFMA, then refilled with the tile after that, so its
+  // loads run under the next tile's MFMAs and the barrier finds the stores done.
   GemmStage<FMT> sg;
   gemm_load<FMT, BUF>(sg, x, M, K, codes, scales, N, m0, n0, 0, xr, cr, sr);
   gemm_store_lds<FMT>(sg, sA0, sB0);
-  if (nk > 1) gemm_load<FMT, BUF>(sg, x, M, K, codes, scales, N, m0, n0, (int64_t)G_BK, xr, cr, sr);
+  gemm_load<FMT, BUF>(sg, x, M, K, codes, scales, N, m0, n0, (int64_t)G_BK, xr, cr, sr);
   lds_barrier();
-  for (int kt = 0; kt < nk; kt += 2) {
-    mfma_tile(0);
-    if (kt + 1 < nk) {
-      gemm_store_lds<FMT>(sg, sA0 + (G_BM * G_LDA), sB0 + (G_BN * G_LDA));
-      if (kt + 2 < nk) gemm_load<FMT, BUF>(sg, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 2) * G_BK, xr, cr, sr);
+  const int srow = threadIdx.x >> 1, scol = 32 * (threadIdx.x & 1);
+  auto step = [&](int cur, int64_t kload) __attribute__((always_inline)) {
+    const uint16_t* a = sA0 + cur * (G_BM * G_LDA);
+    const uint16_t* b = sB0 + cur * (G_BN * G_LDA);
+    uint16_t* wa = sA0 + (cur ^ 1) * (G_BM * G_LDA);
+    uint16_t* wb = sB0 + (cur ^ 1) * (G_BN * G_LDA) + srow * G_LDA + scol;
+    u32x4_t o = {0u, 0u, 0u, 0u};
+    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < G_BK / 32; kk++) {
+      bf16x8_t af[TI], bfr[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; i++)
+        af[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(a + (wm * 64 + i * 16 + li) * G_LDA + kk * 32 + 8 * g));
+#pragma unroll
+      for (int j = 0; j < TJ; j++)
+        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(b + (wn * 128 + j * 16 + li) * G_LDA + kk * 32 + 8 * g));
+      if (kk == 1) {
+        if (FMT == FMT_NVFP4) { d0 = e4m3_to_f32(sg.sv & 0xFFu); d1 = e4m3_to_f32((sg.sv >> 8) & 0xFFu); }
+        else d0 = e8m0_scale_operand(sg.sv);
+      }
+#pragma unroll
+      for (int i = 0; i < TI; i++)
+#pragma unroll
+        for (int j = 0; j < TJ; j++) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          const int slot = i * TJ + j;
+          if (kk == 1) {
+            if (slot < 4) {
+              const int rr = (threadIdx.x >> 3) + 64 * slot, c = 8 * (threadIdx.x & 7);
+              *reinterpret_cast<u32x4_t*>(wa + rr * G_LDA + c) = sg.xv[slot];
+            } else if (slot < 20) {
+              const int di = slot - 4, q = di >> 2, h = di & 3;
+              const uint32_t dw = sg.cv[q];
+              uint32_t v;
+              if (FMT == FMT_NVFP4) {
+                const float d = q < 2 ? d0 : d1;
+                const f32x2_t f = h == 0 ? fp4x2_to_f32x2<0>(dw, 1.0f) : h == 1 ? fp4x2_to_f32x2<1>(dw, 1.0f)
+                                : h == 2 ? fp4x2_to_f32x2<2>(dw, 1.0f) : fp4x2_to_f32x2<3>(dw, 1.0f);
+                v = (__float_as_uint(f.x * d) >> 16) | (__float_as_uint(f.y * d) & 0xFFFF0000u);
+              } else {
+                v = h == 0 ? fp4x2_to_bf16x2_scaled<0>(dw, d0) : h == 1 ? fp4x2_to_bf16x2_scaled<1>(dw, d0)
+                  : h == 2 ? fp4x2_to_bf16x2_scaled<2>(dw, d0) : fp4x2_to_bf16x2_scaled<3>(dw, d0);
+              }
+              o[h] = v;
+              if (h == 3) *reinterpret_cast<u32x4_t*>(wb + 8 * q) = o;
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    gemm_load<FMT, BUF>(sg, x, M, K, codes, scales, N, m0, n0, kload, xr, cr, sr);
+  };
+  // every step stores and loads: loads past K read zeros, and the last steps'
+  // stores go to a buffer no later step reads
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(0, (int64_t)(kt + 2) * G_BK);
     lds_barrier();
     if (kt + 1 >= nk) break;
-    mfma_tile(1);
-    if (kt + 2 < nk) {
-      gemm_store_lds<FMT>(sg, sA0, sB0);
-      if (kt + 3 < nk) gemm_load<FMT, BUF>(sg, x, M, K, codes, scales, N, m0, n0, (int64_t)(kt + 3) * G_BK, xr, cr, sr);
-    }
+    step(1, (int64_t)(kt + 3) * G_BK);
     lds_barrier();
   }
 

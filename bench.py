@@ -284,20 +284,23 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
     rows["decode_linear_with_lora"] = dec
     log("[bench] decode rows done")
 
-    # prefill GEMM: x 16384 x 3584, W (18944, 3584), LoRA r = 16
-    d = decode[(0, "gate_up")]
-    n, k = d["n"], d["k"]
+    # prefill GEMM: x 16384 x 3584, W (18944, 3584), LoRA r = 16, both formats
     mrows = W.PREFILL_M
-    x = bf16(W.normal_bf16(300, W.TID_X, (mrows, k), 1.0))
-    y = torch.empty((mrows, n), dtype=torch.bfloat16, device=dev)
-    q, a, b = d["qs"][0]
-    wsg = torch.zeros(fp4w.linear_workspace_bytes(mrows, n, k, rank), dtype=torch.uint8, device=dev)
-    gms, _ = time_loop(lambda i: fp4w.linear(x, q, a, b, out=y, workspace=wsg), 5, 2)
-    fl = linear_flops(mrows, n, k, rank)
-    tf = fl / (gms * 1e-3) / 1e12
-    rows["prefill_gemm_nvfp4"] = {"m": mrows, "n": n, "k": k, "ms": round(gms, 3), "TFLOP/s": round(tf, 1),
-                                  "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 1), "algorithmic_flop": fl}
-    log(f"[bench] prefill GEMM {gms:.3f} ms, {tf:.1f} TFLOP/s")
+    for fmt in (0, 1):
+        d = decode[(fmt, "gate_up")]
+        n, k = d["n"], d["k"]
+        x = bf16(W.normal_bf16(300, W.TID_X, (mrows, k), 1.0))
+        y = torch.empty((mrows, n), dtype=torch.bfloat16, device=dev)
+        q, a, b = d["qs"][0]
+        wsg = torch.zeros(fp4w.linear_workspace_bytes(mrows, n, k, rank), dtype=torch.uint8, device=dev)
+        gms, _ = time_loop(lambda i: fp4w.linear(x, q, a, b, out=y, workspace=wsg), 5, 3)
+        fl = linear_flops(mrows, n, k, rank)
+        tf = fl / (gms * 1e-3) / 1e12
+        name = "nvfp4" if fmt == 0 else "mxfp4"
+        rows[f"prefill_gemm_{name}"] = {"m": mrows, "n": n, "k": k, "ms": round(gms, 3), "TFLOP/s": round(tf, 1),
+                                        "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 1), "algorithmic_flop": fl}
+        log(f"[bench] prefill GEMM {name} {gms:.3f} ms, {tf:.1f} TFLOP/s")
+        del x, y, wsg
     del x, y
     torch.cuda.empty_cache()
 

@@ -97,6 +97,14 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
                          const void* lora_b, int r, void* y, void* workspace, const LinearPlan& plan,
                          hipStream_t stream);
 
+// The m > 16 GEMM with W decoded in registers (gemm.hip): K a multiple of 256,
+// x and the codes below 2 GiB each, scales 16-byte aligned; t = x A^T (fp32,
+// m x r) formed beforehand.
+bool gemm_w4_supports(int64_t m, int64_t n, int64_t k, const void* scales);
+hipError_t launch_gemm_w4(int fmt, const void* x, int64_t m, int64_t k, const uint8_t* codes, const uint8_t* scales,
+                          const float* tensor_scale, int64_t n, const float* t, const void* lora_b, int r, void* y,
+                          hipStream_t stream);
+
 // Grouped linear on the x-in-registers kernel (decode_xs.hip): K in one span.
 bool grouped_xs_supports(int64_t num_tokens, int64_t n, int64_t k);
 hipError_t launch_grouped_xs(int fmt, const void* x, int64_t num_tokens, const int32_t* row_index,

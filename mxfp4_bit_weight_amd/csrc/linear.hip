@@ -9,8 +9,10 @@
 //   m <= 2 (m <= 4 on small matrices): decode_f8f4_kernel (decode.hip; forms
 //                t = x A^T itself)
 //   other m <= 16: decode_xs_kernel (decode_xs.hip; forms t itself)
-//   m > 16:      lora_down_kernel, then linear_gemm_kernel (LDS-staged bf16 MFMA
-//                GEMM, dequantizing each weight tile once into LDS)
+//   m > 16:      lora_down_kernel, then gemm_w4_kernel (gemm.hip: bf16 MFMA GEMM
+//                with W decoded in registers; K a multiple of 256, x and the
+//                codes below 2 GiB, scales 16-byte aligned) or else
+//                linear_gemm_kernel (each weight tile dequantized once into LDS)
 //   shapes the decode kernels do not take: lora_down_kernel, then
 //                linear_decode_kernel (skinny.hpp)
 // lora_down_kernel: t = x A^T (fp32, M x r), split over K, ordered sum.
@@ -737,6 +739,10 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
     else
       (void)launch_decode<FMT_MXFP4>(1, x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part, cnt_n,
                                plan.splits, stream);
+  } else if (gemm_w4_supports(m, n, k, scales)) {
+    hipError_t e = launch_gemm_w4(fmt, x, m, k, codes, scales, tensor_scale, n, t, has_lora ? lora_b : nullptr,
+                                  has_lora ? r : 0, y, stream);
+    if (e != hipSuccess) return e;
   } else {
     const int64_t tiles = ((m + G_BM - 1) / G_BM) * ((n + G_BN - 1) / G_BN);
     const size_t lds = sizeof(uint16_t) * 2 * (G_BM + G_BN) * G_LDA;

@@ -293,7 +293,7 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
         y = torch.empty((mrows, n), dtype=torch.bfloat16, device=dev)
         q, a, b = d["qs"][0]
         wsg = torch.zeros(fp4w.linear_workspace_bytes(mrows, n, k, rank), dtype=torch.uint8, device=dev)
-        gms, _ = time_loop(lambda i: fp4w.linear(x, q, a, b, out=y, workspace=wsg), 5, 3)
+        gms, _ = time_loop(lambda i: fp4w.linear(x, q, a, b, out=y, workspace=wsg), 10, 10)
         fl = linear_flops(mrows, n, k, rank)
         tf = fl / (gms * 1e-3) / 1e12
         name = "nvfp4" if fmt == 0 else "mxfp4"
@@ -301,7 +301,6 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
                                         "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 1), "algorithmic_flop": fl}
         log(f"[bench] prefill GEMM {name} {gms:.3f} ms, {tf:.1f} TFLOP/s")
         del x, y, wsg
-    del x, y
     torch.cuda.empty_cache()
 
     # quantize over a 7B-shaped set: 28 layers x {2 x (18944,3584), (3584,18944), 4 x (3584,3584)}

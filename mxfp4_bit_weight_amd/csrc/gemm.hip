@@ -6,38 +6,50 @@
 // values (QATFactory page, section on how training repeats the engine's
 // arithmetic), which is why W is decoded to bf16 here, not x squeezed to FP8.
 //
-// Workgroup: a 256 x 256 tile of y, 4 waves (one per SIMD), each a 128 x 128
-// wave tile: 4 x 4 products of v_mfma_f32_32x32x16_bf16, 256 accumulator
-// registers.  Per K tile of 64:
-//   - x (256 rows x 64) is staged in LDS, double-buffered;
-//   - the weight codes and scales stay packed: they are staged in LDS 4 K tiles
-//     (256 k) at a time, with loads of whole 128-byte lines, and each wave reads
-//     the codes of its columns from there and decodes them to exact bf16 just
-//     before the MFMAs that take them (e2m1 * dec(scale) has at most 6
+// One workgroup per CU, looping over 256 x 256 tiles of y; 4 waves (one per
+// SIMD), each a 128 x 128 wave tile: 4 x 4 products of v_mfma_f32_32x32x16_bf16,
+// 256 accumulator registers.  Operands reach LDS by DMA (buffer loads that write
+// LDS directly, 16 bytes a lane, lane-contiguous), with no register staging and
+// no LDS store instructions:
+//   - x: one 256 x 64 bf16 tile per K tile, three buffers, loaded two K tiles
+//     ahead;
+//   - W: codes and scales stay packed, one stage per 2 K tiles (256 rows x 64
+//     code bytes and their scale bytes), three stages, loaded two stages ahead.
+//     Each wave reads the codes of its columns and decodes them to exact bf16
+//     just before the MFMAs that take them (e2m1 * dec(scale) has at most 6
 //     significant bits).  Lane half hh of a wave owns k = 32 hh .. 32 hh + 31
 //     of each of its 4 columns in a K tile; step s of the tile contracts
 //     k = 32 hh + 8 s + e in lane half hh, the x fragment read from the same k.
-// LDS rows of x and of codes are 128 bytes, unpadded, their 8 chunks of 16
-// bytes XOR-swizzled so that tile stores (one row, 8 chunks) and fragment reads
-// (32 rows, one chunk) spread over all bank groups.
+// LDS rows are unpadded, their 16-byte chunks XOR-swizzled (the DMA lanes load
+// the chunk that belongs at their position) so that fragment reads of 32 rows
+// at one chunk spread over all bank groups.  One barrier per K tile; before it
+// each wave waits for its own DMA of the next K tile (a fixed count of later
+// loads may stay in flight).
 // W is product A of the MFMA and x product B; the y block goes out through LDS
 // in whole 128-byte lines.
-// Loads go through buffer descriptors (chunks outside the matrices read zeros,
-// no select after the load): x and the codes must each lie below 2 GiB, K must
-// be a multiple of 256 and the scales 16-byte aligned.
+// Loads and stores go through buffer descriptors (out of range: zeros read,
+// stores dropped): x, the codes and y must each lie below 2 GiB, 2 GiB and
+// 4 GiB, K must be a multiple of 128 and the scales 16-byte aligned.
 #include "fp4w_device.hpp"
 #include "fp4w_internal.hpp"
 
 namespace fp4w {
 
 constexpr int W4_BM = 256, W4_BN = 256, W4_BK = 64, W4_THREADS = 256;
-constexpr int W4_SK = 4;                               // K tiles per weight stage (256 k)
+constexpr int W4_SK = 2;                               // K tiles per weight stage (128 k)
 constexpr int W4_GM = 4;                               // rows of tiles a group of the tile order spans
 constexpr int W4_XB = W4_BM * 128;                     // bytes per x buffer (256 rows x 64 bf16)
-constexpr int W4_CB = W4_BN * 128;                     // bytes per code stage (256 rows x 256 codes)
-constexpr int W4_SB = W4_BN * 16;                      // bytes per scale stage (NVFP4: 16 per row, MXFP4: 8)
-constexpr int W4_LDS = 2 * (W4_XB + W4_CB + W4_SB);    // x buffers, code stages, scale stages
-static_assert(4 * 128 * 272 <= W4_LDS, "the epilogue's 4 blocks of y (128 rows of 272 bytes) fit the LDS");
+constexpr int W4_CB = W4_BN * 64;                      // code bytes per weight stage (256 rows x 128 codes)
+constexpr int W4_WB = W4_CB + W4_BN * 8;               // bytes per weight stage (codes, then 8 scale bytes a row)
+// LDS: [x0][x1][w0][w1][x2][w2]; the last x buffer and weight stage are
+// contiguous and hold the epilogue's y staging (the next tile's first DMA goes
+// to x0, x1, w0, w1 meanwhile)
+constexpr int W4_X0 = 0, W4_X1 = W4_XB, W4_W0 = 2 * W4_XB, W4_W1 = W4_W0 + W4_WB;
+constexpr int W4_X2 = W4_W1 + W4_WB, W4_W2 = W4_X2 + W4_XB;
+constexpr int W4_LDS = W4_W2 + W4_WB;                  // 153600 bytes
+constexpr int W4_YROW = 272;                           // bytes per staged y row (256 + 16 of padding)
+static_assert(4 * 32 * W4_YROW <= W4_XB + W4_WB, "a pass of the y staging fits the last x buffer and stage");
+static_assert(W4_LDS <= 160 * 1024, "LDS of one CU");
 
 // Position of chunk c of LDS row m: c ^ swz(m), swz(m) = (m ^ (m >> 3 & 1)) & 7.
 // Rows m..m+7 (m a multiple of 8) get 8 distinct swizzles, and over 16 rows each
@@ -60,6 +72,26 @@ __device__ __forceinline__ float acc_write(float v) {
   return a;
 }
 
+// Position of chunk c (of 4) of a 64-byte code row r: c ^ swzw(r),
+// swzw(r) = ((r >> 1) ^ (r >> 3)) & 3: reads of 8 or 16 consecutive rows at one
+// chunk hit distinct 16-byte slots for 128- and 256-byte bank widths.
+__device__ __forceinline__ int w4_swzw(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
+}
+
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 struct W4Frag {
@@ -73,23 +105,31 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int N,
     const float* __restrict__ t, const uint16_t* __restrict__ lora_b, int r, uint16_t* __restrict__ y, int flags) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* const xb0 = smem;
-  uint8_t* const xb1 = smem + W4_XB;
-  uint8_t* const cb0 = smem + 2 * W4_XB;
-  uint8_t* const sb0 = smem + 2 * W4_XB + 2 * W4_CB;
   constexpr int BLK = (FMT == FMT_NVFP4) ? 16 : 32;
+  constexpr int NSC = (FMT == FMT_NVFP4) ? 2 : 1;        // scale DMAs per wave and stage
   // Tile order: workgroups go to the 8 XCDs in turn (workgroup b to XCD b % 8),
-  // each XCD with its own L2.  XCD x takes a contiguous range of the tiles, and
-  // within it the tiles run W4_GM rows of tiles at a time, column by column, so
-  // the workgroups an XCD runs together share x rows and weight columns.
+  // each XCD with its own L2.  XCD x owns a contiguous range of the tiles, and
+  // within it the tiles run W4_GM rows of tiles at a time, column by column;
+  // the XCD's workgroups (one per CU) take its tiles in turn, so the ones it
+  // runs together share x rows and weight columns.
   const int tiles_n = (N + W4_BN - 1) / W4_BN, tiles_m = (M + W4_BM - 1) / W4_BM;
   const int ntiles = tiles_n * tiles_m;
-  const int xcd = blockIdx.x % 8, per = ntiles / 8, extra = ntiles % 8;
-  const int g = xcd * per + (xcd < extra ? xcd : extra) + (int)blockIdx.x / 8;
-  const int grp = g / (W4_GM * tiles_n), rem = g - grp * (W4_GM * tiles_n);
-  const int gm = min(W4_GM, tiles_m - grp * W4_GM);
-  const int tm = grp * W4_GM + rem % gm, tn = rem / gm;
-  const int m0 = tm * W4_BM, n0 = tn * W4_BN;
+  // XCD x runs nwg of the grid's workgroups and owns that share of the tiles
+  const int grid = (int)gridDim.x, xcd = blockIdx.x % 8, gq = grid / 8, gr = grid % 8;
+  const int nwg = gq + (xcd < gr ? 1 : 0), cum = xcd * gq + (xcd < gr ? xcd : gr);
+  const int xstart = (int)((int64_t)ntiles * cum / grid);
+  const int xcount = (int)((int64_t)ntiles * (cum + nwg) / grid) - xstart;
+  int local = (int)blockIdx.x / 8;
+  if (local >= xcount) return;
+  auto origin = [&](int lc, int& om0, int& on0) __attribute__((always_inline)) {
+    const int g = xstart + lc;
+    const int grp = g / (W4_GM * tiles_n), rem = g - grp * (W4_GM * tiles_n);
+    const int gm = min(W4_GM, tiles_m - grp * W4_GM);
+    om0 = (grp * W4_GM + rem % gm) * W4_BM;
+    on0 = (rem / gm) * W4_BN;
+  };
+  int m0, n0;
+  origin(local, m0, n0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -98,64 +138,70 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
   const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes, (uint32_t)N * (uint32_t)(K / 2));
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (uint32_t)N * (uint32_t)(K / BLK));
 
-  // Staging: thread tid moves chunk tid & 7 of rows tid / 8 + 32 s, s < 8, of
-  // an x tile and of a code stage.  K is a multiple of 256, so within the K
-  // range a chunk is outside its matrix only when its row is (past the buffer's
-  // end: zeros).
-  const int srow = tid >> 3, sc = tid & 7;
-  const int sst = srow * 128 + 16 * (sc ^ w4_swz(srow));            // + 32 s rows: same swizzle
-  const uint32_t xbase = ((uint32_t)(m0 + srow) * (uint32_t)K + 8u * (uint32_t)sc) * 2u;
-  const uint32_t xstep = 32u * (uint32_t)K * 2u;
-  u32x4_t xv[8];
-  auto load_x = [&](int k0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 8; q++) xv[q] = buffer_load16(xr, xbase + ((uint32_t)q * xstep + (uint32_t)k0 * 2u));
+  // DMA lanes.  x: instruction q (of 8) of wave w fills LDS rows 32 q + 8 w ..
+  // + 7 (1 KB); lane l takes row 32 q + 8 w + l / 8, position l % 8, so it loads
+  // that row's chunk (l % 8) ^ swz(row).  Codes: instruction i (of 4) fills rows
+  // 64 i + 16 w .. + 15 (64 bytes each); lane l takes row + l / 4, position
+  // l % 4, chunk (l % 4) ^ swzw(row).  Scales (4-byte DMA, 256 bytes an
+  // instruction): NVFP4 rows 128 i + 32 w + l / 2, word l % 2 (8 bytes a row);
+  // MXFP4 rows 64 w + l, one word.  K is a multiple of 128, so within the K
+  // range a chunk lies outside its matrix only when its row does (past the
+  // buffer's end: zeros).
+  const int xrow = 8 * wave + (lane >> 3);
+  const uint32_t xlane = (uint32_t)(8 * ((lane & 7) ^ w4_swz(xrow))) * 2u;
+  const int crow = 16 * wave + (lane >> 2);
+  const uint32_t clane = 16u * (uint32_t)((lane & 3) ^ w4_swzw(crow));
+  const int srow = (FMT == FMT_NVFP4) ? 32 * wave + (lane >> 1) : 64 * wave + lane;
+  const uint32_t slane = (FMT == FMT_NVFP4) ? 4u * (uint32_t)(lane & 1) : 0u;
+  uint32_t xbase, cbase, sbase;
+  auto set_bases = [&](int om0, int on0) __attribute__((always_inline)) {
+    xbase = (uint32_t)(om0 + xrow) * (uint32_t)K * 2u + xlane;
+    cbase = (uint32_t)(on0 + crow) * (uint32_t)(K / 2) + clane;
+    sbase = (uint32_t)(on0 + srow) * (uint32_t)(K / BLK) + slane;
   };
-  auto store_x = [&](uint8_t* buf) __attribute__((always_inline)) {
+  set_bases(m0, n0);
+  auto dma_xh = [&](uint8_t* buf, int k0, int h) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 8; q++) *reinterpret_cast<u32x4_t*>(buf + sst + 32 * q * 128) = xv[q];
+    for (int q = 4 * h; q < 4 * h + 4; q++)
+      dma16(xr, buf + (32 * q + 8 * wave) * 128, xbase + (uint32_t)q * 32u * (uint32_t)K * 2u + (uint32_t)k0 * 2u);
   };
-  // a code stage: 256 rows x 128 bytes (k0 .. k0 + 255); its scales: row tid,
-  // 16 bytes (NVFP4) or 8 (MXFP4)
-  const uint32_t cbase = (uint32_t)(n0 + srow) * (uint32_t)(K / 2) + 16u * (uint32_t)sc;
-  const uint32_t cstep = 32u * (uint32_t)(K / 2);
-  const uint32_t sbase = (uint32_t)(n0 + tid) * (uint32_t)(K / BLK);
-  u32x4_t cv[8];
-  u32x4_t sv;
-  auto load_w = [&](int k0) __attribute__((always_inline)) {
+  auto dma_x = [&](uint8_t* buf, int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 8; q++) cv[q] = buffer_load16(cr, cbase + ((uint32_t)q * cstep + (uint32_t)(k0 / 2)));
+    for (int q = 0; q < 8; q++)
+      dma16(xr, buf + (32 * q + 8 * wave) * 128, xbase + (uint32_t)q * 32u * (uint32_t)K * 2u + (uint32_t)k0 * 2u);
+  };
+  auto dma_w = [&](uint8_t* buf, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      dma16(cr, buf + (64 * i + 16 * wave) * 64, cbase + (uint32_t)i * 64u * (uint32_t)(K / 2) + (uint32_t)(k0 / 2));
     if (FMT == FMT_NVFP4) {
-      sv = buffer_load16(sr, sbase + (uint32_t)(k0 / 16));
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+        dma4(sr, buf + W4_CB + (128 * i + 32 * wave) * 8, sbase + (uint32_t)i * 128u * (uint32_t)(K / 16) + (uint32_t)(k0 / 16));
     } else {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(sr, sbase + (uint32_t)(k0 / 32), 0, 0);
-      sv = u32x4_t{v[0], v[1], 0u, 0u};
+      dma4(sr, buf + W4_CB + (64 * wave) * 4, sbase + (uint32_t)(k0 / 32));
     }
   };
-  auto store_w = [&](uint8_t* cbuf, uint8_t* sbuf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 8; q++) *reinterpret_cast<u32x4_t*>(cbuf + sst + 32 * q * 128) = cv[q];
-    if (FMT == FMT_NVFP4) *reinterpret_cast<u32x4_t*>(sbuf + 16 * tid) = sv;
-    else *reinterpret_cast<uint2*>(sbuf + 16 * tid) = make_uint2(sv[0], sv[1]);
-  };
 
-  // fragments: x row 128 wm + 32 i + l32 and W row 128 wn + 32 j + l32, chunk
-  // 4 hh + s of an x tile, chunk 2 q + hh of a code stage (K tile q of it)
+  // fragments: x row 128 wm + 32 i + l32, chunk 4 hh + s of an x tile; W row
+  // 128 wn + 32 j + l32, chunk 2 q + hh of a weight stage (its K tile q)
   const int arow = 128 * wm + l32, wrow = 128 * wn + l32;
   int aoff[4];
 #pragma unroll
   for (int s = 0; s < 4; s++) aoff[s] = arow * 128 + 16 * ((4 * hh + s) ^ w4_swz(arow));
+  int woff[2];
+#pragma unroll
+  for (int q = 0; q < 2; q++) woff[q] = wrow * 64 + 16 * ((2 * q + hh) ^ w4_swzw(wrow));
   auto read_a = [&](bf16x8_t* a, const uint8_t* buf, int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; i++) a[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(buf + aoff[s] + 32 * i * 128));
   };
-  auto read_w = [&](W4Frag& f, const uint8_t* cbuf, const uint8_t* sbuf, int q) __attribute__((always_inline)) {
-    const int coff = wrow * 128 + 16 * ((2 * q + hh) ^ w4_swz(wrow));
+  auto read_w = [&](W4Frag& f, const uint8_t* wbuf, int q) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      f.c[j] = *reinterpret_cast<const u32x4_t*>(cbuf + coff + 32 * j * 128);
-      if (FMT == FMT_NVFP4) f.s[j] = *reinterpret_cast<const uint16_t*>(sbuf + (wrow + 32 * j) * 16 + 4 * q + 2 * hh);
-      else f.s[j] = sbuf[(wrow + 32 * j) * 16 + 2 * q + hh];
+      f.c[j] = *reinterpret_cast<const u32x4_t*>(wbuf + woff[q] + 32 * j * 64);
+      if (FMT == FMT_NVFP4) f.s[j] = *reinterpret_cast<const uint16_t*>(wbuf + W4_CB + (wrow + 32 * j) * 8 + 4 * q + 2 * hh);
+      else f.s[j] = wbuf[W4_CB + (wrow + 32 * j) * 4 + 2 * q + hh];
     }
   };
   // column j's fragment for step s: 8 exact bf16 values
@@ -169,23 +215,17 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
       o.z = fp4x2_to_bf16x2_scaled<2>(dw, sc);
       o.w = fp4x2_to_bf16x2_scaled<3>(dw, sc);
     } else {
+      // the products are exact in bf16, so the packing conversion (RNE) keeps them
       const float d = e4m3_to_f32(s < 2 ? (f.s[j] & 0xFFu) : (f.s[j] >> 8));
-      const f32x2_t a0 = fp4x2_to_f32x2<0>(dw, 1.0f), a1 = fp4x2_to_f32x2<1>(dw, 1.0f);
-      const f32x2_t a2 = fp4x2_to_f32x2<2>(dw, 1.0f), a3 = fp4x2_to_f32x2<3>(dw, 1.0f);
-      o.x = (__float_as_uint(a0.x * d) >> 16) | (__float_as_uint(a0.y * d) & 0xFFFF0000u);
-      o.y = (__float_as_uint(a1.x * d) >> 16) | (__float_as_uint(a1.y * d) & 0xFFFF0000u);
-      o.z = (__float_as_uint(a2.x * d) >> 16) | (__float_as_uint(a2.y * d) & 0xFFFF0000u);
-      o.w = (__float_as_uint(a3.x * d) >> 16) | (__float_as_uint(a3.y * d) & 0xFFFF0000u);
+      o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(fp4x2_to_f32x2<0>(dw, 1.0f) * d, bf16x2_t));
+      o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(fp4x2_to_f32x2<1>(dw, 1.0f) * d, bf16x2_t));
+      o.z = __builtin_bit_cast(uint32_t, __builtin_convertvector(fp4x2_to_f32x2<2>(dw, 1.0f) * d, bf16x2_t));
+      o.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(fp4x2_to_f32x2<3>(dw, 1.0f) * d, bf16x2_t));
     }
     return as_bf16x8(o);
   };
 
   f32x16_t acc[4][4];                             // [j: 32 columns of W][i: 32 rows of x]
-#pragma unroll
-  for (int j = 0; j < 4; j++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) acc[j][i] = f32x16_t{};
-
   // 16 MFMAs of step s (x fragments a), the W fragments decoded on the way
   auto mfma_step = [&](const bf16x8_t* a, const W4Frag& f, int s) __attribute__((always_inline)) {
 #pragma unroll
@@ -196,187 +236,218 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
     }
   };
   auto fence = [&]() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+  auto xbuf = [&](int i) __attribute__((always_inline)) -> uint8_t* {
+    return smem + (i == 0 ? W4_X0 : i == 1 ? W4_X1 : W4_X2);
+  };
+  auto wbuf = [&](int i) __attribute__((always_inline)) -> uint8_t* {
+    return smem + (i == 0 ? W4_W0 : i == 1 ? W4_W1 : W4_W2);
+  };
 
-  const int nst = K / (W4_BK * W4_SK);
+  const int nk = K / W4_BK;
   bf16x8_t a0[4], a1[4], a2[4], a3[4];
   W4Frag f0, f1;
-  // K tile q of weight stage S (LDS stage S & 1), x from buffer cur.  On entry
-  // a0 and f hold its step-0 x fragments and its W fragments (reads issued).
-  // Step 0 reads the next tile's W fragments into fn (the next stage's, for
-  // q = 3: stored two tiles before).  During step 1 the x of the next tile
-  // (loaded a tile ago) goes to buffer nxt and the x of the tile after it is
-  // loaded; q = 0 also loads stage S + 1, which q = 2 stores to the other
-  // stage.  The barrier comes before step 3, whose MFMAs cover the reads of the
-  // next tile's step-0 x fragments.
-  auto tile = [&](int S, int q, const uint8_t* cur, uint8_t* nxt, W4Frag& f, W4Frag& fn)
-                  __attribute__((always_inline)) {
-    const int kt = S * W4_SK + q;
-    uint8_t* const cbuf = cb0 + (S & 1) * W4_CB;
-    uint8_t* const sbuf = sb0 + (S & 1) * W4_SB;
-    uint8_t* const cnext = cb0 + ((S + 1) & 1) * W4_CB;
-    uint8_t* const snext = sb0 + ((S + 1) & 1) * W4_SB;
+  // K tile kt = 2 S + q (x buffer kt % 3, weight stage S % 3).  On entry a0 and
+  // f hold its step-0 x fragments and its W fragments (reads issued).  Step 0
+  // reads the next tile's W fragments into fn.  The DMA of x tile kt + 2 (into
+  // the buffer tile kt - 1 used) goes out in halves in steps 0 and 1, and for
+  // q = 0 the DMA of weight stage S + 2 (into the stage S - 1 used) in step 2:
+  // spread over the MFMA steps rather than in one burst, whose LDS writes held
+  // up the steps' fragment reads.  Before the barrier each wave waits for its
+  // DMA of x tile kt + 1 (and so of weight stage S + 1): the loads issued after
+  // it, 8 of x and 4 + NSC of W, may stay in flight.  The barrier comes before
+  // step 3, whose MFMAs cover the reads of the next tile's step-0 x fragments.
+  auto tile = [&](int kt, int q, W4Frag& f, W4Frag& fn) __attribute__((always_inline)) {
+    const int S = kt >> 1;
+    const uint8_t* cur = xbuf(kt % 3);
     read_a(a1, cur, 1);
-    if (q < 3) read_w(fn, cbuf, sbuf, q + 1);
-    else read_w(fn, cnext, snext, 0);
+    if (q == 0) read_w(fn, wbuf(S % 3), 1);
+    else read_w(fn, wbuf((S + 1) % 3), 0);
+    dma_xh(xbuf((kt + 2) % 3), (kt + 2) * W4_BK, 0);
     mfma_step(a0, f, 0);
     fence();
     read_a(a2, cur, 2);
-    store_x(nxt);
-    load_x((kt + 2) * W4_BK);
-    if (q == 0) load_w((S + 1) * W4_SK * W4_BK);
+    dma_xh(xbuf((kt + 2) % 3), (kt + 2) * W4_BK, 1);
     mfma_step(a1, f, 1);
     fence();
     read_a(a3, cur, 3);
-    if (q == 2) store_w(cnext, snext);
+    if (q == 0) dma_w(wbuf((S + 2) % 3), (S + 2) * W4_SK * W4_BK);
     mfma_step(a2, f, 2);
     fence();
-    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): this wave's LDS stores (and reads) done
+    wait_vm_lgkm0<12 + NSC>();
     __builtin_amdgcn_s_barrier();
     fence();
-    read_a(a0, nxt, 0);
+    read_a(a0, xbuf((kt + 1) % 3), 0);
     mfma_step(a3, f, 3);
     fence();
   };
 
-  load_x(0);
-  load_w(0);
-  store_x(xb0);
-  store_w(cb0, sb0);
-  load_x(W4_BK);
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
-  fence();
-  read_a(a0, xb0, 0);
-  read_w(f0, cb0, sb0, 0);
-  // The prologue's loads land before the loop (the empty asm takes their
-  // registers), so the compiler's wait counts at the loop's head follow the
-  // loop's own order of loads.  Otherwise the compiler sank the prologue's loads
-  // to the loop's entry and the merged counts made tiles wait for loads issued
-  // just before them.
-#pragma unroll
-  for (int q = 0; q < 8; q++) asm volatile("" ::"v"(xv[q]));
-  fence();
-  // Loads past K (the last stage's x tiles and weight stage) read the next
-  // rows' data or zeros past the buffers and feed nothing.  (No exit inside
-  // the loop body: a second loop exit made the compiler copy the accumulators.)
-  for (int S = 0; S < nst; S++) {
-    tile(S, 0, xb0, xb1, f0, f1);
-    tile(S, 1, xb1, xb0, f1, f0);
-    tile(S, 2, xb0, xb1, f0, f1);
-    tile(S, 3, xb1, xb0, f1, f0);
-  }
-
-  // epilogue: y = s_t acc + LoRA, the LoRA as MFMA steps over K' = [t_hi | t_lo]
-  // (t split into two bf16 parts, 8 ranks a step) against [B | B]; s_t is
-  // applied before the first LoRA step, or at the store without LoRA.
-  // flags & 2: r a multiple of 8 and B 16-byte aligned, so a lane's 8 ranks of
-  // B and of t are 16-byte loads.
+  // the first tile's first two x tiles and weight stages
+  dma_x(xbuf(0), 0);
+  dma_x(xbuf(1), W4_BK);
+  dma_w(wbuf(0), 0);
+  dma_w(wbuf(1), W4_SK * W4_BK);
   const float st = (FMT == FMT_NVFP4) ? *tensor_scale : 1.0f;
   const bool has_t = t != nullptr && r > 0;
-  const __amdgpu_buffer_rsrc_t br = make_rsrc(lora_b, has_t ? (uint32_t)N * (uint32_t)r * 2u : 0u);
-  const __amdgpu_buffer_rsrc_t tr = make_rsrc(t, has_t ? (uint32_t)M * (uint32_t)r * 4u : 0u);
-  auto pack8 = [](const uint32_t* h) __attribute__((always_inline)) {
-    return as_bf16x8(u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
-  };
-  auto lora_step = [&](int jb, bool scale_first) __attribute__((always_inline)) {
-    // lane half hh covers K' entries 8 hh .. 8 hh + 7: part hh of ranks jb + e
-    bf16x8_t lb[4], tf[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int n = n0 + 128 * wn + 32 * j + l32;
-      if (flags & 2) {
-        lb[j] = as_bf16x8(buffer_load16(br, ((uint32_t)n * (uint32_t)r + (uint32_t)jb) * 2u));
-      } else {
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; e++) h[e] = (n < N && jb + e < r) ? lora_b[(int64_t)n * r + jb + e] : 0u;
-        lb[j] = pack8(h);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int mr = m0 + 128 * wm + 32 * i + l32;
-      float tv[8];
-      if (flags & 2) {
-        const uint32_t o = ((uint32_t)mr * (uint32_t)r + (uint32_t)jb) * 4u;
-        const u32x4_t v0 = buffer_load16(tr, o), v1 = buffer_load16(tr, o + 16u);
-#pragma unroll
-        for (int e = 0; e < 4; e++) { tv[e] = __uint_as_float(v0[e]); tv[4 + e] = __uint_as_float(v1[e]); }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; e++) tv[e] = (mr < M && jb + e < r) ? t[(int64_t)mr * r + jb + e] : 0.f;
-      }
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const uint32_t hi = f32_to_bf16_rne(tv[e]);
-        h[e] = hh ? f32_to_bf16_rne(tv[e] - __uint_as_float(hi << 16)) : hi;
-      }
-      tf[i] = pack8(h);
-    }
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  fence();
+  for (;;) {
+    read_a(a0, xbuf(0), 0);
+    read_w(f0, wbuf(0), 0);
 #pragma unroll
     for (int j = 0; j < 4; j++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        if (scale_first) {
-#pragma unroll
-          for (int e = 0; e < 16; e++) acc[j][i][e] = acc_write(acc_read(acc[j][i][e]) * st);
-        }
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lb[j], tf[i], acc[j][i], 0, 0, 0);
-      }
-  };
-  if (has_t) {
-    lora_step(0, FMT == FMT_NVFP4);
-    for (int jb = 8; jb < r; jb += 8) lora_step(jb, false);
-  }
+      for (int i = 0; i < 4; i++) acc[j][i] = f32x16_t{};
+    fence();
+    // DMAs past K (the last tiles' x and weight stages) read the next rows'
+    // data or zeros past the buffers and feed nothing.  (No exit inside the
+    // loop body: a second loop exit made the compiler copy the accumulators.)
+    for (int kt = 0; kt < nk; kt += 2) {
+      tile(kt, 0, f0, f1);
+      tile(kt + 1, 1, f1, f0);
+    }
+    // every wave is past the loop's last LDS reads
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    fence();
+    const int em0 = m0, en0 = n0;
 
-  // store: result e of lane (l32, hh) in product (j, i) is y[m][n], m = row l32
-  // of x block i, n = 8 (e / 4) + 4 hh + e % 4 of W block j.  Each wave puts
-  // its 128 x 128 bf16 block in LDS (rows of 272 bytes), then writes it out
-  // row-contiguously, 16 bytes a lane (whole 128-byte lines); flags & 1: y
-  // 16-byte aligned and n a multiple of 8.
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();                   // every wave is done with the loop's LDS
-  uint8_t* const ys = smem + wave * (128 * 272);
+    // epilogue: y = s_t acc + LoRA, the LoRA as MFMA steps over K' = [t_hi | t_lo]
+    // (t split into two bf16 parts, 8 ranks a step) against [B | B]; s_t is
+    // applied before the first LoRA step, or at the store without LoRA.
+    // flags & 2: r a multiple of 8 and B 16-byte aligned, so a lane's 8 ranks of
+    // B and of t are 16-byte loads.
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(lora_b, has_t ? (uint32_t)N * (uint32_t)r * 2u : 0u);
+    const __amdgpu_buffer_rsrc_t tr = make_rsrc(t, has_t ? (uint32_t)M * (uint32_t)r * 4u : 0u);
+    auto pack8 = [](const uint32_t* h) __attribute__((always_inline)) {
+      return as_bf16x8(u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
+    };
+    auto lora_step = [&](int jb, bool scale_first) __attribute__((always_inline)) {
+      // lane half hh covers K' entries 8 hh .. 8 hh + 7: part hh of ranks jb + e
+      bf16x8_t lb[4], tf[4];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+      for (int j = 0; j < 4; j++) {
+        const int n = en0 + 128 * wn + 32 * j + l32;
+        if (flags & 2) {
+          lb[j] = as_bf16x8(buffer_load16(br, ((uint32_t)n * (uint32_t)r + (uint32_t)jb) * 2u));
+        } else {
+          uint32_t h[8];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        uint32_t o[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const float v = acc_read(acc[j][i][4 * q + e]);
-          o[e] = f32_to_bf16_rne((FMT == FMT_NVFP4 && !has_t) ? v * st : v);
+          for (int e = 0; e < 8; e++) h[e] = (n < N && jb + e < r) ? lora_b[(int64_t)n * r + jb + e] : 0u;
+          lb[j] = pack8(h);
         }
-        *reinterpret_cast<uint2*>(ys + (32 * i + l32) * 272 + (32 * j + 8 * q + 4 * hh) * 2) =
-            make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
       }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);             // the wave reads back only what it wrote
-  const int rr = lane >> 4, cc = lane & 15;
-#pragma unroll 4
-  for (int it = 0; it < 32; it++) {
-    const int row = 4 * it + rr;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ys + row * 272 + cc * 16);
-    const int mr = m0 + 128 * wm + row, n = n0 + 128 * wn + 8 * cc;
-    if (mr >= M) continue;
-    uint16_t* dst = y + (int64_t)mr * N + n;
-    if ((flags & 1) && n + 7 < N) {
-      *reinterpret_cast<u32x4_t*>(dst) = v;
-    } else {
 #pragma unroll
-      for (int e = 0; e < 8; e++)
-        if (n + e < N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+      for (int i = 0; i < 4; i++) {
+        const int mr = em0 + 128 * wm + 32 * i + l32;
+        float tv[8];
+        if (flags & 2) {
+          const uint32_t o = ((uint32_t)mr * (uint32_t)r + (uint32_t)jb) * 4u;
+          const u32x4_t v0 = buffer_load16(tr, o), v1 = buffer_load16(tr, o + 16u);
+#pragma unroll
+          for (int e = 0; e < 4; e++) { tv[e] = __uint_as_float(v0[e]); tv[4 + e] = __uint_as_float(v1[e]); }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; e++) tv[e] = (mr < M && jb + e < r) ? t[(int64_t)mr * r + jb + e] : 0.f;
+        }
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const uint32_t hi = f32_to_bf16_rne(tv[e]);
+          h[e] = hh ? f32_to_bf16_rne(tv[e] - __uint_as_float(hi << 16)) : hi;
+        }
+        tf[i] = pack8(h);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          if (scale_first) {
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[j][i][e] = acc_write(acc_read(acc[j][i][e]) * st);
+          }
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lb[j], tf[i], acc[j][i], 0, 0, 0);
+        }
+    };
+    if (has_t) {
+      lora_step(0, FMT == FMT_NVFP4);
+      for (int jb = 8; jb < r; jb += 8) lora_step(jb, false);
     }
+    // the next tile's first x tiles and weight stages go by DMA into x0, x1,
+    // w0, w1 while this tile's y goes out through the x2 / w2 region
+    const int nlocal = local + nwg;
+    const bool more = nlocal < xcount;
+    if (more) {
+      origin(nlocal, m0, n0);
+      set_bases(m0, n0);
+      dma_x(xbuf(0), 0);
+      dma_x(xbuf(1), W4_BK);
+      dma_w(wbuf(0), 0);
+      dma_w(wbuf(1), W4_SK * W4_BK);
+    }
+    asm volatile("" ::: "memory");                // the stores below stay after these DMAs
+    fence();
+
+    // store: result e of lane (l32, hh) in product (j, i) is y[m][n], m = row l32
+    // of x block i, n = 8 (e / 4) + 4 hh + e % 4 of W block j.  In 4 passes (one
+    // x block i each), every wave stages its 32 x 128 bf16 block in LDS (rows
+    // of 272 bytes), then writes it out row-contiguously, 16 bytes a lane
+    // (whole 128-byte lines), through a buffer descriptor (rows and columns
+    // past y are dropped); flags & 1: y 16-byte aligned and n a multiple of 8,
+    // else 2-byte stores.
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)M * (uint32_t)N * 2u);
+    uint8_t* const ys = smem + W4_X2 + wave * (32 * W4_YROW);
+    const int rr = lane >> 4, cc = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+#pragma unroll
+        for (int qq = 0; qq < 4; qq++) {
+          uint32_t o[4];
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const float v = acc_read(acc[j][i][4 * qq + e]);
+            o[e] = f32_to_bf16_rne((FMT == FMT_NVFP4 && !has_t) ? v * st : v);
+          }
+          *reinterpret_cast<uint2*>(ys + l32 * W4_YROW + (32 * j + 8 * qq + 4 * hh) * 2) =
+              make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0): the wave reads back only what it wrote
+#pragma unroll
+      for (int it = 0; it < 8; it++) {
+        const int row = 4 * it + rr;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ys + row * W4_YROW + cc * 16);
+        const int mr = em0 + 128 * wm + 32 * i + row, n = en0 + 128 * wn + 8 * cc;
+        const bool in = mr < M && n < N;
+        if (flags & 1) {
+          const uint32_t yo = in ? ((uint32_t)mr * (uint32_t)N + (uint32_t)n) * 2u : kBufferOob;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), yr, yo, 0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const uint32_t yo = (mr < M && n + e < N) ? ((uint32_t)mr * (uint32_t)N + (uint32_t)(n + e)) * 2u : kBufferOob;
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[e >> 1] >> (16 * (e & 1))), yr, yo, 0, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);         // this pass's LDS reads done before the next pass writes
+    }
+    if (!more) break;
+    // the next tile's DMA was issued before this tile's 32 vector stores of y
+    // (or 256 element stores), which may stay in flight
+    if (flags & 1) wait_vm_lgkm0<32>();
+    else wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    fence();
+    local = nlocal;
   }
 }
 
 bool gemm_w4_supports(int64_t m, int64_t n, int64_t k, const void* scales) {
   return k % (W4_BK * W4_SK) == 0 && (reinterpret_cast<uintptr_t>(scales) & 15u) == 0 &&
-         m * k * 2 < ((int64_t)1 << 31) && n * (k / 2) < ((int64_t)1 << 31);
+         m * k * 2 < ((int64_t)1 << 31) && n * (k / 2) < ((int64_t)1 << 31) && m * n * 2 < ((int64_t)1 << 32);
 }
 
 template <int FMT>
@@ -395,7 +466,13 @@ static hipError_t launch_w4(const uint16_t* x, int64_t m, int64_t k, const uint8
   // 2 = 16-byte loads of B and t (r a multiple of 8, B 16-byte aligned)
   const int flags = ((n % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15u) == 0) ? 1 : 0) |
                     ((t && r > 0 && r % 8 == 0 && (reinterpret_cast<uintptr_t>(lora_b) & 15u) == 0) ? 2 : 0);
-  hipLaunchKernelGGL((gemm_w4_kernel<FMT>), dim3((unsigned)tiles), dim3(W4_THREADS), W4_LDS, stream, x, (int)m,
+  // one workgroup per CU (the LDS holds one), each looping over its XCD's tiles
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t grid = tiles < cus ? tiles : (cus > 0 ? cus : 1);
+  hipLaunchKernelGGL((gemm_w4_kernel<FMT>), dim3((unsigned)grid), dim3(W4_THREADS), W4_LDS, stream, x, (int)m,
                      (int)k, codes, scales, tensor_scale, (int)n, t, lora_b, r, y, flags);
   return hipGetLastError();
 }

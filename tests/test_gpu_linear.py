@@ -81,6 +81,31 @@ def test_gemm_k256(fp4w, fmt, m, n, k, r):
     _full_case(fp4w, fmt, m, n, k, r, seed=m + 3 * r, wkind="outlier" if fmt == 0 else "student_t")
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_gemm_more_tiles_than_cus(fp4w, fmt):
+    """17 x 17 = 289 tiles of 256 x 256, more than the 256 workgroups of one per
+    CU, so workgroups take several tiles: every output is written (y starts as
+    NaN) and 4096 sampled outputs are within the bound."""
+    m = n = 17 * 256 - 40
+    k, seed = 384, 77
+    say(f"[linear] many tiles fmt={fmt} m={m} n={n} k={k}")
+    w, x, a, b = W.linear_inputs(seed, n, k, m, rank=16, wkind="outlier" if fmt == 0 else "student_t")
+    codes, scales, st = O.quantize(fmt, w)
+    q = qweight_dev(fp4w, fmt, codes, scales, st)
+    y = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    fp4w.linear(bf16_dev(x), q, bf16_dev(a), bf16_dev(b), out=y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all().item()), "an output was not written"
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, m, 4096)
+    cols = rng.integers(0, n, 4096)
+    ys = f64_of_bf16(bits_host(y[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)]))
+    y64 = O.linear_sampled(fmt, x, codes, scales, st, rows, cols, a, b)
+    xn = np.sqrt((f64_of_bf16(x[rows]) ** 2).sum(axis=1))
+    wn = weff_norms(fmt, codes, scales, st, a, b, rows=cols)
+    check_bound(ys, y64, xn, wn, f"many tiles fmt={fmt}")
+
+
 def _sampled_case(fp4w, fmt, m, n, k, samples, seed, what):
     say(f"[linear] {what} fmt={fmt} m={m} n={n} k={k} (sampled)")
     wkind = "outlier" if fmt == 0 else "student_t"

@@ -13,6 +13,7 @@ dequantize, grouped MoE).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-rows]
        python bench.py --roofline-only   (the decode kernel's launches and a plain
                                           copy of known size, for profiler runs)
+       python bench.py --gemm-only       (the prefill GEMM rows only, for profiler runs)
 Progress goes to stderr; stdout is exactly one JSON line.
 """
 import argparse
@@ -43,6 +44,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--skip-rows", action="store_true", help="only the headline step and its roofline")
+    p.add_argument("--gemm-only", action="store_true",
+                   help="only the prefill GEMM rows (both formats), for profiler runs")
     p.add_argument("--roofline-only", action="store_true",
                    help="only the roofline launches of the decode kernel and a copy kernel of known size")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
@@ -133,6 +136,17 @@ def main():
         sync()
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
+
+    if args.gemm_only:
+        rank = W.LORA_RANK
+        n, k = W.QWEN7B_SHAPES["gate_up"]
+        weights = {}
+        for fmt in (0, 1):
+            w, _, a, b = W.linear_inputs(100, n, k, 1, rank=rank, wkind="outlier" if fmt == 0 else "student_t")
+            weights[fmt] = (fp4w.quantize(bf16(w), fmt), bf16(a), bf16(b), n, k)
+        rows = gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights)
+        print(json.dumps({"rows": rows}), flush=True)
+        return
 
     # ---- decode weights: quantize once on the device, then clone for rotation ----------
     rank = W.LORA_RANK
@@ -260,6 +274,28 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
+def gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights):
+    """The prefill GEMM: x 16384 x 3584, W (18944, 3584), LoRA r = 16, both formats
+    (weights[fmt] = (qweight, A, B, n, k)); 10 untimed calls first, as the clock
+    ramps up under this load."""
+    rows = {}
+    mrows = W.PREFILL_M
+    for fmt in (0, 1):
+        q, a, b, n, k = weights[fmt]
+        x = bf16(W.normal_bf16(300, W.TID_X, (mrows, k), 1.0))
+        y = torch.empty((mrows, n), dtype=torch.bfloat16, device=dev)
+        wsg = torch.zeros(fp4w.linear_workspace_bytes(mrows, n, k, rank), dtype=torch.uint8, device=dev)
+        gms, _ = time_loop(lambda i: fp4w.linear(x, q, a, b, out=y, workspace=wsg), 10, 10)
+        fl = linear_flops(mrows, n, k, rank)
+        tf = fl / (gms * 1e-3) / 1e12
+        name = "nvfp4" if fmt == 0 else "mxfp4"
+        rows[f"prefill_gemm_{name}"] = {"m": mrows, "n": n, "k": k, "ms": round(gms, 3), "TFLOP/s": round(tf, 1),
+                                        "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 1), "algorithmic_flop": fl}
+        log(f"[bench] prefill GEMM {name} {gms:.3f} ms, {tf:.1f} TFLOP/s")
+        del x, y, wsg
+    return rows
+
+
 def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_graph, rank):
     rows = {}
     reps = max(20, args.steps // 4)
@@ -284,23 +320,9 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
     rows["decode_linear_with_lora"] = dec
     log("[bench] decode rows done")
 
-    # prefill GEMM: x 16384 x 3584, W (18944, 3584), LoRA r = 16, both formats
-    mrows = W.PREFILL_M
-    for fmt in (0, 1):
-        d = decode[(fmt, "gate_up")]
-        n, k = d["n"], d["k"]
-        x = bf16(W.normal_bf16(300, W.TID_X, (mrows, k), 1.0))
-        y = torch.empty((mrows, n), dtype=torch.bfloat16, device=dev)
-        q, a, b = d["qs"][0]
-        wsg = torch.zeros(fp4w.linear_workspace_bytes(mrows, n, k, rank), dtype=torch.uint8, device=dev)
-        gms, _ = time_loop(lambda i: fp4w.linear(x, q, a, b, out=y, workspace=wsg), 10, 10)
-        fl = linear_flops(mrows, n, k, rank)
-        tf = fl / (gms * 1e-3) / 1e12
-        name = "nvfp4" if fmt == 0 else "mxfp4"
-        rows[f"prefill_gemm_{name}"] = {"m": mrows, "n": n, "k": k, "ms": round(gms, 3), "TFLOP/s": round(tf, 1),
-                                        "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 1), "algorithmic_flop": fl}
-        log(f"[bench] prefill GEMM {name} {gms:.3f} ms, {tf:.1f} TFLOP/s")
-        del x, y, wsg
+    weights = {fmt: (*decode[(fmt, "gate_up")]["qs"][0], decode[(fmt, "gate_up")]["n"], decode[(fmt, "gate_up")]["k"])
+               for fmt in (0, 1)}
+    rows.update(gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights))
     torch.cuda.empty_cache()
 
     # quantize over a 7B-shaped set: 28 layers x {2 x (18944,3584), (3584,18944), 4 x (3584,3584)}

@@ -38,6 +38,12 @@ namespace fp4w {
 constexpr int W4_BM = 256, W4_BN = 256, W4_BK = 64, W4_THREADS = 256;
 constexpr int W4_SK = 2;                               // K tiles per weight stage (128 k)
 constexpr int W4_GM = 4;                               // rows of tiles a group of the tile order spans
+#ifndef W4_WL_NVFP4
+#define W4_WL_NVFP4 1                                  // wave layout per format (see gemm_w4_kernel)
+#endif
+#ifndef W4_WL_MXFP4
+#define W4_WL_MXFP4 0
+#endif
 constexpr int W4_XB = W4_BM * 128;                     // bytes per x buffer (256 rows x 64 bf16)
 constexpr int W4_CB = W4_BN * 64;                      // code bytes per weight stage (256 rows x 128 codes)
 constexpr int W4_WB = W4_CB + W4_BN * 8;               // bytes per weight stage (codes, then 8 scale bytes a row)
@@ -48,7 +54,8 @@ constexpr int W4_X0 = 0, W4_X1 = W4_XB, W4_W0 = 2 * W4_XB, W4_W1 = W4_W0 + W4_WB
 constexpr int W4_X2 = W4_W1 + W4_WB, W4_W2 = W4_X2 + W4_XB;
 constexpr int W4_LDS = W4_W2 + W4_WB;                  // 153600 bytes
 constexpr int W4_YROW = 272;                           // bytes per staged y row (256 + 16 of padding)
-static_assert(4 * 32 * W4_YROW <= W4_XB + W4_WB, "a pass of the y staging fits the last x buffer and stage");
+static_assert(4 * 32 * W4_YROW <= W4_XB + W4_WB && 4 * 64 * 144 <= W4_XB + W4_WB,
+              "a pass of the y staging (either wave layout) fits the last x buffer and stage");
 static_assert(W4_LDS <= 160 * 1024, "LDS of one CU");
 
 // Position of chunk c of LDS row m: c ^ swz(m), swz(m) = (m ^ (m >> 3 & 1)) & 7.
@@ -94,12 +101,17 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uin
 
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
+template <int TJ>
 struct W4Frag {
-  u32x4_t c[4];        // codes of column j: k = 32 hh + 8 s .. + 7 in c[j][s]
-  uint32_t s[4];       // scale byte(s) of column j (NVFP4: two, for k = 32 hh and 32 hh + 16)
+  u32x4_t c[TJ];       // codes of column block j: k = 32 hh + 8 s .. + 7 in c[j][s]
+  uint32_t s[TJ];      // scale byte(s) of column block j (NVFP4: two, for k = 32 hh and 32 hh + 16)
 };
 
-template <int FMT>
+// WL: the 4 waves' layout over the 256 x 256 tile: 0 = 2 x 2 waves of 128 x 128
+// (4 x 4 products each), 1 = 1 x 4 waves of 256 rows x 64 columns (8 x 2
+// products each: a weight column is decoded by one wave instead of two, and
+// each x fragment read by four waves instead of two).
+template <int FMT, int WL>
 __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int N,
@@ -131,7 +143,10 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
   int m0, n0;
   origin(local, m0, n0);
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int TI = WL ? 8 : 4, TJ = WL ? 2 : 4;   // x blocks (32 rows) and W blocks (32 columns) of a wave
+  const int xrow0 = WL ? 0 : 128 * (wave >> 1);      // the wave's first x row and W column in the tile
+  const int wcol0 = WL ? 64 * wave : 128 * (wave & 1);
   const int l32 = lane & 31, hh = lane >> 5;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
@@ -183,9 +198,9 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
     }
   };
 
-  // fragments: x row 128 wm + 32 i + l32, chunk 4 hh + s of an x tile; W row
-  // 128 wn + 32 j + l32, chunk 2 q + hh of a weight stage (its K tile q)
-  const int arow = 128 * wm + l32, wrow = 128 * wn + l32;
+  // fragments: x row xrow0 + 32 i + l32, chunk 4 hh + s of an x tile; W row
+  // wcol0 + 32 j + l32, chunk 2 q + hh of a weight stage (its K tile q)
+  const int arow = xrow0 + l32, wrow = wcol0 + l32;
   int aoff[4];
 #pragma unroll
   for (int s = 0; s < 4; s++) aoff[s] = arow * 128 + 16 * ((4 * hh + s) ^ w4_swz(arow));
@@ -194,18 +209,18 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
   for (int q = 0; q < 2; q++) woff[q] = wrow * 64 + 16 * ((2 * q + hh) ^ w4_swzw(wrow));
   auto read_a = [&](bf16x8_t* a, const uint8_t* buf, int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) a[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(buf + aoff[s] + 32 * i * 128));
+    for (int i = 0; i < TI; i++) a[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(buf + aoff[s] + 32 * i * 128));
   };
-  auto read_w = [&](W4Frag& f, const uint8_t* wbuf, int q) __attribute__((always_inline)) {
+  auto read_w = [&](W4Frag<TJ>& f, const uint8_t* wbuf, int q) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int j = 0; j < TJ; j++) {
       f.c[j] = *reinterpret_cast<const u32x4_t*>(wbuf + woff[q] + 32 * j * 64);
       if (FMT == FMT_NVFP4) f.s[j] = *reinterpret_cast<const uint16_t*>(wbuf + W4_CB + (wrow + 32 * j) * 8 + 4 * q + 2 * hh);
       else f.s[j] = wbuf[W4_CB + (wrow + 32 * j) * 4 + 2 * q + hh];
     }
   };
   // column j's fragment for step s: 8 exact bf16 values
-  auto wfrag = [&](const W4Frag& f, int j, int s) __attribute__((always_inline)) -> bf16x8_t {
+  auto wfrag = [&](const W4Frag<TJ>& f, int j, int s) __attribute__((always_inline)) -> bf16x8_t {
     const uint32_t dw = f.c[j][s];
     u32x4_t o;
     if (FMT == FMT_MXFP4) {
@@ -225,14 +240,14 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
     return as_bf16x8(o);
   };
 
-  f32x16_t acc[4][4];                             // [j: 32 columns of W][i: 32 rows of x]
+  f32x16_t acc[TJ][TI];                           // [j: 32 columns of W][i: 32 rows of x]
   // 16 MFMAs of step s (x fragments a), the W fragments decoded on the way
-  auto mfma_step = [&](const bf16x8_t* a, const W4Frag& f, int s) __attribute__((always_inline)) {
+  auto mfma_step = [&](const bf16x8_t* a, const W4Frag<TJ>& f, int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int j = 0; j < TJ; j++) {
       const bf16x8_t b = wfrag(f, j, s);
 #pragma unroll
-      for (int i = 0; i < 4; i++) acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a[i], acc[j][i], 0, 0, 0);
+      for (int i = 0; i < TI; i++) acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a[i], acc[j][i], 0, 0, 0);
     }
   };
   auto fence = [&]() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
@@ -244,8 +259,8 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
   };
 
   const int nk = K / W4_BK;
-  bf16x8_t a0[4], a1[4], a2[4], a3[4];
-  W4Frag f0, f1;
+  bf16x8_t a0[TI], a1[TI], a2[TI], a3[TI];
+  W4Frag<TJ> f0, f1;
   // K tile kt = 2 S + q (x buffer kt % 3, weight stage S % 3).  On entry a0 and
   // f hold its step-0 x fragments and its W fragments (reads issued).  Step 0
   // reads the next tile's W fragments into fn.  The DMA of x tile kt + 2 (into
@@ -256,7 +271,7 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
   // DMA of x tile kt + 1 (and so of weight stage S + 1): the loads issued after
   // it, 8 of x and 4 + NSC of W, may stay in flight.  The barrier comes before
   // step 3, whose MFMAs cover the reads of the next tile's step-0 x fragments.
-  auto tile = [&](int kt, int q, W4Frag& f, W4Frag& fn) __attribute__((always_inline)) {
+  auto tile = [&](int kt, int q, W4Frag<TJ>& f, W4Frag<TJ>& fn) __attribute__((always_inline)) {
     const int S = kt >> 1;
     const uint8_t* cur = xbuf(kt % 3);
     read_a(a1, cur, 1);
@@ -295,9 +310,9 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
     read_a(a0, xbuf(0), 0);
     read_w(f0, wbuf(0), 0);
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < TJ; j++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) acc[j][i] = f32x16_t{};
+      for (int i = 0; i < TI; i++) acc[j][i] = f32x16_t{};
     fence();
     // DMAs past K (the last tiles' x and weight stages) read the next rows'
     // data or zeros past the buffers and feed nothing.  (No exit inside the
@@ -324,10 +339,10 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
     };
     auto lora_step = [&](int jb, bool scale_first) __attribute__((always_inline)) {
       // lane half hh covers K' entries 8 hh .. 8 hh + 7: part hh of ranks jb + e
-      bf16x8_t lb[4], tf[4];
+      bf16x8_t lb[TJ], tf[TI];
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int n = en0 + 128 * wn + 32 * j + l32;
+      for (int j = 0; j < TJ; j++) {
+        const int n = en0 + wcol0 + 32 * j + l32;
         if (flags & 2) {
           lb[j] = as_bf16x8(buffer_load16(br, ((uint32_t)n * (uint32_t)r + (uint32_t)jb) * 2u));
         } else {
@@ -338,8 +353,8 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int mr = em0 + 128 * wm + 32 * i + l32;
+      for (int i = 0; i < TI; i++) {
+        const int mr = em0 + xrow0 + 32 * i + l32;
         float tv[8];
         if (flags & 2) {
           const uint32_t o = ((uint32_t)mr * (uint32_t)r + (uint32_t)jb) * 4u;
@@ -359,9 +374,9 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
         tf[i] = pack8(h);
       }
 #pragma unroll
-      for (int j = 0; j < 4; j++)
+      for (int j = 0; j < TJ; j++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < TI; i++) {
           if (scale_first) {
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[j][i][e] = acc_write(acc_read(acc[j][i][e]) * st);
@@ -389,37 +404,42 @@ __global__ __launch_bounds__(W4_THREADS, 1) void gemm_w4_kernel(
     fence();
 
     // store: result e of lane (l32, hh) in product (j, i) is y[m][n], m = row l32
-    // of x block i, n = 8 (e / 4) + 4 hh + e % 4 of W block j.  In 4 passes (one
-    // x block i each), every wave stages its 32 x 128 bf16 block in LDS (rows
-    // of 272 bytes), then writes it out row-contiguously, 16 bytes a lane
-    // (whole 128-byte lines), through a buffer descriptor (rows and columns
-    // past y are dropped); flags & 1: y 16-byte aligned and n a multiple of 8,
-    // else 2-byte stores.
+    // of x block i, n = 8 (e / 4) + 4 hh + e % 4 of W block j.  In 4 passes (TI / 4
+    // x blocks each), every wave stages its RP x 32 TJ bf16 block in LDS (rows of
+    // 64 TJ + 16 bytes), then writes it out row-contiguously, 16 bytes a lane
+    // (whole 128-byte lines), through a buffer descriptor (rows and columns past
+    // y are dropped): 8 stores a pass.  flags & 1: y 16-byte aligned and n a
+    // multiple of 8, else 2-byte stores.
+    constexpr int IB = TI / 4, RP = 32 * IB, YR = 64 * TJ + 16, LPR = 4 * TJ;   // blocks, rows a pass; row bytes; lanes a row
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)M * (uint32_t)N * 2u);
-    uint8_t* const ys = smem + W4_X2 + wave * (32 * W4_YROW);
-    const int rr = lane >> 4, cc = lane & 15;
+    uint8_t* const ys = smem + W4_X2 + wave * (RP * YR);
+    const int rr = lane / LPR, cc = lane % LPR;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int pass = 0; pass < 4; pass++) {
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
+      for (int ii = 0; ii < IB; ii++) {
+        const int i = pass * IB + ii;
 #pragma unroll
-        for (int qq = 0; qq < 4; qq++) {
-          uint32_t o[4];
+        for (int j = 0; j < TJ; j++) {
 #pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const float v = acc_read(acc[j][i][4 * qq + e]);
-            o[e] = f32_to_bf16_rne((FMT == FMT_NVFP4 && !has_t) ? v * st : v);
+          for (int qq = 0; qq < 4; qq++) {
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              const float v = acc_read(acc[j][i][4 * qq + e]);
+              o[e] = f32_to_bf16_rne((FMT == FMT_NVFP4 && !has_t) ? v * st : v);
+            }
+            *reinterpret_cast<uint2*>(ys + (32 * ii + l32) * YR + (32 * j + 8 * qq + 4 * hh) * 2) =
+                make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
           }
-          *reinterpret_cast<uint2*>(ys + l32 * W4_YROW + (32 * j + 8 * qq + 4 * hh) * 2) =
-              make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0): the wave reads back only what it wrote
 #pragma unroll
       for (int it = 0; it < 8; it++) {
-        const int row = 4 * it + rr;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ys + row * W4_YROW + cc * 16);
-        const int mr = em0 + 128 * wm + 32 * i + row, n = en0 + 128 * wn + 8 * cc;
+        const int row = it * (64 / LPR) + rr;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ys + row * YR + cc * 16);
+        const int mr = em0 + xrow0 + RP * pass + row, n = en0 + wcol0 + 8 * cc;
         const bool in = mr < M && n < N;
         if (flags & 1) {
           const uint32_t yo = in ? ((uint32_t)mr * (uint32_t)N + (uint32_t)n) * 2u : kBufferOob;
@@ -450,14 +470,14 @@ bool gemm_w4_supports(int64_t m, int64_t n, int64_t k, const void* scales) {
          m * k * 2 < ((int64_t)1 << 31) && n * (k / 2) < ((int64_t)1 << 31) && m * n * 2 < ((int64_t)1 << 32);
 }
 
-template <int FMT>
+template <int FMT, int WL>
 static hipError_t launch_w4(const uint16_t* x, int64_t m, int64_t k, const uint8_t* codes, const uint8_t* scales,
                             const float* tensor_scale, int64_t n, const float* t, const uint16_t* lora_b, int r,
                             uint16_t* y, hipStream_t stream) {
   const int64_t tiles = ((m + W4_BM - 1) / W4_BM) * ((n + W4_BN - 1) / W4_BN);
   static bool lds_set = false;
   if (!lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_w4_kernel<FMT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_w4_kernel<FMT, WL>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, W4_LDS);
     if (e != hipSuccess) return e;
     lds_set = true;
@@ -472,7 +492,7 @@ static hipError_t launch_w4(const uint16_t* x, int64_t m, int64_t k, const uint8
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const int64_t grid = tiles < cus ? tiles : (cus > 0 ? cus : 1);
-  hipLaunchKernelGGL((gemm_w4_kernel<FMT>), dim3((unsigned)grid), dim3(W4_THREADS), W4_LDS, stream, x, (int)m,
+  hipLaunchKernelGGL((gemm_w4_kernel<FMT, WL>), dim3((unsigned)grid), dim3(W4_THREADS), W4_LDS, stream, x, (int)m,
                      (int)k, codes, scales, tensor_scale, (int)n, t, lora_b, r, y, flags);
   return hipGetLastError();
 }
@@ -483,8 +503,8 @@ hipError_t launch_gemm_w4(int fmt, const void* x, int64_t m, int64_t k, const ui
   const uint16_t* xx = reinterpret_cast<const uint16_t*>(x);
   const uint16_t* bb = reinterpret_cast<const uint16_t*>(lora_b);
   uint16_t* yy = reinterpret_cast<uint16_t*>(y);
-  return fmt == FMT_NVFP4 ? launch_w4<FMT_NVFP4>(xx, m, k, codes, scales, tensor_scale, n, t, bb, r, yy, stream)
-                          : launch_w4<FMT_MXFP4>(xx, m, k, codes, scales, tensor_scale, n, t, bb, r, yy, stream);
+  return fmt == FMT_NVFP4 ? launch_w4<FMT_NVFP4, W4_WL_NVFP4>(xx, m, k, codes, scales, tensor_scale, n, t, bb, r, yy, stream)
+                          : launch_w4<FMT_MXFP4, W4_WL_MXFP4>(xx, m, k, codes, scales, tensor_scale, n, t, bb, r, yy, stream);
 }
 
 }  // namespace fp4w

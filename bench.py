@@ -358,6 +358,26 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
         nbd = sum(o.n * o.k * 2 + o.n * o.k // 2 + o.n * o.k // (16 if fmt == 0 else 32) for o in outs)
         rows[f"dequantize_7b_set_{'nvfp4' if fmt == 0 else 'mxfp4'}"] = {
             "ms": round(ms_d, 3), "GB/s": round(nbd / (ms_d * 1e-3) / 1e9, 1), "algorithmic_bytes": nbd}
+        # fused fake-quant (dequantize(quantize(W)) in one pass) over the same set: reads 2 B/w,
+        # writes 2 B/w and the block scales
+        fq = [torch.empty((o.n, o.k), dtype=torch.bfloat16, device=dev) for o in outs[:7]]
+        fq_s = [torch.empty_like(o.scales) for o in outs[:7]]
+        fq_t = torch.empty(1, dtype=torch.float32, device=dev)
+
+        def fpass(i):
+            for j, t in enumerate(tensors):
+                y = fq[j % 7]
+                ts = fq_t if fmt == 0 else None
+                fp4w._check(fp4w._fake_quant(fmt, fp4w._ptr(t), t.shape[0], t.shape[1], fp4w._ptr(y),
+                                             fp4w._ptr(fq_s[j % 7]), fp4w._ptr(ts), 0, fp4w._stream(dev)),
+                            "fp4w_fake_quant")
+        ms_f, _ = time_loop(fpass, 3, 1)
+        nbf = sum(t.numel() * 4 + t.numel() // (16 if fmt == 0 else 32) for t in tensors)
+        rows[f"fake_quant_7b_set_{'nvfp4' if fmt == 0 else 'mxfp4'}"] = {
+            "ms": round(ms_f, 3), "GB/s": round(nbf / (ms_f * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbf / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 1), "algorithmic_bytes": nbf}
+        log(f"[bench] fake-quant fmt={fmt}: {ms_f:.2f} ms, {nbf / (ms_f * 1e-3) / 1e9:.1f} GB/s")
+        del fq, fq_s
         if fmt == 0:
             # scale-only merge of the (18944, 3584) weight, in place; ratio to re-quantizing it
             o = outs[0]

@@ -60,7 +60,7 @@ extern "C" {
 #define FP4W_ERR_WORKSPACE (-6)  /* workspace missing or smaller than required       */
 
 /* flags */
-#define FP4W_FROZEN_SCALES 0x1u  /* fp4w_quantize: scales (and tensor scale) are inputs */
+#define FP4W_FROZEN_SCALES 0x1u  /* fp4w_quantize, fp4w_fake_quant: scales (and tensor scale) are inputs */
 #define FP4W_OUT_FP32      0x2u  /* fp4w_dequantize: write fp32 instead of bf16         */
 
 /* Largest LoRA rank the fused linear accepts. */
@@ -101,6 +101,25 @@ int fp4w_quantize(int fmt, const void *w_bf16, int64_t n, int64_t k,
 int fp4w_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
                     const float *tensor_scale, int64_t n, int64_t k,
                     void *out, uint32_t flags, void *stream);
+
+/*
+ * fp4w_fake_quant -- fused fake-quant forward of a bf16 tensor W (n, k): in one
+ * pass per block, the codes fp4w_quantize computes, decoded as fp4w_dequantize
+ * decodes them (bf16), written to out_bf16 (n, k); the codes themselves are not
+ * stored.  Bit for bit, out = dequantize(quantize(W)).  The quantize-then-
+ * dequantize a training forward inserts so that it sees the engine's values
+ * (QATFactory page, section on how training repeats the engine's arithmetic);
+ * its backward is the plain straight-through estimator (the gradient passes
+ * unchanged; page on QAT at low bit widths), which needs no kernel.
+ * scales (n, k/16 or k/32) and, for NVFP4, *tensor_scale are written as
+ * fp4w_quantize writes them (the tensor scale word is the amax scratch during
+ * the call), or read with FP4W_FROZEN_SCALES (frozen-scale training).  Also
+ * fits activations (rows of x) for W4A4 training.  w_bf16 and out_bf16 must be
+ * 16-byte aligned and must not overlap.
+ */
+int fp4w_fake_quant(int fmt, const void *w_bf16, int64_t n, int64_t k,
+                    void *out_bf16, uint8_t *scales, float *tensor_scale,
+                    uint32_t flags, void *stream);
 
 /*
  * Workspace for fp4w_linear, in bytes, for x (m, k), W (n, k) and LoRA rank r

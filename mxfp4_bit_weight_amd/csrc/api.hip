@@ -32,7 +32,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP4W_OK : FP4W_ERR_HIP; 
 
 extern "C" {
 
-int fp4w_version(void) { return 3; }
+int fp4w_version(void) { return 4; }
 
 const char* fp4w_status_string(int status) {
   switch (status) {
@@ -59,6 +59,20 @@ int fp4w_quantize(int fmt, const void* w_bf16, int64_t n, int64_t k, uint8_t* co
   if (fmt == FP4W_NVFP4 && ((reinterpret_cast<uintptr_t>(tensor_scale) & 3u) != 0)) return FP4W_ERR_ALIGN;
   return hip_status(fp4w::launch_quantize(fmt, w_bf16, n, k, codes, scales, tensor_scale,
                                           (flags & FP4W_FROZEN_SCALES) != 0, as_stream(stream)));
+}
+
+int fp4w_fake_quant(int fmt, const void* w_bf16, int64_t n, int64_t k, void* out_bf16, uint8_t* scales,
+                    float* tensor_scale, uint32_t flags, void* stream) {
+  if (!valid_fmt(fmt) || (flags & ~FP4W_FROZEN_SCALES)) return FP4W_ERR_FORMAT;
+  int st = check_nk(n, k);
+  if (st) return st;
+  if (n * k == 0) return FP4W_OK;
+  if (!w_bf16 || !out_bf16 || !scales) return FP4W_ERR_ARG;
+  if (fmt == FP4W_NVFP4 && !tensor_scale) return FP4W_ERR_ARG;
+  if (!aligned16(w_bf16) || !aligned16(out_bf16)) return FP4W_ERR_ALIGN;
+  if (fmt == FP4W_NVFP4 && ((reinterpret_cast<uintptr_t>(tensor_scale) & 3u) != 0)) return FP4W_ERR_ALIGN;
+  return hip_status(fp4w::launch_fake_quant(fmt, w_bf16, n, k, out_bf16, scales, tensor_scale,
+                                            (flags & FP4W_FROZEN_SCALES) != 0, as_stream(stream)));
 }
 
 int fp4w_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t n,

@@ -9,6 +9,8 @@ namespace fp4w {
 
 hipError_t launch_quantize(int fmt, const void* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
                            float* tensor_scale, bool frozen, hipStream_t stream);
+hipError_t launch_fake_quant(int fmt, const void* w, int64_t n, int64_t k, void* out, uint8_t* scales,
+                             float* tensor_scale, bool frozen, hipStream_t stream);
 
 hipError_t launch_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                              int64_t n, int64_t k, void* out, bool out_fp32, hipStream_t stream);

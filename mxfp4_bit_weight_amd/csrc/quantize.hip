@@ -9,6 +9,10 @@
 //   4. finalize: overwrite the word with s_t (1 thread)
 // MXFP4: one pass, one thread per 32-element block.
 // Frozen scales (same page, frozen-scale QAD): only the codes are recomputed.
+// Fused fake-quant (launch_fake_quant): the same passes, the encode writing the
+// values decoded from its codes (bf16, as dequantize rounds them) instead of the
+// codes -- the quantize-dequantize a training forward inserts (QATFactory page,
+// section on how training repeats the engine's arithmetic).
 //
 // Exactness of the NVFP4 element codes: q = |w| / (dec(sb) s_t) is evaluated in
 // binary32 with a relative error below 4 * 2^-24; the code is converted from the
@@ -16,6 +20,7 @@
 // so when both ends give the same code it is the code of the exact quotient.
 // Otherwise (a midpoint lies inside the bracket, about 3e-6 of elements) the
 // lane recomputes its codes with exact fma sign tests.
+#include "codec.hpp"
 #include "fp4w_device.hpp"
 #include "fp4w_internal.hpp"
 
@@ -124,14 +129,17 @@ __device__ __forceinline__ uint32_t sign_codes(const uint32_t* wd) {
   return out;
 }
 
-template <bool FROZEN>
+// FQ: fused fake-quant -- instead of the codes, write the block's 16 values
+// decoded from them as dequantize does (codec.hpp), 32 bytes of bf16 (fq).
+template <bool FROZEN, bool FQ = false>
 __global__ __launch_bounds__(256) void nvfp4_encode_kernel(const uint4* __restrict__ w, int64_t nblocks,
                                                            const uint32_t* __restrict__ ts_word,
                                                            uint8_t* __restrict__ scales,
-                                                           uint2* __restrict__ codes) {
+                                                           uint2* __restrict__ codes, uint4* __restrict__ fq = nullptr) {
   const uint32_t tw = *ts_word;
   const float st = FROZEN ? __uint_as_float(tw) : tensor_scale_from_amax_word(tw);
   const bool st_fast = st >= 0x1p-64f && st <= 0x1p120f;
+  const bool tiny = !(st >= 0x1p-90f);
   for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += (int64_t)gridDim.x * 256) {
     uint4 v0 = w[2 * b];
     uint4 v1 = w[2 * b + 1];
@@ -171,7 +179,22 @@ __global__ __launch_bounds__(256) void nvfp4_encode_kernel(const uint4* __restri
         out.y = nvfp4_codes_exact(wd[4], wd[5], wd[6], wd[7], d, st);
       }
     }
-    codes[b] = out;
+    if (!FQ) {
+      codes[b] = out;
+    } else {
+      const uint32_t cw[2] = {out.x, out.y};
+      uint32_t o[8];
+      float f0, f1;
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        nvfp4_pair(fp4x2_to_f32x2<0>(cw[j], 1.0f), d, st, tiny, f0, f1, o[4 * j + 0], true);
+        nvfp4_pair(fp4x2_to_f32x2<1>(cw[j], 1.0f), d, st, tiny, f0, f1, o[4 * j + 1], true);
+        nvfp4_pair(fp4x2_to_f32x2<2>(cw[j], 1.0f), d, st, tiny, f0, f1, o[4 * j + 2], true);
+        nvfp4_pair(fp4x2_to_f32x2<3>(cw[j], 1.0f), d, st, tiny, f0, f1, o[4 * j + 3], true);
+      }
+      fq[2 * b] = make_uint4(o[0], o[1], o[2], o[3]);
+      fq[2 * b + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
   }
 }
 
@@ -181,10 +204,10 @@ __global__ __launch_bounds__(256) void nvfp4_encode_kernel(const uint4* __restri
 // a block holding inf/NaN (E = 255) gets the NaN scale 0xFF.  The codes come from
 // the scaled conversion, which divides by the power of two exactly and rounds to
 // nearest even with saturation.
-template <bool FROZEN>
+template <bool FROZEN, bool FQ = false>
 __global__ __launch_bounds__(256) void mxfp4_encode_kernel(const uint4* __restrict__ w, int64_t nblocks,
                                                            uint8_t* __restrict__ scales,
-                                                           uint4* __restrict__ codes) {
+                                                           uint4* __restrict__ codes, uint4* __restrict__ fq = nullptr) {
   for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += (int64_t)gridDim.x * 256) {
     uint32_t wd[16];
 #pragma unroll
@@ -217,7 +240,32 @@ __global__ __launch_bounds__(256) void mxfp4_encode_kernel(const uint4* __restri
       c[q] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c[q], as_bf16x2(wd[4 * q + 2]), s, 2);
       c[q] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c[q], as_bf16x2(wd[4 * q + 3]), s, 3);
     }
-    codes[b] = make_uint4(c[0], c[1], c[2], c[3]);
+    if (!FQ) {
+      codes[b] = make_uint4(c[0], c[1], c[2], c[3]);
+    } else {
+      // the 32 values decoded from the codes as dequantize does (codec.hpp)
+      uint32_t o[16];
+      if (sc < 0xFDu) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          o[4 * j + 0] = fp4x2_to_bf16x2_scaled<0>(c[j], s);
+          o[4 * j + 1] = fp4x2_to_bf16x2_scaled<1>(c[j], s);
+          o[4 * j + 2] = fp4x2_to_bf16x2_scaled<2>(c[j], s);
+          o[4 * j + 3] = fp4x2_to_bf16x2_scaled<3>(c[j], s);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          float v[8];
+          mx_plain8(c[j], sc, v);
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            o[4 * j + e] = f32_to_bf16_rne(v[2 * e]) | (f32_to_bf16_rne(v[2 * e + 1]) << 16);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; q++) fq[4 * b + q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    }
   }
 }
 
@@ -257,6 +305,38 @@ hipError_t launch_quantize(int fmt, const void* w, int64_t n, int64_t k, uint8_t
     else
       hipLaunchKernelGGL(mxfp4_encode_kernel<true>, dim3(grid_for(nblocks, 256, 16384)), dim3(256), 0, stream,
                          reinterpret_cast<const uint4*>(w), nblocks, scales, reinterpret_cast<uint4*>(codes));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fake_quant(int fmt, const void* w, int64_t n, int64_t k, void* out, uint8_t* scales,
+                             float* tensor_scale, bool frozen, hipStream_t stream) {
+  const int64_t count = n * k;
+  if (count == 0) return hipSuccess;
+  const uint4* wv = reinterpret_cast<const uint4*>(w);
+  uint4* fq = reinterpret_cast<uint4*>(out);
+  if (fmt == FMT_NVFP4) {
+    const int64_t nblocks = count / 16;
+    uint32_t* word = reinterpret_cast<uint32_t*>(tensor_scale);
+    if (!frozen) {
+      hipLaunchKernelGGL(nvfp4_amax_zero_kernel, dim3(1), dim3(1), 0, stream, word);
+      hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(grid_for(count / 8, AMAX_THREADS * AMAX_UNROLL, 1024)),
+                         dim3(AMAX_THREADS), 0, stream, wv, count / 8, word);
+      hipLaunchKernelGGL((nvfp4_encode_kernel<false, true>), dim3(grid_for(nblocks, 256, 16384)), dim3(256), 0,
+                         stream, wv, nblocks, word, scales, nullptr, fq);
+      hipLaunchKernelGGL(nvfp4_finalize_kernel, dim3(1), dim3(1), 0, stream, word);
+    } else {
+      hipLaunchKernelGGL((nvfp4_encode_kernel<true, true>), dim3(grid_for(nblocks, 256, 16384)), dim3(256), 0,
+                         stream, wv, nblocks, word, scales, nullptr, fq);
+    }
+  } else {
+    const int64_t nblocks = count / 32;
+    if (!frozen)
+      hipLaunchKernelGGL((mxfp4_encode_kernel<false, true>), dim3(grid_for(nblocks, 256, 16384)), dim3(256), 0,
+                         stream, wv, nblocks, scales, nullptr, fq);
+    else
+      hipLaunchKernelGGL((mxfp4_encode_kernel<true, true>), dim3(grid_for(nblocks, 256, 16384)), dim3(256), 0,
+                         stream, wv, nblocks, scales, nullptr, fq);
   }
   return hipGetLastError();
 }

@@ -42,6 +42,7 @@ def _sig(name, restype, *args):
 
 _quantize = _sig("fp4w_quantize", _int, _int, _p, _i64, _i64, _p, _p, _p, _u32, _p)
 _dequantize = _sig("fp4w_dequantize", _int, _int, _p, _p, _p, _i64, _i64, _p, _u32, _p)
+_fake_quant = _sig("fp4w_fake_quant", _int, _int, _p, _i64, _i64, _p, _p, _p, _u32, _p)
 _ws_bytes = _sig("fp4w_linear_workspace_bytes", _sz, _i64, _i64, _i64, _int)
 _linear = _sig("fp4w_linear", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _int, _p, _p, _sz, _p)
 _grouped = _sig("fp4w_grouped_linear", _int, _int, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p)
@@ -52,7 +53,7 @@ _debug_lora_wait = _sig("fp4w_debug_lora_wait", _i64, _i64)
 
 EXPORTED = ["fp4w_quantize", "fp4w_dequantize", "fp4w_linear_workspace_bytes", "fp4w_linear",
             "fp4w_grouped_linear", "fp4w_merge_scales", "fp4w_status_string", "fp4w_version",
-            "fp4w_debug_lora_wait"]
+            "fp4w_debug_lora_wait", "fp4w_fake_quant"]
 
 
 class Fp4wError(RuntimeError):
@@ -126,6 +127,41 @@ def quantize(w: torch.Tensor, fmt: int = NVFP4, out: Optional[QWeight] = None,
     _check(_quantize(fmt, _ptr(w), n, k, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), flags,
                      _stream(w.device)), "fp4w_quantize")
     return q
+
+
+def fake_quant(w: torch.Tensor, fmt: int = NVFP4, frozen: Optional[QWeight] = None,
+               out: Optional[torch.Tensor] = None):
+    """fp4w_fake_quant: dequantize(quantize(w)) in one pass, as bf16 (n, k).
+    Returns (w_fq, scales, tensor_scale); ``frozen`` supplies the scales (and
+    NVFP4 tensor scale) instead of computing them."""
+    _need(w, torch.bfloat16, "w")
+    n, k = w.shape
+    y = out if out is not None else torch.empty((n, k), dtype=torch.bfloat16, device=w.device)
+    _need(y, torch.bfloat16, "out")
+    flags = 0
+    if frozen is not None:
+        flags = FROZEN_SCALES
+        scales, ts = frozen.scales, frozen.tensor_scale
+    else:
+        scales = torch.empty((n, k // BLOCK[fmt]), dtype=torch.uint8, device=w.device)
+        ts = torch.empty(1, dtype=torch.float32, device=w.device) if fmt == NVFP4 else None
+    _check(_fake_quant(fmt, _ptr(w), n, k, _ptr(y), _ptr(scales), _ptr(ts), flags, _stream(w.device)),
+           "fp4w_fake_quant")
+    return y, scales, ts
+
+
+class FakeQuantSTE(torch.autograd.Function):
+    """Training forward through fp4w_fake_quant; backward: the plain
+    straight-through estimator (the gradient passes unchanged)."""
+
+    @staticmethod
+    def forward(ctx, w, fmt=NVFP4):
+        y, _, _ = fake_quant(w.detach(), fmt)
+        return y
+
+    @staticmethod
+    def backward(ctx, grad):
+        return grad, None
 
 
 def dequantize(q: QWeight, dtype=torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:

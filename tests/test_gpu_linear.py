@@ -63,7 +63,7 @@ def test_skinny_ragged(fp4w, fmt, m, n, k, r):
 
 
 GEMM = [(17, 300, 256, 16), (100, 520, 1056, 16), (300, 257, 544, 0), (64, 64, 64, 5), (513, 700, 2048, 64)]
-# K a multiple of 256 (the GEMM that decodes W in registers): ragged rows and
+# K a multiple of 128 (the GEMM that decodes W in registers): ragged rows and
 # columns over several 256 x 256 tiles, n not a multiple of 4 (element stores),
 # the shortest K (one weight stage), LoRA ranks not a multiple of 8
 GEMM_W4 = [(257, 301, 256, 5), (600, 520, 1280, 17), (33, 1030, 512, 1), (300, 257, 768, 0), (40, 64, 256, 64)]

@@ -172,6 +172,27 @@ int fp4w_linear(int fmt, const void *x_bf16, int64_t m, int64_t k,
                 void *y_bf16, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fp4w_linear_w4a4 -- y (m, n) bf16 = deq(x) deq(W)^T with x and W both MXFP4
+ * (W4A4: 4-bit weights and activations, the mode MXFP4 deploys best in when
+ * training quantized both; QATFactory page, section on the strategies NVFP4 and
+ * MXFP4 need), on gfx950's block-scaled matrix core: the E2M1 codes and E8M0
+ * scales go to the instruction as stored, every product is exact and the sum is
+ * accumulated in fp32, rounded once to bf16.
+ *   fmt        FP4W_MXFP4 (NVFP4's E4M3 block scales have no native scaled
+ *              product: FP4W_ERR_FORMAT)
+ *   x_codes    (m, k/2), x_scales (m, k/32): x as fp4w_quantize writes it
+ *   codes      (n, k/2), scales   (n, k/32): W as fp4w_quantize writes it
+ *   y_bf16     (m, n) bf16
+ * k must be a positive multiple of 128 and m * n * 2 below 2^32, each code
+ * plane (plus 512 rows) below 2 GiB: else FP4W_ERR_SHAPE.  Codes 16-byte,
+ * scales 4-byte, y 2-byte aligned (FP4W_ERR_ALIGN).  A NaN block scale (0xFF)
+ * makes the products of its block NaN.  One launch on `stream`; no workspace.
+ */
+int fp4w_linear_w4a4(int fmt, const uint8_t *x_codes, const uint8_t *x_scales,
+                     int64_t m, int64_t k, const uint8_t *codes, const uint8_t *scales,
+                     int64_t n, void *y_bf16, void *stream);
+
+/*
  * fp4w_grouped_linear -- the W4A16 linear over the experts of a mixture of
  * experts (QATFactory page: dense and MoE models; Nemotron page: 30B-A3B base).
  * For every expert e and every row q in [expert_offsets[e], expert_offsets[e+1]):

@@ -32,7 +32,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP4W_OK : FP4W_ERR_HIP; 
 
 extern "C" {
 
-int fp4w_version(void) { return 4; }
+int fp4w_version(void) { return 5; }
 
 const char* fp4w_status_string(int status) {
   switch (status) {
@@ -120,6 +120,19 @@ int fp4w_linear(int fmt, const void* x_bf16, int64_t m, int64_t k, const uint8_t
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP4W_ERR_ALIGN;
   return hip_status(fp4w::launch_linear(fmt, x_bf16, m, k, codes, scales, tensor_scale, n, lora ? lora_a : nullptr,
                                         lora ? lora_b : nullptr, rr, y_bf16, workspace, plan, as_stream(stream)));
+}
+
+int fp4w_linear_w4a4(int fmt, const uint8_t* x_codes, const uint8_t* x_scales, int64_t m, int64_t k,
+                     const uint8_t* codes, const uint8_t* scales, int64_t n, void* y_bf16, void* stream) {
+  if (fmt != FP4W_MXFP4) return FP4W_ERR_FORMAT;
+  if (m < 0 || n < 0 || k < 0) return FP4W_ERR_ARG;
+  if (m == 0 || n == 0) return FP4W_OK;
+  if (k == 0 || !fp4w::gemm_a4w4_supports(m, n, k)) return FP4W_ERR_SHAPE;
+  if (!x_codes || !x_scales || !codes || !scales || !y_bf16) return FP4W_ERR_ARG;
+  if (!aligned16(x_codes) || !aligned16(codes) || !aligned2(y_bf16)) return FP4W_ERR_ALIGN;
+  if (((reinterpret_cast<uintptr_t>(x_scales) | reinterpret_cast<uintptr_t>(scales)) & 3u) != 0)
+    return FP4W_ERR_ALIGN;
+  return hip_status(fp4w::launch_gemm_a4w4(x_codes, x_scales, m, k, codes, scales, n, y_bf16, as_stream(stream)));
 }
 
 int fp4w_grouped_linear(int fmt, const void* x_bf16, int64_t num_tokens, const int32_t* row_index,

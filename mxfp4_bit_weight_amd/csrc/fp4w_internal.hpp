@@ -107,6 +107,12 @@ hipError_t launch_gemm_w4(int fmt, const void* x, int64_t m, int64_t k, const ui
                           const float* tensor_scale, int64_t n, const float* t, const void* lora_b, int r, void* y,
                           hipStream_t stream);
 
+// The W4A4 MXFP4 GEMM on the block-scaled matrix core (a4w4.hip): K a multiple
+// of 128, each operand's codes and y within the buffer-offset range.
+bool gemm_a4w4_supports(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_a4w4(const uint8_t* xc, const uint8_t* xs, int64_t m, int64_t k, const uint8_t* wc,
+                            const uint8_t* ws, int64_t n, void* y, hipStream_t stream);
+
 // Grouped linear on the x-in-registers kernel (decode_xs.hip): K in one span.
 bool grouped_xs_supports(int64_t num_tokens, int64_t n, int64_t k);
 hipError_t launch_grouped_xs(int fmt, const void* x, int64_t num_tokens, const int32_t* row_index,

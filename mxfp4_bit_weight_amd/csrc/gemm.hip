@@ -32,6 +32,7 @@
 // 4 GiB, K must be a multiple of 128 and the scales 16-byte aligned.
 #include "fp4w_device.hpp"
 #include "fp4w_internal.hpp"
+#include "gemm_common.hpp"
 
 namespace fp4w {
 
@@ -58,48 +59,6 @@ static_assert(4 * 32 * W4_YROW <= W4_XB + W4_WB && 4 * 64 * 144 <= W4_XB + W4_WB
               "a pass of the y staging (either wave layout) fits the last x buffer and stage");
 static_assert(W4_LDS <= 160 * 1024, "LDS of one CU");
 
-// Position of chunk c of LDS row m: c ^ swz(m), swz(m) = (m ^ (m >> 3 & 1)) & 7.
-// Rows m..m+7 (m a multiple of 8) get 8 distinct swizzles, and over 16 rows each
-// parity class gets 8 distinct ones: a b128 access of 16 rows at one chunk, or
-// of one row's 8 chunks, is conflict-free for 128- and 256-byte bank widths.
-__device__ __forceinline__ int w4_swz(int m) { return (m ^ ((m >> 3) & 1)) & 7; }
-
-// The accumulators live in AGPRs (v_mfma's AGPR form); the epilogue moves them
-// through these explicit copies, because a plain VALU use of an accumulator
-// made the register allocator keep some of them in VGPRs and shuffle them
-// through the loop.
-__device__ __forceinline__ float acc_read(float a) {
-  float v;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
-  return v;
-}
-__device__ __forceinline__ float acc_write(float v) {
-  float a;
-  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
-  return a;
-}
-
-// Position of chunk c (of 4) of a 64-byte code row r: c ^ swzw(r),
-// swzw(r) = ((r >> 1) ^ (r >> 3)) & 3: reads of 8 or 16 consecutive rows at one
-// chunk hit distinct 16-byte slots for 128- and 256-byte bank widths.
-__device__ __forceinline__ int w4_swzw(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
-// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14)
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
-}
-
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 template <int TJ>
 struct W4Frag {

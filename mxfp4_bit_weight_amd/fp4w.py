@@ -45,6 +45,7 @@ _dequantize = _sig("fp4w_dequantize", _int, _int, _p, _p, _p, _i64, _i64, _p, _u
 _fake_quant = _sig("fp4w_fake_quant", _int, _int, _p, _i64, _i64, _p, _p, _p, _u32, _p)
 _ws_bytes = _sig("fp4w_linear_workspace_bytes", _sz, _i64, _i64, _i64, _int)
 _linear = _sig("fp4w_linear", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _int, _p, _p, _sz, _p)
+_w4a4 = _sig("fp4w_linear_w4a4", _int, _int, _p, _p, _i64, _i64, _p, _p, _i64, _p, _p)
 _grouped = _sig("fp4w_grouped_linear", _int, _int, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p)
 _merge = _sig("fp4w_merge_scales", _int, _int, _p, _p, _i64, _p, _p, _p, _i64, _p)
 _status = _sig("fp4w_status_string", ctypes.c_char_p, _int)
@@ -53,7 +54,7 @@ _debug_lora_wait = _sig("fp4w_debug_lora_wait", _i64, _i64)
 
 EXPORTED = ["fp4w_quantize", "fp4w_dequantize", "fp4w_linear_workspace_bytes", "fp4w_linear",
             "fp4w_grouped_linear", "fp4w_merge_scales", "fp4w_status_string", "fp4w_version",
-            "fp4w_debug_lora_wait", "fp4w_fake_quant"]
+            "fp4w_debug_lora_wait", "fp4w_fake_quant", "fp4w_linear_w4a4"]
 
 
 class Fp4wError(RuntimeError):
@@ -214,6 +215,26 @@ def linear(x: torch.Tensor, q: QWeight, lora_a: Optional[torch.Tensor] = None,
                    _ptr(lora_a), _ptr(lora_b), r, _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)),
            "fp4w_linear")
     return y
+
+
+def linear_w4a4(xq: QWeight, q: QWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4w_linear_w4a4: y = deq(x) deq(W)^T for x (m, k) and W (n, k) both
+    MXFP4 (``xq`` as ``quantize(x, MXFP4)`` returns it), bf16 out."""
+    if xq.fmt != MXFP4 or q.fmt != MXFP4:
+        raise ValueError("linear_w4a4 takes MXFP4 activations and weights")
+    if xq.k != q.k:
+        raise ValueError(f"x has k={xq.k}, the weight k={q.k}")
+    y = out if out is not None else torch.empty((xq.n, q.n), dtype=torch.bfloat16, device=q.codes.device)
+    _need(y, torch.bfloat16, "out")
+    _check(_w4a4(MXFP4, _ptr(xq.codes), _ptr(xq.scales), xq.n, xq.k, _ptr(q.codes), _ptr(q.scales), q.n,
+                 _ptr(y), _stream(y.device)), "fp4w_linear_w4a4")
+    return y
+
+
+def linear_a4(x: torch.Tensor, q: QWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The W4A4 forward from bf16 activations: x quantized to MXFP4 (fp4w_quantize),
+    then fp4w_linear_w4a4."""
+    return linear_w4a4(quantize(x, MXFP4), q, out)
 
 
 def grouped_linear(x: torch.Tensor, row_index: torch.Tensor, expert_offsets: torch.Tensor, fmt: int,

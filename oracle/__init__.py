@@ -244,6 +244,27 @@ def linear_sampled(fmt: int, x, codes, scales, tensor_scale, rows, cols, lora_a=
     return y
 
 
+def linear_w4a4(x_codes, x_scales, codes, scales):
+    """W4A4 MXFP4 (QATFactory page, section on the strategies NVFP4 and MXFP4
+    need: weights and activations both 4-bit): y (m, n) in binary64 =
+    deq(x) deq(W)^T, each operand decoded exactly (E2M1 code times its block's
+    E8M0 scale), then one binary64 matrix product."""
+    xd = dequantize(MXFP4, x_codes, x_scales, 1.0, "f64")
+    wd = dequantize(MXFP4, codes, scales, 1.0, "f64")
+    return xd @ wd.T
+
+
+def linear_w4a4_sampled(x_codes, x_scales, codes, scales, rows, cols):
+    """The outputs y[rows[s], cols[s]] of ``linear_w4a4`` only: each a binary64
+    dot product of one decoded row of x and one decoded row of W."""
+    x_codes, x_scales = _c(x_codes, np.uint8), _c(x_scales, np.uint8)
+    codes, scales = _c(codes, np.uint8), _c(scales, np.uint8)
+    rows, cols = np.asarray(rows, np.int64), np.asarray(cols, np.int64)
+    xd = dequantize(MXFP4, x_codes[rows], x_scales[rows], 1.0, "f64")
+    wd = dequantize(MXFP4, codes[cols], scales[cols], 1.0, "f64")
+    return np.einsum("sk,sk->s", xd, wd)
+
+
 def grouped_linear(fmt: int, x, row_index, offsets, codes, scales, tensor_scales):
     """MoE grouped linear: codes (E, n, k/2), scales (E, n, k/blk), tensor_scales (E,);
     rows sorted by expert with offsets (E+1,); returns y (R, n) in binary64."""

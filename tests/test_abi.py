@@ -112,3 +112,18 @@ def test_validation_errors_without_launch(lib):
     assert mg(0, None, _fake(A), 4, _fake(A), None, None, 0, None) == -1
     assert mg(0, _fake(A), _fake(A), 4, _fake(A), _fake(A + 1), _fake(A + 64), 16, None) == -3
     assert mg(0, _fake(A), _fake(A), 0, _fake(A), None, None, 0, None) == 0
+
+
+def test_w4a4_validation_without_launch(lib):
+    f = lib._w4a4
+    A = 0x10000
+    assert f(0, _fake(A), _fake(A), 4, 128, _fake(A), _fake(A), 4, _fake(A), None) == -4      # NVFP4
+    assert f(1, _fake(A), _fake(A), -1, 128, _fake(A), _fake(A), 4, _fake(A), None) == -1    # negative
+    assert f(1, _fake(A), _fake(A), 4, 96, _fake(A), _fake(A), 4, _fake(A), None) == -2      # k % 128
+    assert f(1, _fake(A), _fake(A), 4, 0, _fake(A), _fake(A), 4, _fake(A), None) == -2       # k = 0
+    assert f(1, _fake(A), _fake(A), 70000, 128, _fake(A), _fake(A), 70000, _fake(A), None) == -2  # y >= 4 GiB
+    assert f(1, None, _fake(A), 4, 128, _fake(A), _fake(A), 4, _fake(A), None) == -1         # null
+    assert f(1, _fake(A + 8), _fake(A), 4, 128, _fake(A), _fake(A), 4, _fake(A), None) == -3  # codes
+    assert f(1, _fake(A), _fake(A + 2), 4, 128, _fake(A), _fake(A), 4, _fake(A), None) == -3  # scales
+    assert f(1, _fake(A), _fake(A), 4, 128, _fake(A), _fake(A), 4, _fake(A + 1), None) == -3  # y
+    assert f(1, None, None, 0, 128, None, None, 4, None, None) == 0                          # empty

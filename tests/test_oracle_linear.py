@@ -4,6 +4,10 @@ Linear: against numpy binary64 matmul on the exactly dequantized weights; one-ho
 inputs (pin the nibble order and scale indexing); W = 0 and B = 0 special cases;
 an all-ones weight (y = sum x).  Grouped: a single expert equals the linear,
 permuting tokens permutes rows, and every row equals numpy on its expert.
+W4A4: exact-rational brute force on a tiny case (E2M1 and E8M0 decoded from
+their bit definitions), equal to the W4A16 linear when x's decoded values are
+bf16 values, one-hot activations pick one column of deq(W), the sampled form
+equals the full one.
 Merge: identity at delta 0, one grid step up, exact-rational brute force with
 constructed ties, PyTorch casts on non-tie values, code plane byte-identical.
 """
@@ -217,3 +221,81 @@ def test_merge_copies_codes_verbatim():
     sgn = np.where(q & 8, -1.0, 1.0)
     sv = np.repeat(np.array([O.e4m3_decode(s) for s in new_scales.reshape(-1)]).reshape(scales.shape), 16, axis=1)
     assert np.array_equal(d_new, sgn * mags[q & 7] * sv * float(st))
+
+
+def _e2m1_exact(c):
+    # sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0; exponent 0 is subnormal (0 or 1/2)
+    e, mnt = (c >> 1) & 3, c & 1
+    v = Fraction(mnt, 2) if e == 0 else Fraction(2 + mnt, 2) * Fraction(2) ** (e - 1)
+    return -v if c & 8 else v
+
+
+def _w4a4_exact(xc, xs, wc, ws):
+    def dec(codes, scales):
+        rows = []
+        for r in range(codes.shape[0]):
+            vals = []
+            for j in range(codes.shape[1] * 2):
+                nib = (int(codes[r, j // 2]) >> (4 * (j % 2))) & 15
+                vals.append(_e2m1_exact(nib) * Fraction(2) ** (int(scales[r, j // 32]) - 127))
+            rows.append(vals)
+        return rows
+    xd, wd = dec(xc, xs), dec(wc, ws)
+    return [[sum(a * b for a, b in zip(xr, wr)) for wr in wd] for xr in xd]
+
+
+def test_w4a4_vs_exact_fractions():
+    rng = np.random.default_rng(41)
+    m, n, k = 3, 4, 128
+    xc = rng.integers(0, 256, (m, k // 2)).astype(np.uint8)
+    wc = rng.integers(0, 256, (n, k // 2)).astype(np.uint8)
+    xs = rng.integers(100, 150, (m, k // 32)).astype(np.uint8)
+    ws = rng.integers(1, 254, (n, k // 32)).astype(np.uint8)
+    got = O.linear_w4a4(xc, xs, wc, ws)
+    want = _w4a4_exact(xc, xs, wc, ws)
+    for i in range(m):
+        for j in range(n):
+            # every product is a binary64 value; the sum of 128 of them is exact to 2^-45 relative
+            mag = max(abs(float(want[i][j])), 1e-300)
+            assert abs(got[i, j] - float(want[i][j])) <= 2.0 ** -40 * mag + 1e-300, (i, j)
+
+
+def test_w4a4_equals_w4a16_when_x_is_bf16_exact():
+    # scales in [120, 134] keep every decoded x value a bf16 value, so the
+    # W4A16 linear on deq(x) in bf16 computes the same product
+    rng = np.random.default_rng(42)
+    m, n, k = 5, 33, 256
+    xc = rng.integers(0, 256, (m, k // 2)).astype(np.uint8)
+    xs = rng.integers(120, 135, (m, k // 32)).astype(np.uint8)
+    w, _, _, _ = W.linear_inputs(5, n, k, 1)
+    wc, ws, _ = O.quantize(O.MXFP4, w)
+    x_bf16 = O.dequantize(O.MXFP4, xc, xs, 1.0, "bf16")
+    assert np.array_equal(_f64(x_bf16), O.dequantize(O.MXFP4, xc, xs, 1.0, "f64"))
+    want = O.linear(O.MXFP4, x_bf16, wc, ws, 1.0)
+    got = O.linear_w4a4(xc, xs, wc, ws)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def test_w4a4_one_hot_pins_layout():
+    w, _, _, _ = W.linear_inputs(6, 16, 64, 1)
+    wc, ws, _ = O.quantize(O.MXFP4, w)
+    deq = O.dequantize(O.MXFP4, wc, ws, 1.0, "f64")
+    for kk in (0, 1, 31, 32, 63):
+        xc = np.zeros((1, 32), np.uint8)
+        xc[0, kk // 2] = 0x2 << (4 * (kk % 2))       # code 0x2 = 1.0
+        xs = np.full((1, 2), 127, np.uint8)          # E8M0 127 = 2^0
+        xs[0, kk // 32] = 128                        # this block: x[kk] = 2
+        got = O.linear_w4a4(xc, xs, wc, ws)
+        assert np.array_equal(got[0], 2.0 * deq[:, kk]), kk
+
+
+def test_w4a4_sampled_matches_full():
+    rng = np.random.default_rng(43)
+    m, n, k = 9, 7, 96 + 32
+    xc = rng.integers(0, 256, (m, k // 2)).astype(np.uint8)
+    wc = rng.integers(0, 256, (n, k // 2)).astype(np.uint8)
+    xs = rng.integers(110, 140, (m, k // 32)).astype(np.uint8)
+    ws = rng.integers(110, 140, (n, k // 32)).astype(np.uint8)
+    full = O.linear_w4a4(xc, xs, wc, ws)
+    rows, cols = rng.integers(0, m, 20), rng.integers(0, n, 20)
+    assert np.array_equal(O.linear_w4a4_sampled(xc, xs, wc, ws, rows, cols), full[rows, cols])

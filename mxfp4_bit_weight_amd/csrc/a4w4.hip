@@ -36,14 +36,18 @@
 
 namespace fp4w {
 
-constexpr int A4_BM = 256, A4_BN = 256, A4_BK = 128, A4_THREADS = 256, A4_GM = 4;
-constexpr int A4_CB = 256 * 64;                       // code bytes of one operand's tile
-constexpr int A4_SB = 256 * 4;                        // scale bytes of one operand's tile
-constexpr int A4_XC = 0, A4_WC = A4_CB, A4_XS = 2 * A4_CB, A4_WS = 2 * A4_CB + A4_SB;   // offsets in a set
-constexpr int A4_SET = 2 * (A4_CB + A4_SB);           // 34816 bytes per buffer set
-constexpr int A4_LDS = 3 * A4_SET;
+constexpr int A4_BM = 256, A4_BN = 256, A4_BK = 256, A4_THREADS = 256, A4_GM = 4;
+constexpr int A4_CB = 256 * 128;                      // code bytes of one operand's K tile (256 rows x 128 B)
+constexpr int A4_SET = 2 * A4_CB;                     // one buffer set: x codes, then W codes
+constexpr int A4_SC = 2 * A4_SET;                     // scale buffers: [2][x, W][256 rows][16 B]
+constexpr int A4_SCB = 256 * 16;                      // scale bytes of one operand's 512-k chunk
+constexpr int A4_LDS = A4_SC + 4 * A4_SCB;            // 147456 bytes
 constexpr int A4_YROW = 272;                          // bytes per staged y row (128 bf16 + 16)
-static_assert(4 * 32 * A4_YROW <= A4_SET, "the y staging of one pass fits buffer set 2");
+static_assert(4 * 32 * A4_YROW <= A4_SET, "the y staging of one pass fits buffer set 1");
+
+// position of 16-byte chunk c of code row r in LDS: c ^ swz(r); 8 (16) consecutive
+// rows read at one chunk hit 8 (16) distinct 16-byte bank groups
+__device__ __forceinline__ int a4_swz(int r) { return (r & 7) ^ ((r >> 3) & 3); }
 
 __global__ __launch_bounds__(A4_THREADS, 1) void gemm_a4w4_kernel(
     const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, int M, int K,
@@ -72,70 +76,83 @@ __global__ __launch_bounds__(A4_THREADS, 1) void gemm_a4w4_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int xrow0 = 128 * (wave >> 1), wcol0 = 128 * (wave & 1);
   const int l32 = lane & 31, hh = lane >> 5;
+  const int nkf = K / A4_BK, nk = (K + A4_BK - 1) / A4_BK;   // full K tiles; with a 128-k tail
 
   const __amdgpu_buffer_rsrc_t xcr = make_rsrc(xc, (uint32_t)M * (uint32_t)(K / 2));
   const __amdgpu_buffer_rsrc_t xsr = make_rsrc(xs, (uint32_t)M * (uint32_t)(K / 32));
   const __amdgpu_buffer_rsrc_t wcr = make_rsrc(wc, (uint32_t)N * (uint32_t)(K / 2));
   const __amdgpu_buffer_rsrc_t wsr = make_rsrc(ws, (uint32_t)N * (uint32_t)(K / 32));
 
-  // DMA lanes.  Codes: instruction i (of 4) of wave w fills rows 64 i + 16 w ..
-  // + 15 of a 256 x 64-byte tile; lane l takes row + l / 4, position l % 4, so
-  // it loads that row's chunk (l % 4) ^ swzw(row).  Scales (4-byte DMA): wave w
-  // fills rows 64 w + l, the 4 scale bytes of the tile's 128 k.  Rows past the
-  // matrix read zeros (past the buffer's end).
-  const int crow = 16 * wave + (lane >> 2);
-  const uint32_t clane = 16u * (uint32_t)((lane & 3) ^ w4_swzw(crow));
-  const int srow = 64 * wave + lane;
+  // DMA lanes.  Codes: instruction i (of 8) of wave w fills rows 32 i + 8 w ..
+  // + 7 of a 256 x 128-byte tile; lane l takes row + l / 8, position l % 8, so it
+  // loads that row's chunk (l % 8) ^ swz(row).  Scales, every second K tile: the
+  // 16 bytes of 512 k of each row, 4 lanes a row (4-byte DMA): instruction i (of
+  // 4) of wave w fills rows 64 w + 16 i .. + 15.  Rows past the matrix read zeros
+  // (past the buffer's end); bytes past a row's end feed nothing.
+  const int crow = 8 * wave + (lane >> 3);
+  const uint32_t clane = 16u * (uint32_t)((lane & 7) ^ a4_swz(crow));
+  const int srow = 64 * wave + (lane >> 2);
+  const uint32_t slane = 4u * (uint32_t)(lane & 3);
   uint32_t xcb, wcb, xsb, wsb;
   auto set_bases = [&](int om0, int on0) __attribute__((always_inline)) {
     xcb = (uint32_t)(om0 + crow) * (uint32_t)(K / 2) + clane;
     wcb = (uint32_t)(on0 + crow) * (uint32_t)(K / 2) + clane;
-    xsb = (uint32_t)(om0 + srow) * (uint32_t)(K / 32);
-    wsb = (uint32_t)(on0 + srow) * (uint32_t)(K / 32);
+    xsb = (uint32_t)(om0 + srow) * (uint32_t)(K / 32) + slane;
+    wsb = (uint32_t)(on0 + srow) * (uint32_t)(K / 32) + slane;
   };
   set_bases(m0, n0);
   auto setp = [&](int i) __attribute__((always_inline)) -> uint8_t* { return smem + i * A4_SET; };
-  // 10 DMAs a wave: 4 + 4 of codes, 1 + 1 of scales
-  auto dma_tile = [&](uint8_t* set, int k0) __attribute__((always_inline)) {
+  auto scp = [&](int b) __attribute__((always_inline)) -> uint8_t* { return smem + A4_SC + b * 2 * A4_SCB; };
+  // live == false: the DMAs still run (no branch around them in the K loop)
+  // but read past the buffers, so they fetch nothing and write zeros
+  auto dma_codes = [&](uint8_t* set, int k0, bool live) __attribute__((always_inline)) {   // 16 DMAs a wave
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const uint32_t ro = (uint32_t)i * 32u * (uint32_t)(K / 2) + (uint32_t)(k0 / 2);
+      dma16(xcr, set + (32 * i + 8 * wave) * 128, live ? xcb + ro : kBufferOob);
+      dma16(wcr, set + A4_CB + (32 * i + 8 * wave) * 128, live ? wcb + ro : kBufferOob);
+    }
+  };
+  auto dma_scales = [&](uint8_t* sb, int k0, bool live) __attribute__((always_inline)) {   // 8 DMAs a wave
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const uint32_t ro = (uint32_t)i * 64u * (uint32_t)(K / 2) + (uint32_t)(k0 / 2);
-      dma16(xcr, set + A4_XC + (64 * i + 16 * wave) * 64, xcb + ro);
-      dma16(wcr, set + A4_WC + (64 * i + 16 * wave) * 64, wcb + ro);
+      const uint32_t ro = (uint32_t)i * 16u * (uint32_t)(K / 32) + (uint32_t)(k0 / 32);
+      dma4(xsr, sb + (64 * wave + 16 * i) * 16, live ? xsb + ro : kBufferOob);
+      dma4(wsr, sb + A4_SCB + (64 * wave + 16 * i) * 16, live ? wsb + ro : kBufferOob);
     }
-    dma4(xsr, set + A4_XS + 64 * wave * 4, xsb + (uint32_t)(k0 / 32));
-    dma4(wsr, set + A4_WS + 64 * wave * 4, wsb + (uint32_t)(k0 / 32));
   };
 
-  // fragments of step s (k 64 s .. 64 s + 63 of the tile): chunk 2 s + hh of
-  // rows xrow0 / wcol0 + 32 i + l32; the rows' 4 scale bytes once a tile, shifted
-  // so that the block of step s and half hh sits in byte 2 s (the MFMA's opsel)
+  // fragments of step s (k 64 s .. 64 s + 63 of the K tile): chunk 2 s + hh of
+  // rows xrow0 / wcol0 + 32 i + l32 (swz does not depend on the 32 i)
   const int arow = xrow0 + l32, brow = wcol0 + l32;
-  int xoff[2], woff[2];
-#pragma unroll
-  for (int s = 0; s < 2; s++) {
-    xoff[s] = arow * 64 + 16 * ((2 * s + hh) ^ w4_swzw(arow));
-    woff[s] = brow * 64 + 16 * ((2 * s + hh) ^ w4_swzw(brow));
-  }
   typedef __attribute__((ext_vector_type(8))) int i32x8_t;
   struct Frag {
     i32x8_t x[4], w[4];
   };
   auto read_frag = [&](Frag& f, const uint8_t* set, int s) __attribute__((always_inline)) {
+    const int xo = arow * 128 + 16 * ((2 * s + hh) ^ a4_swz(arow));
+    const int wo = A4_CB + brow * 128 + 16 * ((2 * s + hh) ^ a4_swz(brow));
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(set + A4_XC + xoff[s] + 32 * i * 64);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(set + xo + 32 * i * 128);
       f.x[i] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      const u32x4_t u = *reinterpret_cast<const u32x4_t*>(set + A4_WC + woff[s] + 32 * i * 64);
+      const u32x4_t u = *reinterpret_cast<const u32x4_t*>(set + wo + 32 * i * 128);
       f.w[i] = i32x8_t{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
     }
   };
-  uint32_t xsc[4], wsc[4];
-  auto read_scales = [&](const uint8_t* set) __attribute__((always_inline)) {
+  // the 8 scale bytes of K tile kt for each fragment row, as two words shifted
+  // so that the block of step s and half hh sits in byte 2 (s % 2) of word s / 2
+  uint32_t xsc[4][2], wsc[4][2];
+  auto read_scales = [&](int kt) __attribute__((always_inline)) {
+    const uint8_t* sb = scp((kt >> 1) & 1) + 8 * (kt & 1);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      xsc[i] = *reinterpret_cast<const uint32_t*>(set + A4_XS + (arow + 32 * i) * 4) >> (8 * hh);
-      wsc[i] = *reinterpret_cast<const uint32_t*>(set + A4_WS + (brow + 32 * i) * 4) >> (8 * hh);
+      const uint2 a = *reinterpret_cast<const uint2*>(sb + (arow + 32 * i) * 16);
+      const uint2 b = *reinterpret_cast<const uint2*>(sb + A4_SCB + (brow + 32 * i) * 16);
+      xsc[i][0] = a.x >> (8 * hh);
+      xsc[i][1] = a.y >> (8 * hh);
+      wsc[i][0] = b.x >> (8 * hh);
+      wsc[i][1] = b.y >> (8 * hh);
     }
   };
 
@@ -145,80 +162,88 @@ __global__ __launch_bounds__(A4_THREADS, 1) void gemm_a4w4_kernel(
     for (int j = 0; j < 4; j++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        if (s == 0)
+        if ((s & 1) == 0)
           acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[j], f.x[i], acc[j][i], 4, 4, 0,
-                                                                       (int)wsc[j], 0, (int)xsc[i]);
+                                                                       (int)wsc[j][s >> 1], 0, (int)xsc[i][s >> 1]);
         else
           acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[j], f.x[i], acc[j][i], 4, 4, 2,
-                                                                       (int)wsc[j], 2, (int)xsc[i]);
+                                                                       (int)wsc[j][s >> 1], 2, (int)xsc[i][s >> 1]);
       }
   };
   auto fence = [&]() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
 
-  const int nk = K / A4_BK;
   Frag f0, f1;
-  uint32_t xsn[4], wsn[4];
-  // one K tile (buffer set kt % 3): on entry f0 and xsc / wsc hold its step-0
-  // fragments and its scale words (reads issued)
+  // one full K tile (buffer set kt % 2): on entry f0 and the scale words hold
+  // its step-0 fragments and its scales (reads issued).  Step 0 issues the DMA
+  // of tile kt + 1 into the other set (every wave finished reading it before
+  // the previous barrier); each wave waits for its own DMA before the barrier
+  // ahead of step 3, which reads the next tile's step-0 fragments and scales.
   auto tile = [&](int kt) __attribute__((always_inline)) {
-    const uint8_t* cur = setp(kt % 3);
+    const uint8_t* cur = setp(kt & 1);
     read_frag(f1, cur, 1);
-    dma_tile(setp((kt + 2) % 3), (kt + 2) * A4_BK);
+    // the next K tile's codes; on odd kt the scales of the next 512 k into the
+    // scale buffer not in use (on even kt that buffer, idle, takes zeros)
+    dma_codes(setp((kt + 1) & 1), (kt + 1) * A4_BK, kt + 1 < nk);
+    dma_scales(scp(((kt >> 1) + 1) & 1), (kt + 1) * A4_BK, (kt & 1) && kt + 1 < nk);
     mfma_step(f0, 0);
     fence();
-    wait_vm_lgkm0<10>();                          // this wave's DMA of tile kt + 1 is done
-    __builtin_amdgcn_s_barrier();
-    fence();
-    const uint8_t* nxt = setp((kt + 1) % 3);
-    read_frag(f0, nxt, 0);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      xsn[i] = *reinterpret_cast<const uint32_t*>(nxt + A4_XS + (arow + 32 * i) * 4) >> (8 * hh);
-      wsn[i] = *reinterpret_cast<const uint32_t*>(nxt + A4_WS + (brow + 32 * i) * 4) >> (8 * hh);
-    }
+    read_frag(f0, cur, 2);
     mfma_step(f1, 1);
     fence();
-#pragma unroll
-    for (int i = 0; i < 4; i++) { xsc[i] = xsn[i]; wsc[i] = wsn[i]; }
+    read_frag(f1, cur, 3);
+    mfma_step(f0, 2);
+    fence();
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    fence();
+    read_frag(f0, setp((kt + 1) & 1), 0);
+    mfma_step(f1, 3);
+    fence();
+    read_scales(kt + 1);
   };
 
-  dma_tile(setp(0), 0);
-  dma_tile(setp(1), A4_BK);
+  dma_codes(setp(0), 0, true);
+  dma_scales(scp(0), 0, true);
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   fence();
   for (;;) {
     read_frag(f0, setp(0), 0);
-    read_scales(setp(0));
+    read_scales(0);
 #pragma unroll
     for (int j = 0; j < 4; j++)
 #pragma unroll
       for (int i = 0; i < 4; i++) acc[j][i] = f32x16_t{};
     fence();
-    // DMAs past K (the last two tiles' successors) read the next rows' data or
-    // zeros past the buffers and feed nothing
-    for (int kt = 0; kt < nk; kt++) tile(kt);
+    for (int kt = 0; kt < nkf; kt++) tile(kt);
+    if (nk > nkf) {                               // the last 128 k: steps 0 and 1 of tile nkf
+      read_frag(f1, setp(nkf & 1), 1);
+      mfma_step(f0, 0);
+      fence();
+      mfma_step(f1, 1);
+      fence();
+    }
     wait_vm_lgkm0<0>();                           // every wave is past the loop's last LDS reads
     __builtin_amdgcn_s_barrier();
     fence();
     const int em0 = m0, en0 = n0;
     const int nlocal = local + nwg;
     const bool more = nlocal < xcount;
-    if (more) {                                   // the next tile's first two K tiles, into sets 0 and 1
+    if (more) {                                   // the next tile's first K tile, into set 0
       origin(nlocal, m0, n0);
       set_bases(m0, n0);
-      dma_tile(setp(0), 0);
-      dma_tile(setp(1), A4_BK);
+      dma_codes(setp(0), 0, true);
+      dma_scales(scp(0), 0, true);
     }
     asm volatile("" ::: "memory");                // the stores below stay after these DMAs
     fence();
 
-    // store (as in gemm.hip): 4 passes of one x block each through set 2, 32 rows
+    // store (as in gemm.hip): 4 passes of one x block each through set 1, 32 rows
     // x 128 bf16 a wave, 8 stores of 16 bytes a lane and pass (rows and columns
     // past y dropped); flags & 1: y 16-byte aligned and n a multiple of 8, else
     // 2-byte stores
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)M * (uint32_t)N * 2u);
-    uint8_t* const ysg = smem + 2 * A4_SET + wave * (32 * A4_YROW);
+    uint8_t* const ysg = setp(1) + wave * (32 * A4_YROW);
     const int rr = lane >> 4, cc = lane & 15;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -253,8 +278,8 @@ __global__ __launch_bounds__(A4_THREADS, 1) void gemm_a4w4_kernel(
       __builtin_amdgcn_s_waitcnt(0xC07F);         // this pass's LDS reads done before the next pass writes
     }
     if (!more) break;
-    // the next tile's DMA was issued before this tile's 32 vector stores of y
-    // (or 256 element stores), which may stay in flight
+    // the next tile's 24 DMAs were issued before this tile's 32 vector stores of
+    // y (or 256 element stores), which may stay in flight
     if (flags & 1) wait_vm_lgkm0<32>();
     else wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
@@ -263,11 +288,11 @@ __global__ __launch_bounds__(A4_THREADS, 1) void gemm_a4w4_kernel(
   }
 }
 
-// The DMA offsets reach (rows + 255) * k/2 + k/2 + 112 bytes into a code plane
-// (the last tile's rows and the two K tiles past the end), all 32-bit.
+// The DMA offsets reach (rows + 255) * k/2 + k/2 + 64 bytes into a code plane
+// (the last tile's rows, a 128-k tail loaded as a full K tile), all 32-bit.
 bool gemm_a4w4_supports(int64_t m, int64_t n, int64_t k) {
   const int64_t lim = (int64_t)1 << 31;
-  return k > 0 && k % A4_BK == 0 && k < lim && (m + 2 * A4_BM) * (k / 2) < lim && (n + 2 * A4_BN) * (k / 2) < lim &&
+  return k > 0 && k % 128 == 0 && k < lim && (m + 2 * A4_BM) * (k / 2) < lim && (n + 2 * A4_BN) * (k / 2) < lim &&
          m * n * 2 < ((int64_t)1 << 32);
 }
 

@@ -143,16 +143,22 @@ __global__ __launch_bounds__(A4_THREADS, 1) void gemm_a4w4_kernel(
   // the 8 scale bytes of K tile kt for each fragment row, as two words shifted
   // so that the block of step s and half hh sits in byte 2 (s % 2) of word s / 2
   uint32_t xsc[4][2], wsc[4][2];
-  auto read_scales = [&](int kt) __attribute__((always_inline)) {
+  uint2 xsr_[4], wsr_[4];
+  auto read_scales_raw = [&](int kt) __attribute__((always_inline)) {
     const uint8_t* sb = scp((kt >> 1) & 1) + 8 * (kt & 1);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const uint2 a = *reinterpret_cast<const uint2*>(sb + (arow + 32 * i) * 16);
-      const uint2 b = *reinterpret_cast<const uint2*>(sb + A4_SCB + (brow + 32 * i) * 16);
-      xsc[i][0] = a.x >> (8 * hh);
-      xsc[i][1] = a.y >> (8 * hh);
-      wsc[i][0] = b.x >> (8 * hh);
-      wsc[i][1] = b.y >> (8 * hh);
+      xsr_[i] = *reinterpret_cast<const uint2*>(sb + (arow + 32 * i) * 16);
+      wsr_[i] = *reinterpret_cast<const uint2*>(sb + A4_SCB + (brow + 32 * i) * 16);
+    }
+  };
+  auto shift_scales = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      xsc[i][0] = xsr_[i].x >> (8 * hh);
+      xsc[i][1] = xsr_[i].y >> (8 * hh);
+      wsc[i][0] = wsr_[i].x >> (8 * hh);
+      wsc[i][1] = wsr_[i].y >> (8 * hh);
     }
   };
 
@@ -181,6 +187,7 @@ __global__ __launch_bounds__(A4_THREADS, 1) void gemm_a4w4_kernel(
   auto tile = [&](int kt) __attribute__((always_inline)) {
     const uint8_t* cur = setp(kt & 1);
     read_frag(f1, cur, 1);
+    fence();                                      // each step's reads go out ahead of its MFMAs
     // the next K tile's codes; on odd kt the scales of the next 512 k into the
     // scale buffer not in use (on even kt that buffer, idle, takes zeros)
     dma_codes(setp((kt + 1) & 1), (kt + 1) * A4_BK, kt + 1 < nk);
@@ -188,18 +195,22 @@ __global__ __launch_bounds__(A4_THREADS, 1) void gemm_a4w4_kernel(
     mfma_step(f0, 0);
     fence();
     read_frag(f0, cur, 2);
+    fence();
     mfma_step(f1, 1);
     fence();
     read_frag(f1, cur, 3);
+    fence();
     mfma_step(f0, 2);
     fence();
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
     fence();
     read_frag(f0, setp((kt + 1) & 1), 0);
+    read_scales_raw(kt + 1);
+    fence();
     mfma_step(f1, 3);
     fence();
-    read_scales(kt + 1);
+    shift_scales();
   };
 
   dma_codes(setp(0), 0, true);
@@ -209,7 +220,8 @@ __global__ __launch_bounds__(A4_THREADS, 1) void gemm_a4w4_kernel(
   fence();
   for (;;) {
     read_frag(f0, setp(0), 0);
-    read_scales(0);
+    read_scales_raw(0);
+    shift_scales();
 #pragma unroll
     for (int j = 0; j < 4; j++)
 #pragma unroll
@@ -218,6 +230,7 @@ __global__ __launch_bounds__(A4_THREADS, 1) void gemm_a4w4_kernel(
     for (int kt = 0; kt < nkf; kt++) tile(kt);
     if (nk > nkf) {                               // the last 128 k: steps 0 and 1 of tile nkf
       read_frag(f1, setp(nkf & 1), 1);
+      fence();
       mfma_step(f0, 0);
       fence();
       mfma_step(f1, 1);

@@ -7,8 +7,8 @@ of distinct copies so that every call streams its weights from HBM.  ``value``
 is the step's algorithmic bytes over its time (GB/s).  The JSON line also holds
 the roofline of the decode kernel (HIP events around a graph of back-to-back
 launches of it), the CPU oracle timed on a bounded sample, and the other
-hot-path rows (M = 8, MXFP4, the 16384-row prefill GEMM, quantize, merge,
-dequantize, grouped MoE).
+hot-path rows (M = 8, MXFP4, the 16384-row prefill GEMM and its W4A4 MXFP4
+form, quantize, merge, dequantize, grouped MoE).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-rows]
        python bench.py --roofline-only   (the decode kernel's launches and a plain
@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 ROTATE_BYTES = 1 << 30         # rotate each weight over at least 1 GiB (4x the 256 MB MALL)
 METRIC = "W4A16 NVFP4 linear: effective HBM GB/s (% peak) at M=1/8; TFLOP/s at M=16K"
@@ -292,6 +293,17 @@ def gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights):
         rows[f"prefill_gemm_{name}"] = {"m": mrows, "n": n, "k": k, "ms": round(gms, 3), "TFLOP/s": round(tf, 1),
                                         "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 1), "algorithmic_flop": fl}
         log(f"[bench] prefill GEMM {name} {gms:.3f} ms, {tf:.1f} TFLOP/s")
+        if fmt == 1:
+            # W4A4: the same x quantized to MXFP4 (outside the timed region), then
+            # the block-scaled fp4 product against the same MXFP4 weight
+            xq = fp4w.quantize(x, 1)
+            ams, _ = time_loop(lambda i: fp4w.linear_w4a4(xq, q, out=y), 10, 10)
+            afl = 2 * mrows * n * k
+            atf = afl / (ams * 1e-3) / 1e12
+            rows["prefill_w4a4_mxfp4"] = {"m": mrows, "n": n, "k": k, "ms": round(ams, 3), "TFLOP/s": round(atf, 1),
+                                          "pct_fp4_peak": round(100 * atf / FP4_PEAK_TFLOPS, 1), "algorithmic_flop": afl}
+            log(f"[bench] prefill W4A4 mxfp4 {ams:.3f} ms, {atf:.1f} TFLOP/s")
+            del xq
         del x, y, wsg
     return rows
 

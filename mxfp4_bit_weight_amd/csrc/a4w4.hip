@@ -23,13 +23,13 @@
 //
 // One workgroup per CU, looping over 256 x 256 tiles of y (tile order as in
 // gemm.hip); 4 waves in 2 x 2, each 128 x 128 = 4 x 4 products, 256 fp32
-// accumulators in AGPRs.  Per K tile of 128 (two MFMA steps of 64): the codes of
-// x and of W (256 rows x 64 bytes each) and their scale bytes (4 a row) reach
-// LDS by DMA, three buffer sets, two K tiles ahead; code rows are swizzled as
-// in gemm.hip.  Step 0 reads step 1's fragments and issues the DMA of tile
-// kt + 2; the barrier (after each wave's wait for its DMA of tile kt + 1) sits
-// before step 1, whose MFMAs cover the reads of the next tile's step-0
-// fragments.
+// accumulators in AGPRs.  Per K tile of 256 (four MFMA steps of 64): the codes
+// of x and of W (256 rows x 128 bytes each, one cache line a row) reach LDS by
+// DMA, two buffer sets, one K tile ahead; the scale bytes of 512 k per row
+// (16 bytes) every second K tile into one of two scale buffers.  Each step's
+// fragment reads are issued ahead of its MFMAs; one barrier per K tile, after
+// each wave's wait for its own DMA of the next tile.  K a multiple of 128 (a
+// 128-k tail runs two steps of a last K tile).
 #include "fp4w_device.hpp"
 #include "fp4w_internal.hpp"
 #include "gemm_common.hpp"

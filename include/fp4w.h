@@ -193,6 +193,25 @@ int fp4w_linear_w4a4(int fmt, const uint8_t *x_codes, const uint8_t *x_scales,
                      int64_t n, void *y_bf16, void *stream);
 
 /*
+ * fp4w_linear_backward_dx -- the input gradient through the frozen 4-bit base:
+ * dx (m, k) bf16 = dy (m, n) deq(W) (n, k), fp32 accumulation, rounded once to
+ * bf16 (training with the quantized base frozen back-propagates through it;
+ * Telegram post, "Metod").  The weight is decoded exactly (as fp4w_dequantize
+ * to bf16), the NVFP4 tensor scale multiplies the fp32 sums.  The LoRA branch's
+ * own gradients are not formed here.
+ *   dy_bf16    (m, n) bf16, 16-byte aligned;  n % 8 == 0 (else FP4W_ERR_SHAPE)
+ *   codes, scales, tensor_scale   a quantized W (n, k), as fp4w_quantize writes it
+ *   dx_bf16    (m, k) bf16, 8-byte aligned
+ * m at most 65535 * 128.  n == 0 writes zeros; m == 0 or k == 0 does nothing.
+ * A NaN block scale makes the outputs of its block's k columns NaN in every
+ * row.  One launch on `stream`; no workspace.
+ */
+int fp4w_linear_backward_dx(int fmt, const void *dy_bf16, int64_t m, int64_t n,
+                            const uint8_t *codes, const uint8_t *scales,
+                            const float *tensor_scale, int64_t k, void *dx_bf16,
+                            void *stream);
+
+/*
  * fp4w_grouped_linear -- the W4A16 linear over the experts of a mixture of
  * experts (QATFactory page: dense and MoE models; Nemotron page: 30B-A3B base).
  * For every expert e and every row q in [expert_offsets[e], expert_offsets[e+1]):

@@ -32,7 +32,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP4W_OK : FP4W_ERR_HIP; 
 
 extern "C" {
 
-int fp4w_version(void) { return 5; }
+int fp4w_version(void) { return 6; }
 
 const char* fp4w_status_string(int status) {
   switch (status) {
@@ -133,6 +133,23 @@ int fp4w_linear_w4a4(int fmt, const uint8_t* x_codes, const uint8_t* x_scales, i
   if (((reinterpret_cast<uintptr_t>(x_scales) | reinterpret_cast<uintptr_t>(scales)) & 3u) != 0)
     return FP4W_ERR_ALIGN;
   return hip_status(fp4w::launch_gemm_a4w4(x_codes, x_scales, m, k, codes, scales, n, y_bf16, as_stream(stream)));
+}
+
+int fp4w_linear_backward_dx(int fmt, const void* dy_bf16, int64_t m, int64_t n, const uint8_t* codes,
+                            const uint8_t* scales, const float* tensor_scale, int64_t k, void* dx_bf16, void* stream) {
+  if (!valid_fmt(fmt)) return FP4W_ERR_FORMAT;
+  if (m < 0 || n < 0 || k < 0) return FP4W_ERR_ARG;
+  int st = check_nk(n, k);
+  if (st) return st;
+  if (n % 8 != 0 || m > ((int64_t)65535 * 128) || n > 0x7FFFFFFF || k > 0x7FFFFFFF) return FP4W_ERR_SHAPE;
+  if (m > 0 && n > kMaxElems / (m > 0 ? m : 1)) return FP4W_ERR_SHAPE;
+  if (m == 0 || k == 0) return FP4W_OK;
+  if (!dx_bf16 || (n > 0 && (!dy_bf16 || !codes || !scales))) return FP4W_ERR_ARG;
+  if (fmt == FP4W_NVFP4 && !tensor_scale) return FP4W_ERR_ARG;
+  if (!aligned16(dy_bf16) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(dx_bf16) & 7u) != 0)
+    return FP4W_ERR_ALIGN;
+  return hip_status(fp4w::launch_backward_dx(fmt, dy_bf16, m, n, codes, scales, tensor_scale, k, dx_bf16,
+                                             as_stream(stream)));
 }
 
 int fp4w_grouped_linear(int fmt, const void* x_bf16, int64_t num_tokens, const int32_t* row_index,

@@ -46,6 +46,7 @@ _fake_quant = _sig("fp4w_fake_quant", _int, _int, _p, _i64, _i64, _p, _p, _p, _u
 _ws_bytes = _sig("fp4w_linear_workspace_bytes", _sz, _i64, _i64, _i64, _int)
 _linear = _sig("fp4w_linear", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _int, _p, _p, _sz, _p)
 _w4a4 = _sig("fp4w_linear_w4a4", _int, _int, _p, _p, _i64, _i64, _p, _p, _i64, _p, _p)
+_bwd_dx = _sig("fp4w_linear_backward_dx", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p)
 _grouped = _sig("fp4w_grouped_linear", _int, _int, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p)
 _merge = _sig("fp4w_merge_scales", _int, _int, _p, _p, _i64, _p, _p, _p, _i64, _p)
 _status = _sig("fp4w_status_string", ctypes.c_char_p, _int)
@@ -54,7 +55,7 @@ _debug_lora_wait = _sig("fp4w_debug_lora_wait", _i64, _i64)
 
 EXPORTED = ["fp4w_quantize", "fp4w_dequantize", "fp4w_linear_workspace_bytes", "fp4w_linear",
             "fp4w_grouped_linear", "fp4w_merge_scales", "fp4w_status_string", "fp4w_version",
-            "fp4w_debug_lora_wait", "fp4w_fake_quant", "fp4w_linear_w4a4"]
+            "fp4w_debug_lora_wait", "fp4w_fake_quant", "fp4w_linear_w4a4", "fp4w_linear_backward_dx"]
 
 
 class Fp4wError(RuntimeError):
@@ -235,6 +236,20 @@ def linear_a4(x: torch.Tensor, q: QWeight, out: Optional[torch.Tensor] = None) -
     """The W4A4 forward from bf16 activations: x quantized to MXFP4 (fp4w_quantize),
     then fp4w_linear_w4a4."""
     return linear_w4a4(quantize(x, MXFP4), q, out)
+
+
+def linear_backward_dx(dy: torch.Tensor, q: QWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4w_linear_backward_dx: dx = dy deq(W) (the input gradient through the
+    frozen base), bf16 in and out, fp32 accumulation."""
+    _need(dy, torch.bfloat16, "dy")
+    m, n = dy.shape
+    if n != q.n:
+        raise ValueError(f"dy has n={n}, the weight n={q.n}")
+    dx = out if out is not None else torch.empty((m, q.k), dtype=torch.bfloat16, device=dy.device)
+    _need(dx, torch.bfloat16, "out")
+    _check(_bwd_dx(q.fmt, _ptr(dy), m, n, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.k, _ptr(dx),
+                   _stream(dy.device)), "fp4w_linear_backward_dx")
+    return dx
 
 
 def grouped_linear(x: torch.Tensor, row_index: torch.Tensor, expert_offsets: torch.Tensor, fmt: int,

@@ -244,6 +244,16 @@ def linear_sampled(fmt: int, x, codes, scales, tensor_scale, rows, cols, lora_a=
     return y
 
 
+def linear_backward_dx(fmt: int, dy, codes, scales, tensor_scale):
+    """Input gradient through the frozen quantized base (Telegram post, "Metod":
+    the base stays frozen while training back-propagates through it): dX (m, k)
+    in binary64 = dY deq(W), dY bf16 (m, n), W decoded exactly, one binary64
+    matrix product."""
+    dy = _c(np.atleast_2d(dy), np.uint16)
+    dyf = (dy.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return dyf @ dequantize(fmt, codes, scales, tensor_scale, "f64")
+
+
 def linear_w4a4(x_codes, x_scales, codes, scales):
     """W4A4 MXFP4 (QATFactory page, section on the strategies NVFP4 and MXFP4
     need: weights and activations both 4-bit): y (m, n) in binary64 =

@@ -299,3 +299,32 @@ def test_w4a4_sampled_matches_full():
     full = O.linear_w4a4(xc, xs, wc, ws)
     rows, cols = rng.integers(0, m, 20), rng.integers(0, n, 20)
     assert np.array_equal(O.linear_w4a4_sampled(xc, xs, wc, ws, rows, cols), full[rows, cols])
+
+
+@pytest.mark.parametrize("fmt", [O.NVFP4, O.MXFP4])
+def test_backward_dx_adjoint_of_linear(fmt):
+    # <dY, x deq(W)^T> = <dY deq(W), x>: the backward oracle is the adjoint of
+    # the (independent, C) forward oracle -- a transposed or mis-scaled operand fails
+    w, x, _, _ = W.linear_inputs(21, 40, 96, 7)
+    codes, scales, st = O.quantize(fmt, w)
+    rng = np.random.default_rng(22)
+    dy = W.to_bf16_bits(rng.standard_normal((7, 40)))
+    lhs = float(np.sum(_f64(dy) * O.linear(fmt, x, codes, scales, st)))
+    dx = O.linear_backward_dx(fmt, dy, codes, scales, st)
+    assert dx.shape == (7, 96)
+    rhs = float(np.sum(dx * _f64(x)))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+@pytest.mark.parametrize("fmt", [O.NVFP4, O.MXFP4])
+def test_backward_dx_one_hot_rows(fmt):
+    w, _, _, _ = W.linear_inputs(23, 24, 64, 1)
+    codes, scales, st = O.quantize(fmt, w)
+    deq = O.dequantize(fmt, codes, scales, st, "f64")
+    dy = np.zeros((3, 24), np.uint16)
+    dy[0, 5] = 0x3F80                                # 1.0
+    dy[2, 23] = 0xC000                               # -2.0
+    dx = O.linear_backward_dx(fmt, dy, codes, scales, st)
+    assert np.array_equal(dx[0], deq[5])
+    assert not dx[1].any()
+    assert np.array_equal(dx[2], -2.0 * deq[23])

@@ -7,8 +7,9 @@ of distinct copies so that every call streams its weights from HBM.  ``value``
 is the step's algorithmic bytes over its time (GB/s).  The JSON line also holds
 the roofline of the decode kernel (HIP events around a graph of back-to-back
 launches of it), the CPU oracle timed on a bounded sample, and the other
-hot-path rows (M = 8, MXFP4, the 16384-row prefill GEMM and its W4A4 MXFP4
-form, quantize, merge, dequantize, grouped MoE).
+hot-path rows (M = 8, MXFP4, the 16384-row prefill GEMM, its backward dX
+through the frozen base and its W4A4 MXFP4 form, quantize, merge, dequantize,
+grouped MoE).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-rows]
        python bench.py --roofline-only   (the decode kernel's launches and a plain
@@ -293,6 +294,16 @@ def gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights):
         rows[f"prefill_gemm_{name}"] = {"m": mrows, "n": n, "k": k, "ms": round(gms, 3), "TFLOP/s": round(tf, 1),
                                         "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 1), "algorithmic_flop": fl}
         log(f"[bench] prefill GEMM {name} {gms:.3f} ms, {tf:.1f} TFLOP/s")
+        # the input gradient through the frozen base for the same shape: dX = dY deq(W),
+        # dY the forward's output (m x n), dX m x k
+        dx = torch.empty((mrows, k), dtype=torch.bfloat16, device=dev)
+        bms, _ = time_loop(lambda i: fp4w.linear_backward_dx(y, q, out=dx), 10, 10)
+        bfl = 2 * mrows * n * k
+        btf = bfl / (bms * 1e-3) / 1e12
+        rows[f"backward_dx_{name}"] = {"m": mrows, "n": n, "k": k, "ms": round(bms, 3), "TFLOP/s": round(btf, 1),
+                                       "pct_bf16_peak": round(100 * btf / BF16_PEAK_TFLOPS, 1), "algorithmic_flop": bfl}
+        log(f"[bench] backward dX {name} {bms:.3f} ms, {btf:.1f} TFLOP/s")
+        del dx
         if fmt == 1:
             # W4A4: the same x quantized to MXFP4 (outside the timed region), then
             # the block-scaled fp4 product against the same MXFP4 weight

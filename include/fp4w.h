@@ -212,6 +212,26 @@ int fp4w_linear_backward_dx(int fmt, const void *dy_bf16, int64_t m, int64_t n,
                             void *stream);
 
 /*
+ * fp4w_scale_delta_grad -- the Scale-QLoRA training gradient of the block-scale
+ * deltas (Scale-QLoRA page: block-scale corrections trained with the codes
+ * frozen, rounded to the scale grid in every forward; the rounding is passed
+ * straight through): for y = x deq(W)^T with W's block scales shifted by deltas
+ * in the decoded scale domain (before any tensor scale, as fp4w_merge_scales
+ * takes them),
+ *   grad[n, b] = s_t * sum_{k in block b} e2m1(q[n, k]) * (dy^T x)[n, k]
+ * with s_t the NVFP4 tensor scale (1 for MXFP4); dy^T x is accumulated in fp32
+ * and never stored.
+ *   dy_bf16  (m, n) bf16, the gradient of y;  x_bf16 (m, k) bf16, the input
+ *   codes    (n, k/2) of W, as fp4w_quantize writes them; tensor_scale (NVFP4)
+ *   grad     (n, k/16) fp32 (NVFP4) or (n, k/32) (MXFP4), fully written
+ * n % 8 == 0 and k % 32 == 0 (else FP4W_ERR_SHAPE); dy, x and codes 16-byte
+ * aligned, grad 4-byte aligned.  m == 0 writes zeros.  One launch on `stream`.
+ */
+int fp4w_scale_delta_grad(int fmt, const void *dy_bf16, const void *x_bf16,
+                          int64_t m, int64_t n, int64_t k, const uint8_t *codes,
+                          const float *tensor_scale, float *grad, void *stream);
+
+/*
  * fp4w_grouped_linear -- the W4A16 linear over the experts of a mixture of
  * experts (QATFactory page: dense and MoE models; Nemotron page: 30B-A3B base).
  * For every expert e and every row q in [expert_offsets[e], expert_offsets[e+1]):

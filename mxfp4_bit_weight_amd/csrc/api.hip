@@ -32,7 +32,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP4W_OK : FP4W_ERR_HIP; 
 
 extern "C" {
 
-int fp4w_version(void) { return 6; }
+int fp4w_version(void) { return 7; }
 
 const char* fp4w_status_string(int status) {
   switch (status) {
@@ -150,6 +150,24 @@ int fp4w_linear_backward_dx(int fmt, const void* dy_bf16, int64_t m, int64_t n, 
     return FP4W_ERR_ALIGN;
   return hip_status(fp4w::launch_backward_dx(fmt, dy_bf16, m, n, codes, scales, tensor_scale, k, dx_bf16,
                                              as_stream(stream)));
+}
+
+int fp4w_scale_delta_grad(int fmt, const void* dy_bf16, const void* x_bf16, int64_t m, int64_t n, int64_t k,
+                          const uint8_t* codes, const float* tensor_scale, float* grad, void* stream) {
+  if (!valid_fmt(fmt)) return FP4W_ERR_FORMAT;
+  if (m < 0 || n < 0 || k < 0) return FP4W_ERR_ARG;
+  int st = check_nk(n, k);
+  if (st) return st;
+  if (n % 8 != 0 || n > (int64_t)65535 * 128 || m > 0x7FFFFFFF || k > 0x7FFFFFFF) return FP4W_ERR_SHAPE;
+  if (m > 0 && (n > kMaxElems / m || k > kMaxElems / m)) return FP4W_ERR_SHAPE;
+  if (n == 0 || k == 0) return FP4W_OK;
+  if (!codes || !grad || (m > 0 && (!dy_bf16 || !x_bf16))) return FP4W_ERR_ARG;
+  if (fmt == FP4W_NVFP4 && !tensor_scale) return FP4W_ERR_ARG;
+  if (!aligned16(dy_bf16) || !aligned16(x_bf16) || !aligned16(codes) ||
+      (reinterpret_cast<uintptr_t>(grad) & 3u) != 0)
+    return FP4W_ERR_ALIGN;
+  return hip_status(fp4w::launch_delta_grad(fmt, dy_bf16, x_bf16, m, n, k, codes, tensor_scale, grad,
+                                            as_stream(stream)));
 }
 
 int fp4w_grouped_linear(int fmt, const void* x_bf16, int64_t num_tokens, const int32_t* row_index,

@@ -47,6 +47,7 @@ _ws_bytes = _sig("fp4w_linear_workspace_bytes", _sz, _i64, _i64, _i64, _int)
 _linear = _sig("fp4w_linear", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _int, _p, _p, _sz, _p)
 _w4a4 = _sig("fp4w_linear_w4a4", _int, _int, _p, _p, _i64, _i64, _p, _p, _i64, _p, _p)
 _bwd_dx = _sig("fp4w_linear_backward_dx", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p)
+_delta_grad = _sig("fp4w_scale_delta_grad", _int, _int, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p)
 _grouped = _sig("fp4w_grouped_linear", _int, _int, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p)
 _merge = _sig("fp4w_merge_scales", _int, _int, _p, _p, _i64, _p, _p, _p, _i64, _p)
 _status = _sig("fp4w_status_string", ctypes.c_char_p, _int)
@@ -55,7 +56,8 @@ _debug_lora_wait = _sig("fp4w_debug_lora_wait", _i64, _i64)
 
 EXPORTED = ["fp4w_quantize", "fp4w_dequantize", "fp4w_linear_workspace_bytes", "fp4w_linear",
             "fp4w_grouped_linear", "fp4w_merge_scales", "fp4w_status_string", "fp4w_version",
-            "fp4w_debug_lora_wait", "fp4w_fake_quant", "fp4w_linear_w4a4", "fp4w_linear_backward_dx"]
+            "fp4w_debug_lora_wait", "fp4w_fake_quant", "fp4w_linear_w4a4", "fp4w_linear_backward_dx",
+            "fp4w_scale_delta_grad"]
 
 
 class Fp4wError(RuntimeError):
@@ -250,6 +252,21 @@ def linear_backward_dx(dy: torch.Tensor, q: QWeight, out: Optional[torch.Tensor]
     _check(_bwd_dx(q.fmt, _ptr(dy), m, n, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.k, _ptr(dx),
                    _stream(dy.device)), "fp4w_linear_backward_dx")
     return dx
+
+
+def scale_delta_grad(dy: torch.Tensor, x: torch.Tensor, q: QWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4w_scale_delta_grad: the gradient of the Scale-QLoRA block-scale deltas,
+    fp32 (n, k / blk), from the output gradient dy (m, n) and the input x (m, k)."""
+    _need(dy, torch.bfloat16, "dy")
+    _need(x, torch.bfloat16, "x")
+    m, n = dy.shape
+    if n != q.n or x.shape != (m, q.k):
+        raise ValueError("dy must be (m, n) and x (m, k) for the weight (n, k)")
+    g = out if out is not None else torch.empty((q.n, q.k // BLOCK[q.fmt]), dtype=torch.float32, device=dy.device)
+    _need(g, torch.float32, "out")
+    _check(_delta_grad(q.fmt, _ptr(dy), _ptr(x), m, n, q.k, _ptr(q.codes), _ptr(q.tensor_scale), _ptr(g),
+                       _stream(dy.device)), "fp4w_scale_delta_grad")
+    return g
 
 
 def grouped_linear(x: torch.Tensor, row_index: torch.Tensor, expert_offsets: torch.Tensor, fmt: int,

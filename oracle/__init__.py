@@ -254,6 +254,25 @@ def linear_backward_dx(fmt: int, dy, codes, scales, tensor_scale):
     return dyf @ dequantize(fmt, codes, scales, tensor_scale, "f64")
 
 
+def scale_delta_grad(fmt: int, dy, x, codes, tensor_scale):
+    """Scale-QLoRA delta gradient (Scale-QLoRA page: block-scale corrections in
+    the decoded scale domain, rounded to the grid in every forward, the rounding
+    passed straight through): g[n, b] = s_t * sum_{k in b} e2m1(q[n, k]) *
+    (dY^T X)[n, k], in binary64.  e2m1(q) is the oracle's decoding of the codes
+    under the unit block scale (E4M3 0x38, E8M0 127)."""
+    dy = _c(np.atleast_2d(dy), np.uint16)
+    x = _c(np.atleast_2d(x), np.uint16)
+    codes = _c(codes, np.uint8)
+    n, k = codes.shape[0], codes.shape[1] * 2
+    blk = BLOCK[fmt]
+    unit = np.full((n, k // blk), 0x38 if fmt == NVFP4 else 127, np.uint8)
+    e2m1 = dequantize(fmt, codes, unit, 1.0, "f64")
+    f = lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    gmat = f(dy).T @ f(x)
+    ts = float(np.float32(tensor_scale)) if fmt == NVFP4 else 1.0
+    return ts * (e2m1 * gmat).reshape(n, k // blk, blk).sum(axis=2)
+
+
 def linear_w4a4(x_codes, x_scales, codes, scales):
     """W4A4 MXFP4 (QATFactory page, section on the strategies NVFP4 and MXFP4
     need: weights and activations both 4-bit): y (m, n) in binary64 =

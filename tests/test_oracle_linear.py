@@ -328,3 +328,34 @@ def test_backward_dx_one_hot_rows(fmt):
     assert np.array_equal(dx[0], deq[5])
     assert not dx[1].any()
     assert np.array_equal(dx[2], -2.0 * deq[23])
+
+
+@pytest.mark.parametrize("fmt", [O.NVFP4, O.MXFP4])
+def test_delta_grad_adjoint_of_linear(fmt):
+    # sum_b dec(S_b) g_b = <dY, x deq_S(W)^T> for any block scales S: the delta
+    # gradient contracted with a scale field is the forward (independent C oracle)
+    # run with those scales -- pins codes, block indexing, transposition and s_t
+    w, x, _, _ = W.linear_inputs(25, 32, 128, 9)
+    codes, scales, st = O.quantize(fmt, w)
+    dy = W.to_bf16_bits(np.random.default_rng(26).standard_normal((9, 32)))
+    g = O.scale_delta_grad(fmt, dy, x, codes, st)
+    assert g.shape == scales.shape
+    dec = O.dequantize(fmt, np.full((32, 64), 0x22, np.uint8), scales, 1.0, "f64")[:, ::O.BLOCK[fmt]]
+    lhs = float(np.sum(dec * g))                     # 0x22: both nibbles 1.0, so dec = block scale values
+    rhs = float(np.sum(_f64(dy) * O.linear(fmt, x, codes, scales, st)))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(rhs))
+
+
+@pytest.mark.parametrize("fmt", [O.NVFP4, O.MXFP4])
+def test_delta_grad_one_hot(fmt):
+    w, _, _, _ = W.linear_inputs(27, 16, 64, 1)
+    codes, _, st = O.quantize(fmt, w)
+    dy = np.zeros((3, 16), np.uint16)
+    x = np.zeros((3, 64), np.uint16)
+    dy[1, 5] = 0x3F80                                # dY[1, 5] = 1
+    x[1, 37] = 0x4000                                # x[1, 37] = 2: G = 2 e_{5, 37}
+    g = O.scale_delta_grad(fmt, dy, x, codes, st)
+    nib = (int(codes[5, 37 // 2]) >> 4) & 15         # odd k: high nibble
+    want = np.zeros_like(g)
+    want[5, 37 // O.BLOCK[fmt]] = (float(np.float32(st)) if fmt == O.NVFP4 else 1.0) * 2.0 * O.e2m1_decode(nib)
+    assert np.array_equal(g, want)

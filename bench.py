@@ -8,8 +8,8 @@ is the step's algorithmic bytes over its time (GB/s).  The JSON line also holds
 the roofline of the decode kernel (HIP events around a graph of back-to-back
 launches of it), the CPU oracle timed on a bounded sample, and the other
 hot-path rows (M = 8, MXFP4, the 16384-row prefill GEMM, its backward dX
-through the frozen base and its W4A4 MXFP4 form, quantize, merge, dequantize,
-grouped MoE).
+through the frozen base, its Scale-QLoRA delta gradient and its W4A4 MXFP4
+form, quantize, merge, dequantize, grouped MoE).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-rows]
        python bench.py --roofline-only   (the decode kernel's launches and a plain
@@ -303,7 +303,15 @@ def gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights):
         rows[f"backward_dx_{name}"] = {"m": mrows, "n": n, "k": k, "ms": round(bms, 3), "TFLOP/s": round(btf, 1),
                                        "pct_bf16_peak": round(100 * btf / BF16_PEAK_TFLOPS, 1), "algorithmic_flop": bfl}
         log(f"[bench] backward dX {name} {bms:.3f} ms, {btf:.1f} TFLOP/s")
-        del dx
+        # the Scale-QLoRA delta gradient of the same layer: dY = y, X = x
+        gout = torch.empty((n, k // (16 if fmt == 0 else 32)), dtype=torch.float32, device=dev)
+        dms, _ = time_loop(lambda i: fp4w.scale_delta_grad(y, x, q, out=gout), 10, 10)
+        dtf = bfl / (dms * 1e-3) / 1e12
+        rows[f"scale_delta_grad_{name}"] = {"m": mrows, "n": n, "k": k, "ms": round(dms, 3), "TFLOP/s": round(dtf, 1),
+                                            "pct_bf16_peak": round(100 * dtf / BF16_PEAK_TFLOPS, 1),
+                                            "algorithmic_flop": bfl}
+        log(f"[bench] scale delta grad {name} {dms:.3f} ms, {dtf:.1f} TFLOP/s")
+        del dx, gout
         if fmt == 1:
             # W4A4: the same x quantized to MXFP4 (outside the timed region), then
             # the block-scaled fp4 product against the same MXFP4 weight

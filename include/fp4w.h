@@ -232,6 +232,31 @@ int fp4w_scale_delta_grad(int fmt, const void *dy_bf16, const void *x_bf16,
                           const float *tensor_scale, float *grad, void *stream);
 
 /*
+ * fp4w_aqn_rmsnorm -- the noisy RMSNorm ahead of the projections (adaptive
+ * noise for exploration in the RL fine-tuning of the Telegram post, "Metod":
+ * noise applied in the RMS norm before the projections, which is multiplicative
+ * noise on their weights).  Per row of x (m, k):
+ *   y[k] = bf16( x[k] / sqrt(mean(x^2) + eps) * gamma[k] * (1 + sigma * noise[k]) )
+ * computed in fp32, rounded once (RNE).  The linear that consumes y sees its
+ * weight columns scaled by (1 + sigma * noise[k]).
+ *   x_bf16, y_bf16 (m, k) bf16 (may be the same buffer); gamma_bf16 (k) bf16;
+ *   noise (k) fp32, drawn by the caller each step (standard normal);
+ *   sigma from fp4w_aqn_sigma; eps the norm's epsilon
+ * k % 8 == 0 (else FP4W_ERR_SHAPE); all pointers 16-byte aligned.
+ */
+int fp4w_aqn_rmsnorm(const void *x_bf16, int64_t m, int64_t k, const void *gamma_bf16,
+                     const float *noise, float sigma, float eps, void *y_bf16, void *stream);
+
+/*
+ * fp4w_aqn_sigma -- the noise scale at `step` of `total_steps` on the
+ * exponential schedule from sigma_max down to sigma_min (the post: 1e-2 to
+ * 5e-4, exponential decay doing slightly better than other schedules):
+ * sigma_max * (sigma_min / sigma_max)^(step / total_steps), clamped to the ends;
+ * 0 for non-positive sigmas.  Host function.
+ */
+double fp4w_aqn_sigma(int64_t step, int64_t total_steps, double sigma_max, double sigma_min);
+
+/*
  * fp4w_grouped_linear -- the W4A16 linear over the experts of a mixture of
  * experts (QATFactory page: dense and MoE models; Nemotron page: 30B-A3B base).
  * For every expert e and every row q in [expert_offsets[e], expert_offsets[e+1]):

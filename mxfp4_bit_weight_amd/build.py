@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp4w.so")
-SOURCES = ["api.hip", "quantize.hip", "dequantize.hip", "merge.hip", "linear.hip", "decode.hip", "decode_xs.hip", "grouped.hip", "gemm.hip", "a4w4.hip", "backward.hip", "delta_grad.hip"]
+SOURCES = ["api.hip", "quantize.hip", "dequantize.hip", "merge.hip", "linear.hip", "decode.hip", "decode_xs.hip", "grouped.hip", "gemm.hip", "a4w4.hip", "backward.hip", "delta_grad.hip", "aqn.hip"]
 ARCH = "gfx950"
 
 

@@ -3,6 +3,8 @@
 // synchronizes; every kernel goes on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "../../include/fp4w.h"
 #include "fp4w_internal.hpp"
 
@@ -32,7 +34,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP4W_OK : FP4W_ERR_HIP; 
 
 extern "C" {
 
-int fp4w_version(void) { return 7; }
+int fp4w_version(void) { return 8; }
 
 const char* fp4w_status_string(int status) {
   switch (status) {
@@ -168,6 +170,23 @@ int fp4w_scale_delta_grad(int fmt, const void* dy_bf16, const void* x_bf16, int6
     return FP4W_ERR_ALIGN;
   return hip_status(fp4w::launch_delta_grad(fmt, dy_bf16, x_bf16, m, n, k, codes, tensor_scale, grad,
                                             as_stream(stream)));
+}
+
+double fp4w_aqn_sigma(int64_t step, int64_t total_steps, double sigma_max, double sigma_min) {
+  if (!(sigma_max > 0.0) || !(sigma_min > 0.0)) return 0.0;
+  if (total_steps <= 0 || step >= total_steps) return sigma_min;
+  if (step <= 0) return sigma_max;
+  return sigma_max * std::pow(sigma_min / sigma_max, (double)step / (double)total_steps);
+}
+
+int fp4w_aqn_rmsnorm(const void* x_bf16, int64_t m, int64_t k, const void* gamma_bf16, const float* noise,
+                     float sigma, float eps, void* y_bf16, void* stream) {
+  if (m < 0 || k < 0) return FP4W_ERR_ARG;
+  if (k % 8 != 0 || m > 0x7FFFFFFF || (m > 0 && k > kMaxElems / m)) return FP4W_ERR_SHAPE;
+  if (m == 0 || k == 0) return FP4W_OK;
+  if (!x_bf16 || !gamma_bf16 || !noise || !y_bf16) return FP4W_ERR_ARG;
+  if (!aligned16(x_bf16) || !aligned16(gamma_bf16) || !aligned16(noise) || !aligned16(y_bf16)) return FP4W_ERR_ALIGN;
+  return hip_status(fp4w::launch_aqn_rmsnorm(x_bf16, m, k, gamma_bf16, noise, sigma, eps, y_bf16, as_stream(stream)));
 }
 
 int fp4w_grouped_linear(int fmt, const void* x_bf16, int64_t num_tokens, const int32_t* row_index,

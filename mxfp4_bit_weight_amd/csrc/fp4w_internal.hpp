@@ -122,6 +122,10 @@ hipError_t launch_backward_dx(int fmt, const void* dy, int64_t m, int64_t n, con
 hipError_t launch_delta_grad(int fmt, const void* dy, const void* x, int64_t m, int64_t n, int64_t k,
                              const uint8_t* codes, const float* tensor_scale, float* grad, hipStream_t stream);
 
+// Noisy RMSNorm ahead of the projections (aqn.hip): k % 8 == 0.
+hipError_t launch_aqn_rmsnorm(const void* x, int64_t m, int64_t k, const void* gamma, const float* noise,
+                              float sigma, float eps, void* y, hipStream_t stream);
+
 // Grouped linear on the x-in-registers kernel (decode_xs.hip): K in one span.
 bool grouped_xs_supports(int64_t num_tokens, int64_t n, int64_t k);
 hipError_t launch_grouped_xs(int fmt, const void* x, int64_t num_tokens, const int32_t* row_index,

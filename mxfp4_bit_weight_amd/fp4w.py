@@ -48,6 +48,8 @@ _linear = _sig("fp4w_linear", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, 
 _w4a4 = _sig("fp4w_linear_w4a4", _int, _int, _p, _p, _i64, _i64, _p, _p, _i64, _p, _p)
 _bwd_dx = _sig("fp4w_linear_backward_dx", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p)
 _delta_grad = _sig("fp4w_scale_delta_grad", _int, _int, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p)
+_aqn = _sig("fp4w_aqn_rmsnorm", _int, _p, _i64, _i64, _p, _p, ctypes.c_float, ctypes.c_float, _p, _p)
+_aqn_sigma = _sig("fp4w_aqn_sigma", ctypes.c_double, _i64, _i64, ctypes.c_double, ctypes.c_double)
 _grouped = _sig("fp4w_grouped_linear", _int, _int, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p)
 _merge = _sig("fp4w_merge_scales", _int, _int, _p, _p, _i64, _p, _p, _p, _i64, _p)
 _status = _sig("fp4w_status_string", ctypes.c_char_p, _int)
@@ -57,7 +59,7 @@ _debug_lora_wait = _sig("fp4w_debug_lora_wait", _i64, _i64)
 EXPORTED = ["fp4w_quantize", "fp4w_dequantize", "fp4w_linear_workspace_bytes", "fp4w_linear",
             "fp4w_grouped_linear", "fp4w_merge_scales", "fp4w_status_string", "fp4w_version",
             "fp4w_debug_lora_wait", "fp4w_fake_quant", "fp4w_linear_w4a4", "fp4w_linear_backward_dx",
-            "fp4w_scale_delta_grad"]
+            "fp4w_scale_delta_grad", "fp4w_aqn_rmsnorm", "fp4w_aqn_sigma"]
 
 
 class Fp4wError(RuntimeError):
@@ -267,6 +269,27 @@ def scale_delta_grad(dy: torch.Tensor, x: torch.Tensor, q: QWeight, out: Optiona
     _check(_delta_grad(q.fmt, _ptr(dy), _ptr(x), m, n, q.k, _ptr(q.codes), _ptr(q.tensor_scale), _ptr(g),
                        _stream(dy.device)), "fp4w_scale_delta_grad")
     return g
+
+
+def aqn_sigma(step: int, total_steps: int, sigma_max: float = 1e-2, sigma_min: float = 5e-4) -> float:
+    """fp4w_aqn_sigma: the exponentially decaying noise scale."""
+    return float(_aqn_sigma(step, total_steps, sigma_max, sigma_min))
+
+
+def aqn_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, noise: torch.Tensor, sigma: float, eps: float = 1e-6,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4w_aqn_rmsnorm: RMSNorm with the per-channel gain gamma * (1 + sigma * noise)."""
+    _need(x, torch.bfloat16, "x")
+    _need(gamma, torch.bfloat16, "gamma")
+    _need(noise, torch.float32, "noise")
+    m, k = x.shape
+    if gamma.numel() != k or noise.numel() != k:
+        raise ValueError("gamma and noise must have k elements")
+    y = out if out is not None else torch.empty_like(x)
+    _need(y, torch.bfloat16, "out")
+    _check(_aqn(_ptr(x), m, k, _ptr(gamma), _ptr(noise), float(sigma), float(eps), _ptr(y), _stream(x.device)),
+           "fp4w_aqn_rmsnorm")
+    return y
 
 
 def grouped_linear(x: torch.Tensor, row_index: torch.Tensor, expert_offsets: torch.Tensor, fmt: int,

@@ -273,6 +273,29 @@ def scale_delta_grad(fmt: int, dy, x, codes, tensor_scale):
     return ts * (e2m1 * gmat).reshape(n, k // blk, blk).sum(axis=2)
 
 
+def aqn_sigma(step: int, total_steps: int, sigma_max: float = 1e-2, sigma_min: float = 5e-4) -> float:
+    """Noise scale on the exponential schedule from sigma_max to sigma_min
+    (Telegram post, "Metod": the noise decays from 1e-2 to 5e-4 exponentially)."""
+    if total_steps <= 0 or step >= total_steps:
+        return sigma_min
+    if step <= 0:
+        return sigma_max
+    return sigma_max * (sigma_min / sigma_max) ** (step / total_steps)
+
+
+def aqn_rmsnorm(x, gamma, noise, sigma: float, eps: float):
+    """Noisy RMSNorm ahead of the projections (Telegram post, "Metod": noise in
+    the RMS norm before the projections, multiplicative on their weights), in
+    binary64: y = x / sqrt(mean(x^2) + eps) * gamma * (1 + sigma * noise); x and
+    gamma bf16 bit patterns, noise fp32; the reading of where the noise enters
+    (a factor on the gain) is stated with the kernel's."""
+    f = lambda a: (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    xf = f(np.atleast_2d(x))
+    r = 1.0 / np.sqrt((xf * xf).mean(axis=1, keepdims=True) + float(np.float32(eps)))
+    gain = f(gamma)[None, :] * (1.0 + float(np.float32(sigma)) * np.asarray(noise, np.float32).astype(np.float64))[None, :]
+    return xf * r * gain
+
+
 def linear_w4a4(x_codes, x_scales, codes, scales):
     """W4A4 MXFP4 (QATFactory page, section on the strategies NVFP4 and MXFP4
     need: weights and activations both 4-bit): y (m, n) in binary64 =

@@ -351,6 +351,26 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
     rows["decode_linear_with_lora"] = dec
     log("[bench] decode rows done")
 
+    # the noisy RMSNorm prologue (m = 1, k = 3584) alone and ahead of the gate/up
+    # decode linear (NVFP4, LoRA r = 16): two launches per call
+    d = decode[(0, "gate_up")]
+    gam = bf16(W.normal_bf16(301, W.TID_X, (d["k"],), 1.0))
+    noise = torch.from_numpy(np.random.default_rng(302).standard_normal(d["k"]).astype(np.float32)).to(dev)
+    xn = torch.empty_like(d["x1"])
+    yn = torch.empty((1, d["n"]), dtype=torch.bfloat16, device=dev)
+    sig = fp4w.aqn_sigma(100, 1000)
+    ams, _ = time_graph(lambda i: fp4w.aqn_rmsnorm(d["x1"], gam, noise, sig, 1e-6, out=xn), reps, 5)
+
+    def norm_linear(i):
+        q, a, b = d["qs"][i % len(d["qs"])]
+        fp4w.aqn_rmsnorm(d["x1"], gam, noise, sig, 1e-6, out=xn)
+        fp4w.linear(xn, q, a, b, out=yn, workspace=ws)
+    nms, _ = time_graph(norm_linear, reps, 5)
+    rows["aqn_rmsnorm_m1_k3584"] = {"us": round(ams * 1e3, 2),
+                                    "us_with_gate_up_linear_nvfp4": round(nms * 1e3, 2),
+                                    "linear_alone_us": dec["nvfp4/gate_up/M1"]["us"]}
+    log(f"[bench] noisy RMSNorm {ams * 1e3:.2f} us, with the gate/up linear {nms * 1e3:.2f} us")
+
     weights = {fmt: (*decode[(fmt, "gate_up")]["qs"][0], decode[(fmt, "gate_up")]["n"], decode[(fmt, "gate_up")]["k"])
                for fmt in (0, 1)}
     rows.update(gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights))

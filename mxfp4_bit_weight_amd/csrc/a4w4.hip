@@ -313,12 +313,10 @@ hipError_t launch_gemm_a4w4(const uint8_t* xc, const uint8_t* xs, int64_t m, int
                             const uint8_t* ws, int64_t n, void* y, hipStream_t stream) {
   if (m == 0 || n == 0) return hipSuccess;
   const int64_t tiles = ((m + A4_BM - 1) / A4_BM) * ((n + A4_BN - 1) / A4_BN);
-  static bool lds_set = false;
-  if (!lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_a4w4_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, A4_LDS);
+  static std::atomic<uint64_t> lds_done{0};
+  {
+    hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&gemm_a4w4_kernel), A4_LDS, lds_done);
     if (e != hipSuccess) return e;
-    lds_set = true;
   }
   const int flags = (n % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15u) == 0) ? 1 : 0;
   int dev = 0, cus = 0;

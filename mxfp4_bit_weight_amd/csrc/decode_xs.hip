@@ -39,6 +39,7 @@
 // partials in span order, so results never depend on scheduling.
 #include "fp4w_device.hpp"
 #include "fp4w_internal.hpp"
+#include "gemm_common.hpp"
 #include "lora_handover.hpp"
 #include "sync.hpp"
 
@@ -530,12 +531,10 @@ struct XsLaunch {
 template <int FMT, int TG, int SC, bool LORA>
 static hipError_t launch_xs_tg(dim3 grid, dim3 block, size_t lds, hipStream_t stream, const XsLaunch& a,
                                const XsConfig& c) {
-  static bool lds_set = false;
-  if (!lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_xs_kernel<FMT, TG, SC, LORA>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kXsMaxLds);
+  static std::atomic<uint64_t> lds_done{0};
+  {
+    hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&decode_xs_kernel<FMT, TG, SC, LORA>), kXsMaxLds, lds_done);
     if (e != hipSuccess) return e;
-    lds_set = true;
   }
   hipLaunchKernelGGL((decode_xs_kernel<FMT, TG, SC, LORA>), grid, block, lds, stream, a.x, a.m, a.k, a.codes, a.scales,
                      a.ts, a.n, a.la, a.lb, a.r, a.lparts, a.lsw, a.lsync, (uint64_t)(LORA ? lora_wait_ticks() : 0),
@@ -642,12 +641,10 @@ static hipError_t launch_gxs_tg(dim3 grid, dim3 block, size_t lds, hipStream_t s
                                 int64_t num_tokens, const int32_t* row_index, const int32_t* offsets,
                                 int64_t total_rows, int64_t n, int64_t k, const uint8_t* codes, const uint8_t* scales,
                                 const float* ts, uint16_t* y, int qspan, int ntiles, int G, int tg) {
-  static bool lds_set = false;
-  if (!lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_xs_kernel<FMT, TG, SC>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kXsMaxLds);
+  static std::atomic<uint64_t> lds_done{0};
+  {
+    hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&grouped_xs_kernel<FMT, TG, SC>), kXsMaxLds, lds_done);
     if (e != hipSuccess) return e;
-    lds_set = true;
   }
   hipLaunchKernelGGL((grouped_xs_kernel<FMT, TG, SC>), grid, block, lds, stream, x, num_tokens, row_index, offsets,
                      total_rows, n, k, codes, scales, ts, y, qspan, ntiles, G, tg);

@@ -434,12 +434,10 @@ static hipError_t launch_w4(const uint16_t* x, int64_t m, int64_t k, const uint8
                             const float* tensor_scale, int64_t n, const float* t, const uint16_t* lora_b, int r,
                             uint16_t* y, hipStream_t stream) {
   const int64_t tiles = ((m + W4_BM - 1) / W4_BM) * ((n + W4_BN - 1) / W4_BN);
-  static bool lds_set = false;
-  if (!lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_w4_kernel<FMT, WL>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, W4_LDS);
+  static std::atomic<uint64_t> lds_done{0};
+  {
+    hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&gemm_w4_kernel<FMT, WL>), W4_LDS, lds_done);
     if (e != hipSuccess) return e;
-    lds_set = true;
   }
   // flags: 1 = 16-byte stores of y (y 16-byte aligned, n a multiple of 8);
   // 2 = 16-byte loads of B and t (r a multiple of 8, B 16-byte aligned)

@@ -1,6 +1,9 @@
 // gemm_common.hpp -- pieces shared by the MFMA GEMM kernels (gemm.hip, a4w4.hip):
-// LDS chunk swizzles, DMA into LDS, wait counts, accumulator copies.
+// LDS chunk swizzles, DMA into LDS, wait counts, accumulator copies, and the
+// once-per-device dynamic LDS limit (also used by decode_xs.hip, linear.hip).
 #pragma once
+
+#include <atomic>
 #include "fp4w_device.hpp"
 
 namespace fp4w {
@@ -47,5 +50,19 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uin
 }
 
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+// Raise `fn`'s dynamic LDS limit to `bytes` once per device: the attribute is
+// per device, so `done` keeps one bit per device id (ids past 63 set it on every
+// call); safe to call from several host threads.
+inline hipError_t set_max_lds_once(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 }  // namespace fp4w

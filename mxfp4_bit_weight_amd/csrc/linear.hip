@@ -21,6 +21,7 @@
 // the caller's workspace and are returned to zero by that last workgroup.
 #include "fp4w_device.hpp"
 #include "fp4w_internal.hpp"
+#include "gemm_common.hpp"
 #include "skinny.hpp"
 #include "sync.hpp"
 
@@ -752,12 +753,11 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
     const bool buf = m * k * 2 < ((int64_t)1 << 31) && n * (k / 2) < ((int64_t)1 << 31);
 #define FP4W_GEMM(FMTv, BUFv)                                                                                \
   do {                                                                                                       \
-    static bool lds_set = false;                                                                             \
-    if (!lds_set) {                                                                                          \
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_gemm_kernel<FMTv, BUFv>),     \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);             \
+    static std::atomic<uint64_t> lds_done{0};                                                                \
+    {                                                                                                        \
+      hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&linear_gemm_kernel<FMTv, BUFv>),        \
+                                      (int)lds, lds_done);                                                   \
       if (e != hipSuccess) return e;                                                                         \
-      lds_set = true;                                                                                        \
     }                                                                                                        \
     hipLaunchKernelGGL((linear_gemm_kernel<FMTv, BUFv>), dim3((unsigned)tiles), dim3(G_THREADS), lds, stream, \
                        xx, m, k, codes, scales, tensor_scale, n, t, bb, has_lora ? r : 0, yy);              \

@@ -101,6 +101,17 @@ def _need(t: torch.Tensor, dtype, name):
         raise ValueError(f"{name} must be a contiguous {dtype} tensor on the GPU")
 
 
+
+def _out(out: Optional[torch.Tensor], shape, dtype, device, name="out") -> torch.Tensor:
+    """`out` checked to be a contiguous GPU tensor of exactly `shape` and `dtype`
+    (a smaller buffer would be written past its end), or a new one."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(out, dtype, name)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    return out
+
 @dataclass
 class QWeight:
     """A block-scaled 4-bit weight W (n, k): codes (n, k/2) uint8, scales
@@ -120,15 +131,29 @@ def empty_qweight(fmt: int, n: int, k: int, device) -> QWeight:
                    torch.empty(1, dtype=torch.float32, device=dev) if fmt == NVFP4 else None, n, k)
 
 
+def _check_frozen(frozen: "QWeight", fmt: int, n: int, k: int, device) -> None:
+    """Frozen scales (and NVFP4 tensor scale) must match W's shape: the kernels read them whole."""
+    _out(frozen.scales, (n, k // BLOCK[fmt]), torch.uint8, device, "frozen.scales")
+    if fmt == NVFP4:
+        _out(frozen.tensor_scale, (1,), torch.float32, device, "frozen.tensor_scale")
+
+
 def quantize(w: torch.Tensor, fmt: int = NVFP4, out: Optional[QWeight] = None,
              frozen: Optional[QWeight] = None) -> QWeight:
     """fp4w_quantize.  ``frozen``: reuse its scales (and tensor scale) and compute codes only."""
     _need(w, torch.bfloat16, "w")
     n, k = w.shape
     q = out if out is not None else empty_qweight(fmt, n, k, w.device)
+    if out is not None:
+        _out(out.codes, (n, k // 2), torch.uint8, w.device, "out.codes")
+        if frozen is None:
+            _out(out.scales, (n, k // BLOCK[fmt]), torch.uint8, w.device, "out.scales")
+            if fmt == NVFP4:
+                _out(out.tensor_scale, (1,), torch.float32, w.device, "out.tensor_scale")
     flags = 0
     if frozen is not None:
         flags = FROZEN_SCALES
+        _check_frozen(frozen, fmt, n, k, w.device)
         q.scales, q.tensor_scale = frozen.scales, frozen.tensor_scale
     _check(_quantize(fmt, _ptr(w), n, k, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), flags,
                      _stream(w.device)), "fp4w_quantize")
@@ -142,11 +167,11 @@ def fake_quant(w: torch.Tensor, fmt: int = NVFP4, frozen: Optional[QWeight] = No
     NVFP4 tensor scale) instead of computing them."""
     _need(w, torch.bfloat16, "w")
     n, k = w.shape
-    y = out if out is not None else torch.empty((n, k), dtype=torch.bfloat16, device=w.device)
-    _need(y, torch.bfloat16, "out")
+    y = _out(out, (n, k), torch.bfloat16, w.device)
     flags = 0
     if frozen is not None:
         flags = FROZEN_SCALES
+        _check_frozen(frozen, fmt, n, k, w.device)
         scales, ts = frozen.scales, frozen.tensor_scale
     else:
         scales = torch.empty((n, k // BLOCK[fmt]), dtype=torch.uint8, device=w.device)
@@ -174,7 +199,7 @@ def dequantize(q: QWeight, dtype=torch.bfloat16, out: Optional[torch.Tensor] = N
     """fp4w_dequantize: the exact decoded values rounded once to bf16 or fp32."""
     if dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("dtype must be bfloat16 or float32")
-    y = out if out is not None else torch.empty((q.n, q.k), dtype=dtype, device=q.codes.device)
+    y = _out(out, (q.n, q.k), dtype, q.codes.device)
     _check(_dequantize(q.fmt, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.n, q.k, _ptr(y),
                        OUT_FP32 if dtype == torch.float32 else 0, _stream(q.codes.device)), "fp4w_dequantize")
     return y
@@ -213,7 +238,7 @@ def linear(x: torch.Tensor, q: QWeight, lora_a: Optional[torch.Tensor] = None,
         r = lora_a.shape[0]
         if lora_a.shape != (r, k) or lora_b.shape != (q.n, r):
             raise ValueError("lora_a must be (r, k) and lora_b (n, r)")
-    y = out if out is not None else torch.empty((m, q.n), dtype=torch.bfloat16, device=x.device)
+    y = _out(out, (m, q.n), torch.bfloat16, x.device)
     nbytes = linear_workspace_bytes(m, q.n, k, r)
     ws = workspace if workspace is not None else workspace_for(x.device, nbytes)
     _check(_linear(q.fmt, _ptr(x), m, k, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.n,
@@ -229,8 +254,7 @@ def linear_w4a4(xq: QWeight, q: QWeight, out: Optional[torch.Tensor] = None) -> 
         raise ValueError("linear_w4a4 takes MXFP4 activations and weights")
     if xq.k != q.k:
         raise ValueError(f"x has k={xq.k}, the weight k={q.k}")
-    y = out if out is not None else torch.empty((xq.n, q.n), dtype=torch.bfloat16, device=q.codes.device)
-    _need(y, torch.bfloat16, "out")
+    y = _out(out, (xq.n, q.n), torch.bfloat16, q.codes.device)
     _check(_w4a4(MXFP4, _ptr(xq.codes), _ptr(xq.scales), xq.n, xq.k, _ptr(q.codes), _ptr(q.scales), q.n,
                  _ptr(y), _stream(y.device)), "fp4w_linear_w4a4")
     return y
@@ -249,8 +273,7 @@ def linear_backward_dx(dy: torch.Tensor, q: QWeight, out: Optional[torch.Tensor]
     m, n = dy.shape
     if n != q.n:
         raise ValueError(f"dy has n={n}, the weight n={q.n}")
-    dx = out if out is not None else torch.empty((m, q.k), dtype=torch.bfloat16, device=dy.device)
-    _need(dx, torch.bfloat16, "out")
+    dx = _out(out, (m, q.k), torch.bfloat16, dy.device)
     _check(_bwd_dx(q.fmt, _ptr(dy), m, n, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.k, _ptr(dx),
                    _stream(dy.device)), "fp4w_linear_backward_dx")
     return dx
@@ -264,8 +287,7 @@ def scale_delta_grad(dy: torch.Tensor, x: torch.Tensor, q: QWeight, out: Optiona
     m, n = dy.shape
     if n != q.n or x.shape != (m, q.k):
         raise ValueError("dy must be (m, n) and x (m, k) for the weight (n, k)")
-    g = out if out is not None else torch.empty((q.n, q.k // BLOCK[q.fmt]), dtype=torch.float32, device=dy.device)
-    _need(g, torch.float32, "out")
+    g = _out(out, (q.n, q.k // BLOCK[q.fmt]), torch.float32, dy.device)
     _check(_delta_grad(q.fmt, _ptr(dy), _ptr(x), m, n, q.k, _ptr(q.codes), _ptr(q.tensor_scale), _ptr(g),
                        _stream(dy.device)), "fp4w_scale_delta_grad")
     return g
@@ -285,8 +307,7 @@ def aqn_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, noise: torch.Tensor, sigma
     m, k = x.shape
     if gamma.numel() != k or noise.numel() != k:
         raise ValueError("gamma and noise must have k elements")
-    y = out if out is not None else torch.empty_like(x)
-    _need(y, torch.bfloat16, "out")
+    y = _out(out, (m, k), torch.bfloat16, x.device)
     _check(_aqn(_ptr(x), m, k, _ptr(gamma), _ptr(noise), float(sigma), float(eps), _ptr(y), _stream(x.device)),
            "fp4w_aqn_rmsnorm")
     return y
@@ -302,7 +323,7 @@ def grouped_linear(x: torch.Tensor, row_index: torch.Tensor, expert_offsets: tor
     e, n, kh = codes.shape
     k = kh * 2
     total = row_index.numel()
-    y = out if out is not None else torch.empty((total, n), dtype=torch.bfloat16, device=x.device)
+    y = _out(out, (total, n), torch.bfloat16, x.device)
     _check(_grouped(fmt, _ptr(x), x.shape[0], _ptr(row_index), _ptr(expert_offsets), e, total, n, k,
                     _ptr(codes), _ptr(scales), _ptr(tensor_scales), _ptr(y), _stream(x.device)),
            "fp4w_grouped_linear")

@@ -143,3 +143,26 @@ def test_w4a4_more_tiles_than_cus(fp4w):
 def test_w4a4_full_size_prefill(fp4w):
     # Qwen-2.5-7B gate/up at 16384 tokens
     _sampled(fp4w, 16384, 18944, 3584, 78, "prefill gate/up")
+
+
+def test_binding_rejects_wrong_output_shapes(fp4w):
+    # a wrong-sized output or frozen-scale buffer is refused before any launch
+    m, n, k = 64, 32, 256
+    xc, xs, wc, ws = _inputs(3, m, n, k)
+    xq, q = _q_dev(fp4w, xc, xs), _q_dev(fp4w, wc, ws)
+    with pytest.raises(ValueError):
+        fp4w.linear_w4a4(xq, q, out=torch.empty((m, n - 1), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        fp4w.linear_backward_dx(torch.zeros((m, n), dtype=torch.bfloat16, device=DEV), q,
+                                out=torch.empty((m - 1, k), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        fp4w.scale_delta_grad(torch.zeros((m, n), dtype=torch.bfloat16, device=DEV),
+                              torch.zeros((m, k), dtype=torch.bfloat16, device=DEV), q,
+                              out=torch.empty((n, k // 16), dtype=torch.float32, device=DEV))
+    w = torch.zeros((n, k), dtype=torch.bfloat16, device=DEV)
+    bad = fp4w.QWeight(1, None, torch.zeros((n, k // 32 - 1), dtype=torch.uint8, device=DEV), None, n, k)
+    with pytest.raises(ValueError):
+        fp4w.quantize(w, 1, frozen=bad)
+    with pytest.raises(ValueError):
+        fp4w.fake_quant(w, 1, frozen=bad)
+    torch.cuda.synchronize()

@@ -127,3 +127,29 @@ def test_w4a4_validation_without_launch(lib):
     assert f(1, _fake(A), _fake(A + 2), 4, 128, _fake(A), _fake(A), 4, _fake(A), None) == -3  # scales
     assert f(1, _fake(A), _fake(A), 4, 128, _fake(A), _fake(A), 4, _fake(A + 1), None) == -3  # y
     assert f(1, None, None, 0, 128, None, None, 4, None, None) == 0                          # empty
+
+
+def test_backward_delta_aqn_validation_without_launch(lib):
+    A = 0x10000
+    f = lib._bwd_dx
+    assert f(7, _fake(A), 4, 8, _fake(A), _fake(A), _fake(A), 32, _fake(A), None) == -4     # format
+    assert f(0, _fake(A), -1, 8, _fake(A), _fake(A), _fake(A), 32, _fake(A), None) == -1    # negative
+    assert f(0, _fake(A), 4, 12, _fake(A), _fake(A), _fake(A), 32, _fake(A), None) == -2    # n % 8
+    assert f(0, _fake(A), 4, 8, _fake(A), _fake(A), _fake(A), 48, _fake(A), None) == -2    # k % 32
+    assert f(0, _fake(A), 4, 8, _fake(A), _fake(A), None, 32, _fake(A), None) == -1        # NVFP4 tensor scale
+    assert f(1, _fake(A + 8), 4, 8, _fake(A), _fake(A), None, 32, _fake(A), None) == -3    # dy alignment
+    assert f(1, _fake(A), 4, 8, _fake(A), _fake(A), None, 32, _fake(A + 4), None) == -3    # dx alignment
+    assert f(1, None, 0, 8, None, None, None, 32, None, None) == 0                          # m = 0
+    g = lib._delta_grad
+    assert g(7, _fake(A), _fake(A), 4, 8, 32, _fake(A), _fake(A), _fake(A), None) == -4
+    assert g(0, _fake(A), _fake(A), 4, 12, 32, _fake(A), _fake(A), _fake(A), None) == -2   # n % 8
+    assert g(0, _fake(A), _fake(A), 4, 8, 40, _fake(A), _fake(A), _fake(A), None) == -2    # k % 32
+    assert g(1, None, _fake(A), 4, 8, 32, _fake(A), None, _fake(A), None) == -1            # dy null, m > 0
+    assert g(1, _fake(A), _fake(A), 4, 8, 32, _fake(A), None, _fake(A + 2), None) == -3    # grad alignment
+    assert g(1, None, None, 4, 0, 32, None, None, None, None) == 0                          # n = 0
+    a = lib._aqn
+    assert a(_fake(A), 4, 12, _fake(A), _fake(A), 0.01, 1e-6, _fake(A), None) == -2       # k % 8
+    assert a(_fake(A), -1, 16, _fake(A), _fake(A), 0.01, 1e-6, _fake(A), None) == -1
+    assert a(_fake(A), 4, 16, _fake(A), None, 0.01, 1e-6, _fake(A), None) == -1            # noise null
+    assert a(_fake(A), 4, 16, _fake(A), _fake(A + 4), 0.01, 1e-6, _fake(A), None) == -3    # noise alignment
+    assert a(None, 0, 16, None, None, 0.01, 1e-6, None, None) == 0                          # m = 0

@@ -99,29 +99,55 @@ int64_t fp4w_debug_lora_wait(int64_t ticks) {
   return ticks < 0 ? fp4w::lora_wait_ticks() : fp4w::set_lora_wait_ticks(ticks);
 }
 
-int fp4w_linear(int fmt, const void* x_bf16, int64_t m, int64_t k, const uint8_t* codes, const uint8_t* scales,
-                const float* tensor_scale, int64_t n, const void* lora_a, const void* lora_b, int r, void* y_bf16,
-                void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host validation shared by fp4w_linear and fp4w_linear_noalloc: arguments,
+// shapes and alignment, then the plan (kernel shape and workspace layout).
+// FP4W_OK with *nothing = true when there is no work.
+int linear_check(int fmt, const void* x_bf16, int64_t m, int64_t k, const uint8_t* codes, const uint8_t* scales,
+                 const float* tensor_scale, int64_t n, const void* lora_a, const void* lora_b, int r, void* y_bf16,
+                 bool* nothing, bool* lora, fp4w::LinearPlan* plan) {
+  *nothing = false;
   if (!valid_fmt(fmt)) return FP4W_ERR_FORMAT;
   if (m < 0 || n < 0 || k < 0 || r < 0) return FP4W_ERR_ARG;
   int st = check_nk(n, k);
   if (st) return st;
   if (r > FP4W_MAX_LORA_RANK) return FP4W_ERR_SHAPE;
   if (m > 0 && k > 0 && m > kMaxElems / k) return FP4W_ERR_SHAPE;
-  if (m == 0 || n == 0) return FP4W_OK;
+  if (m == 0 || n == 0) {
+    *nothing = true;
+    return FP4W_OK;
+  }
   if (!x_bf16 || !y_bf16 || (k > 0 && (!codes || !scales))) return FP4W_ERR_ARG;
   if (fmt == FP4W_NVFP4 && !tensor_scale) return FP4W_ERR_ARG;
-  const bool lora = r > 0 && (lora_a || lora_b);
-  if (lora && (!lora_a || !lora_b)) return FP4W_ERR_ARG;
+  *lora = r > 0 && (lora_a || lora_b);
+  if (*lora && (!lora_a || !lora_b)) return FP4W_ERR_ARG;
   if (!aligned16(x_bf16) || !aligned16(codes) || !aligned2(y_bf16)) return FP4W_ERR_ALIGN;
   if (fmt == FP4W_NVFP4 && !aligned2(scales)) return FP4W_ERR_ALIGN;
-  if (lora && (!aligned16(lora_a) || !aligned2(lora_b))) return FP4W_ERR_ALIGN;
-  const int rr = lora ? r : 0;
-  const fp4w::LinearPlan plan = fp4w::plan_linear(m, n, k, rr);
+  if (*lora && (!aligned16(lora_a) || !aligned2(lora_b))) return FP4W_ERR_ALIGN;
+  *plan = fp4w::plan_linear(m, n, k, *lora ? r : 0);
+  return FP4W_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4w_linear(int fmt, const void* x_bf16, int64_t m, int64_t k, const uint8_t* codes, const uint8_t* scales,
+                const float* tensor_scale, int64_t n, const void* lora_a, const void* lora_b, int r, void* y_bf16,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  bool nothing = false, lora = false;
+  fp4w::LinearPlan plan{};
+  int st = linear_check(fmt, x_bf16, m, k, codes, scales, tensor_scale, n, lora_a, lora_b, r, y_bf16, &nothing,
+                        &lora, &plan);
+  if (st || nothing) return st;
   if (!workspace || workspace_bytes < plan.bytes) return FP4W_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP4W_ERR_ALIGN;
   return hip_status(fp4w::launch_linear(fmt, x_bf16, m, k, codes, scales, tensor_scale, n, lora ? lora_a : nullptr,
-                                        lora ? lora_b : nullptr, rr, y_bf16, workspace, plan, as_stream(stream)));
+                                        lora ? lora_b : nullptr, lora ? r : 0, y_bf16, workspace, plan,
+                                        as_stream(stream)));
 }
 
 int fp4w_linear_w4a4(int fmt, const uint8_t* x_codes, const uint8_t* x_scales, int64_t m, int64_t k,

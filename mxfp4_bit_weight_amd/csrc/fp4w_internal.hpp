@@ -99,7 +99,7 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
                          const void* lora_b, int r, void* y, void* workspace, const LinearPlan& plan,
                          hipStream_t stream);
 
-// The m > 16 GEMM with W decoded in registers (gemm.hip): K a multiple of 256,
+// The m > 16 GEMM with W decoded in registers (gemm.hip): K a multiple of 128,
 // x and the codes below 2 GiB each, scales 16-byte aligned; t = x A^T (fp32,
 // m x r) formed beforehand.
 bool gemm_w4_supports(int64_t m, int64_t n, int64_t k, const void* scales);

@@ -10,7 +10,7 @@
 //                t = x A^T itself)
 //   other m <= 16: decode_xs_kernel (decode_xs.hip; forms t itself)
 //   m > 16:      lora_down_kernel, then gemm_w4_kernel (gemm.hip: bf16 MFMA GEMM
-//                with W decoded in registers; K a multiple of 256, x and the
+//                with W decoded in registers; K a multiple of 128, x and the
 //                codes below 2 GiB, scales 16-byte aligned) or else
 //                linear_gemm_kernel (each weight tile dequantized once into LDS)
 //   shapes the decode kernels do not take: lora_down_kernel, then
@@ -696,7 +696,7 @@ static hipError_t launch_decode(int mg, const void* x, int64_t m, int64_t k, con
     }
   }
 #undef FP4W_DECODE
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uint8_t* codes,
@@ -734,12 +734,13 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
                                     y, part, cnt_n, stream);
     if (e != hipSuccess) return e;
   } else if (plan.path == 2) {
-    if (fmt == FMT_NVFP4)
-      (void)launch_decode<FMT_NVFP4>((int)((m + 3) / 4), x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part,
-                               cnt_n, plan.splits, stream);
-    else
-      (void)launch_decode<FMT_MXFP4>(1, x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part, cnt_n,
-                               plan.splits, stream);
+    hipError_t e =
+        fmt == FMT_NVFP4
+            ? launch_decode<FMT_NVFP4>((int)((m + 3) / 4), x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y,
+                                       part, cnt_n, plan.splits, stream)
+            : launch_decode<FMT_MXFP4>(1, x, m, k, codes, scales, tensor_scale, n, t, lora_b, r, y, part, cnt_n,
+                                       plan.splits, stream);
+    if (e != hipSuccess) return e;
   } else if (gemm_w4_supports(m, n, k, scales)) {
     hipError_t e = launch_gemm_w4(fmt, x, m, k, codes, scales, tensor_scale, n, t, has_lora ? lora_b : nullptr,
                                   has_lora ? r : 0, y, stream);

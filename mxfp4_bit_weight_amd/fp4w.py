@@ -316,17 +316,44 @@ def aqn_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, noise: torch.Tensor, sigma
 def grouped_linear(x: torch.Tensor, row_index: torch.Tensor, expert_offsets: torch.Tensor, fmt: int,
                    codes: torch.Tensor, scales: torch.Tensor, tensor_scales: Optional[torch.Tensor],
                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """fp4w_grouped_linear over experts: codes (E, n, k/2), scales (E, n, k/blk)."""
+    """fp4w_grouped_linear over experts: codes (E, n, k/2), scales (E, n, k/blk).
+
+    Every shape the kernels index with is checked before the launch (a narrower
+    x, short offsets or scales of the other format would be read past their
+    ends).  Without ``out``, y is zero-filled first, so rows no expert covers
+    read as zero rather than as stale memory."""
+    if fmt not in BLOCK:
+        raise ValueError(f"unknown format {fmt}")
     _need(x, torch.bfloat16, "x")
     _need(row_index, torch.int32, "row_index")
     _need(expert_offsets, torch.int32, "expert_offsets")
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    if codes.dim() != 3:
+        raise ValueError("codes must be (num_experts, n, k/2)")
     e, n, kh = codes.shape
     k = kh * 2
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be (num_tokens, {k}), got {tuple(x.shape)}")
+    if row_index.dim() != 1:
+        raise ValueError("row_index must be one-dimensional")
+    if expert_offsets.shape != (e + 1,):
+        raise ValueError(f"expert_offsets must hold num_experts + 1 = {e + 1} entries, "
+                         f"got {tuple(expert_offsets.shape)}")
+    if tuple(scales.shape) != (e, n, k // BLOCK[fmt]):
+        raise ValueError(f"scales must be {(e, n, k // BLOCK[fmt])} for this format, got {tuple(scales.shape)}")
+    if fmt == NVFP4:
+        if tensor_scales is None:
+            raise ValueError("NVFP4 needs one tensor scale per expert")
+        _need(tensor_scales, torch.float32, "tensor_scales")
+        if tensor_scales.numel() != e:
+            raise ValueError(f"tensor_scales must hold {e} entries, got {tensor_scales.numel()}")
     total = row_index.numel()
-    y = _out(out, (total, n), torch.bfloat16, x.device)
+    y = torch.zeros((total, n), dtype=torch.bfloat16, device=x.device) if out is None else \
+        _out(out, (total, n), torch.bfloat16, x.device)
     _check(_grouped(fmt, _ptr(x), x.shape[0], _ptr(row_index), _ptr(expert_offsets), e, total, n, k,
-                    _ptr(codes), _ptr(scales), _ptr(tensor_scales), _ptr(y), _stream(x.device)),
-           "fp4w_grouped_linear")
+                    _ptr(codes), _ptr(scales), _ptr(tensor_scales) if fmt == NVFP4 else None, _ptr(y),
+                    _stream(x.device)), "fp4w_grouped_linear")
     return y
 
 

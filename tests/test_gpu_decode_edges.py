@@ -161,3 +161,39 @@ def test_lora_b_not_16_byte_aligned(fp4w, m):
     y_ref = fp4w.linear(bf16_dev(x), q, bf16_dev(a), bf16_dev(b))
     torch.cuda.synchronize()
     assert torch.equal(y_off.view(torch.int16), y_ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_codes_beyond_2gib_on_the_fallback_decode(fp4w, fmt):
+    """9 rows of x against W (16400, 262144): 2.15e9 bytes of codes, past the
+    32-bit buffer offsets of the x-in-registers kernel, so the call runs the
+    fallback decode (t = x A^T by its own launch, then the bf16-MFMA decode
+    tile).  Random codes under random valid scales (codes and scales drawn
+    directly: quantizing a 4.3e9-weight bf16 tensor on the host would take
+    minutes); 512 sampled outputs against the oracle, every output written."""
+    m, n, k, r = 9, 16400, 262144, 16
+    assert n * (k // 2) >= 1 << 31
+    say(f"[decode-edges] codes beyond 2 GiB fmt={fmt} m={m} n={n} k={k}")
+    g = np.random.default_rng(71 + fmt)
+    codes = g.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    if fmt == 0:
+        scales = g.integers(0x20, 0x48, (n, k // 16), dtype=np.uint8)      # E4M3 2^-3 .. 2^2
+        st = np.float32(1.0 / 64)
+    else:
+        scales = g.integers(120, 130, (n, k // 32), dtype=np.uint8)
+        st = np.float32(1.0)
+    _, x, a, b = W.linear_inputs(72, 16, k, m, rank=r)
+    b = W.normal_bf16(72, W.TID_B, (n, r), 0.01)
+    q = qweight_dev(fp4w, fmt, codes, scales, st)
+    y = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    fp4w.linear(bf16_dev(x), q, bf16_dev(a), bf16_dev(b), out=y)
+    torch.cuda.synchronize()
+    del q
+    assert bool(torch.isfinite(y).all().item()), "an output was not written"
+    rows = g.integers(0, m, 512)
+    cols = g.integers(0, n, 512)
+    ys = f64_of_bf16(bits_host(y[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)]))
+    y64 = O.linear_sampled(fmt, x, codes, scales, st, rows, cols, a, b)
+    xn = np.sqrt((f64_of_bf16(x[rows]) ** 2).sum(axis=1))
+    wn = weff_norms(fmt, codes, scales, st, a, b, rows=cols)
+    check_bound(ys, y64, xn, wn, "codes beyond 2 GiB")

@@ -119,3 +119,37 @@ def test_bad_token_index_gives_nan_rows(fp4w, fmt):
     yh = y.float().cpu().numpy()
     assert np.isnan(yh[1]).all() and np.isnan(yh[3]).all()
     assert np.isfinite(yh[[0, 2, 4]]).all()
+
+
+def test_binding_rejects_bad_shapes_before_launch(fp4w):
+    """Shapes the kernels index with are checked before any launch: a narrower x,
+    short offsets, scales of the other format, a short tensor-scale vector or a
+    wrongly sized output raise ValueError; without ``out`` y starts as zeros."""
+    e, n, k = 3, 32, 256
+    codes = torch.zeros((e, n, k // 2), dtype=torch.uint8, device=DEV)
+    sc_nv = torch.full((e, n, k // 16), 0x38, dtype=torch.uint8, device=DEV)
+    sc_mx = torch.full((e, n, k // 32), 127, dtype=torch.uint8, device=DEV)
+    ts = torch.ones(e, dtype=torch.float32, device=DEV)
+    x = torch.ones((4, k), dtype=torch.bfloat16, device=DEV)
+    ri = torch.zeros(6, dtype=torch.int32, device=DEV)
+    off = torch.tensor([0, 2, 4, 6], dtype=torch.int32, device=DEV)
+    bad = [
+        dict(x=x[:, :k - 32].contiguous()),                                  # narrower x
+        dict(expert_offsets=off[:3].contiguous()),                            # num_experts entries only
+        dict(scales=sc_mx),                                                   # MXFP4-shaped scales with NVFP4
+        dict(tensor_scales=ts[:2].contiguous()),                              # one tensor scale short
+        dict(tensor_scales=None),                                             # NVFP4 without tensor scales
+        dict(codes=codes.view(torch.int8)),                                   # not uint8
+        dict(out=torch.empty((6, n - 1), dtype=torch.bfloat16, device=DEV)),  # short output rows
+    ]
+    base = dict(x=x, row_index=ri, expert_offsets=off, fmt=0, codes=codes, scales=sc_nv, tensor_scales=ts)
+    for change in bad:
+        args = dict(base, **change)
+        with pytest.raises(ValueError):
+            fp4w.grouped_linear(**args)
+    with pytest.raises(ValueError):
+        fp4w.grouped_linear(**dict(base, fmt=1))                              # NVFP4-shaped scales with MXFP4
+    y = fp4w.grouped_linear(**dict(base, expert_offsets=torch.tensor([0, 1, 2, 3], dtype=torch.int32,
+                                                                        device=DEV)))
+    torch.cuda.synchronize()
+    assert bool((y[3:] == 0).all().item()), "rows no expert covers must read as zero"

@@ -22,10 +22,12 @@ def fp4w():
     return F
 
 
-def _run_dev(fp4w, fmt, w, x, a, b):
+def _run_dev(fp4w, fmt, w, x, a, b, nan_out=False):
     codes, scales, st = O.quantize(fmt, w)
     q = qweight_dev(fp4w, fmt, codes, scales, st)
-    y = fp4w.linear(bf16_dev(x), q, bf16_dev(a) if a is not None else None, bf16_dev(b) if b is not None else None)
+    out = torch.full((x.shape[0], q.n), float("nan"), dtype=torch.bfloat16, device=DEV) if nan_out else None
+    y = fp4w.linear(bf16_dev(x), q, bf16_dev(a) if a is not None else None, bf16_dev(b) if b is not None else None,
+                    out=out)
     torch.cuda.synchronize()
     return y, codes, scales, st
 
@@ -110,12 +112,12 @@ def _sampled_case(fp4w, fmt, m, n, k, samples, seed, what):
     say(f"[linear] {what} fmt={fmt} m={m} n={n} k={k} (sampled)")
     wkind = "outlier" if fmt == 0 else "student_t"
     w, x, a, b = W.linear_inputs(seed, n, k, m, rank=16, wkind=wkind)
-    yd, codes, scales, st = _run_dev(fp4w, fmt, w, x, a, b)
+    yd, codes, scales, st = _run_dev(fp4w, fmt, w, x, a, b, nan_out=True)   # y starts as NaN
     rng = np.random.default_rng(seed)
     rows = rng.integers(0, m, samples)
     cols = rng.integers(0, n, samples)
     ys = f64_of_bf16(bits_host(yd[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)]))
-    assert bool(torch.isfinite(yd).all().item())
+    assert bool(torch.isfinite(yd).all().item()), "an output was not written"
     del yd
     y64 = O.linear_sampled(fmt, x, codes, scales, st, rows, cols, a, b)
     xn = np.sqrt((f64_of_bf16(x[rows]) ** 2).sum(axis=1))

@@ -50,3 +50,32 @@ def test_gain_noise_is_multiplicative_weight_noise(fmt):
     plain = O.aqn_rmsnorm(x, gamma, np.zeros(128, np.float32), 0.0, 1e-6)
     wn = deq * (1.0 + float(np.float32(sigma)) * noise.astype(np.float64))[None, :]
     assert np.allclose(noisy, plain @ wn.T, rtol=1e-12, atol=1e-12 * np.abs(noisy).max())
+
+
+def test_gain_against_closed_forms():
+    """The gain gamma enters once, per channel, as a factor (Telegram post,
+    "Metod": the norm ahead of the projections).  Two closed forms pin it:
+    a constant row x = c has RMS |c|, so at sigma = 0 and eps = 0 the output is
+    sign(c) * gamma exactly; a one-hot row (value v at channel j) has mean square
+    v^2 / k, so y_j = sign(v) * sqrt(k) * gamma_j * (1 + sigma * noise_j) and
+    every other channel is 0.  A dropped, squared or shifted gamma fails both."""
+    k = 64
+    gamma_f = np.where(np.arange(k) % 3 == 0, 2.0, 0.5)       # 2 on channels 0, 3, 6, ...; 0.5 elsewhere
+    gamma_f[5] = -1.5
+    gamma = W.to_bf16_bits(gamma_f)
+    zeros = np.zeros(k, np.float32)
+    for c in (3.0, -0.75):
+        x = W.to_bf16_bits(np.full((1, k), c))
+        y = O.aqn_rmsnorm(x, gamma, zeros, 0.0, 0.0)[0]
+        assert np.array_equal(y, np.sign(c) * gamma_f)
+    rng = np.random.default_rng(11)
+    noise = rng.standard_normal(k).astype(np.float32)
+    sigma = 1e-2
+    for j, v in ((0, 5.0), (5, -2.0), (7, 0.25)):
+        row = np.zeros((1, k))
+        row[0, j] = v
+        y = O.aqn_rmsnorm(W.to_bf16_bits(row), gamma, noise, sigma, 0.0)[0]
+        want = np.sign(v) * math.sqrt(k) * gamma_f[j] * (1.0 + float(np.float32(sigma)) * float(noise[j]))
+        assert abs(y[j] - want) <= 1e-14 * abs(want)
+        others = np.delete(y, j)
+        assert np.all(others == 0.0)

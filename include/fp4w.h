@@ -58,6 +58,7 @@ extern "C" {
 #define FP4W_ERR_FORMAT    (-4)  /* unknown format or flag                            */
 #define FP4W_ERR_HIP       (-5)  /* a kernel launch failed                            */
 #define FP4W_ERR_WORKSPACE (-6)  /* workspace missing or smaller than required       */
+#define FP4W_ERR_SCRATCH   (-7)  /* fp4w_linear_noalloc: needs more than its device array */
 
 /* flags */
 #define FP4W_FROZEN_SCALES 0x1u  /* fp4w_quantize, fp4w_fake_quant: scales (and tensor scale) are inputs */
@@ -170,6 +171,26 @@ int fp4w_linear(int fmt, const void *x_bf16, int64_t m, int64_t k,
                 const uint8_t *codes, const uint8_t *scales, const float *tensor_scale,
                 int64_t n, const void *lora_a, const void *lora_b, int r,
                 void *y_bf16, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fp4w_linear_noalloc -- fp4w_linear without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, kernels and
+ * results as fp4w_linear (bit for bit); the workspace is a library-owned device
+ * array of FP4W_NOALLOC_SCRATCH_BYTES bytes, one per device, set up at the first
+ * call on a device and held until the process ends.  The call allocates and
+ * frees nothing.  A call whose fp4w_linear_workspace_bytes exceeds that size
+ * returns FP4W_ERR_SCRATCH and launches nothing (8 MiB covers every m <= 16 up
+ * to about 1.1e9 weights, and m * r * 4 up to about 8 MB on the GEMM path).
+ * Every call on one device shares the array, which keeps the last call's
+ * contents (its counter area is zero between calls): calls that overlap in
+ * time on one device race, so issue them in one stream order.
+ */
+#define FP4W_NOALLOC_SCRATCH_BYTES (8u << 20)
+int fp4w_linear_noalloc(int fmt, const void *x_bf16, int64_t m, int64_t k,
+                        const uint8_t *codes, const uint8_t *scales, const float *tensor_scale,
+                        int64_t n, const void *lora_a, const void *lora_b, int r,
+                        void *y_bf16, void *stream);
 
 /*
  * fp4w_linear_w4a4 -- y (m, n) bf16 = deq(x) deq(W)^T with x and W both MXFP4

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "../../include/fp4w.h"
 #include "fp4w_internal.hpp"
@@ -45,6 +46,9 @@ const char* fp4w_status_string(int status) {
     case FP4W_ERR_FORMAT: return "unknown format or flag";
     case FP4W_ERR_HIP: return "HIP kernel launch failed";
     case FP4W_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP4W_ERR_SCRATCH:
+      return "the call needs more workspace than the no-allocation entry point's device array holds "
+             "(FP4W_NOALLOC_SCRATCH_BYTES); use fp4w_linear with a workspace";
     default: return "unknown status";
   }
 }
@@ -250,3 +254,66 @@ int fp4w_merge_scales(int fmt, const uint8_t* scales_in, const float* deltas, in
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------
+// fp4w_linear_noalloc: fp4w_linear with its workspace in a library-owned device
+// array instead of a caller's buffer, for callers that cannot allocate.
+//
+// `scratch` is one array per device (each device that loads the library holds
+// its own copy until the process ends).  In host code its name is only a
+// host-side stand-in, so it is never passed to a kernel: at the first call on a
+// device (with that device current) hipGetSymbolAddress gives that device's
+// address, which is kept per device and used for every launch.  The first 28800
+// bytes hold the linear's arrival counters and LoRA hand-over words, which must
+// be zero before a call; every call returns them to zero, and the set-up clears
+// them once with a fill kernel on the caller's stream.  All calls on one device
+// share the array: calls that overlap in time on one device race.
+// ---------------------------------------------------------------------------------
+__device__ __align__(256) uint8_t scratch[FP4W_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+__global__ void zero_words_kernel(uint32_t* __restrict__ p, int words) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < words; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// This device's address of `scratch`, set up on the first call on the device.
+int device_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP4W_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP4W_ERR_HIP;
+    const int words = fp4w::kCounterSlots;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t*>(p), words);
+    if (hipGetLastError() != hipSuccess) return FP4W_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP4W_OK;
+}
+
+}  // namespace
+
+extern "C" int fp4w_linear_noalloc(int fmt, const void* x_bf16, int64_t m, int64_t k, const uint8_t* codes,
+                                   const uint8_t* scales, const float* tensor_scale, int64_t n, const void* lora_a,
+                                   const void* lora_b, int r, void* y_bf16, void* stream) {
+  bool nothing = false, lora = false;
+  fp4w::LinearPlan plan{};
+  int st = linear_check(fmt, x_bf16, m, k, codes, scales, tensor_scale, n, lora_a, lora_b, r, y_bf16, &nothing,
+                        &lora, &plan);
+  if (st || nothing) return st;
+  if (plan.bytes > (size_t)FP4W_NOALLOC_SCRATCH_BYTES) return FP4W_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = device_scratch(as_stream(stream), &ws);
+  if (st) return st;
+  return hip_status(fp4w::launch_linear(fmt, x_bf16, m, k, codes, scales, tensor_scale, n, lora ? lora_a : nullptr,
+                                        lora ? lora_b : nullptr, lora ? r : 0, y_bf16, ws, plan,
+                                        as_stream(stream)));
+}

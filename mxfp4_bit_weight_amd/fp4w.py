@@ -45,6 +45,7 @@ _dequantize = _sig("fp4w_dequantize", _int, _int, _p, _p, _p, _i64, _i64, _p, _u
 _fake_quant = _sig("fp4w_fake_quant", _int, _int, _p, _i64, _i64, _p, _p, _p, _u32, _p)
 _ws_bytes = _sig("fp4w_linear_workspace_bytes", _sz, _i64, _i64, _i64, _int)
 _linear = _sig("fp4w_linear", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _int, _p, _p, _sz, _p)
+_linear_noalloc = _sig("fp4w_linear_noalloc", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _int, _p, _p)
 _w4a4 = _sig("fp4w_linear_w4a4", _int, _int, _p, _p, _i64, _i64, _p, _p, _i64, _p, _p)
 _bwd_dx = _sig("fp4w_linear_backward_dx", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p)
 _delta_grad = _sig("fp4w_scale_delta_grad", _int, _int, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p)
@@ -59,7 +60,7 @@ _debug_lora_wait = _sig("fp4w_debug_lora_wait", _i64, _i64)
 EXPORTED = ["fp4w_quantize", "fp4w_dequantize", "fp4w_linear_workspace_bytes", "fp4w_linear",
             "fp4w_grouped_linear", "fp4w_merge_scales", "fp4w_status_string", "fp4w_version",
             "fp4w_debug_lora_wait", "fp4w_fake_quant", "fp4w_linear_w4a4", "fp4w_linear_backward_dx",
-            "fp4w_scale_delta_grad", "fp4w_aqn_rmsnorm", "fp4w_aqn_sigma"]
+            "fp4w_scale_delta_grad", "fp4w_aqn_rmsnorm", "fp4w_aqn_sigma", "fp4w_linear_noalloc"]
 
 
 class Fp4wError(RuntimeError):
@@ -244,6 +245,30 @@ def linear(x: torch.Tensor, q: QWeight, lora_a: Optional[torch.Tensor] = None,
     _check(_linear(q.fmt, _ptr(x), m, k, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.n,
                    _ptr(lora_a), _ptr(lora_b), r, _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)),
            "fp4w_linear")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def linear_noalloc(x: torch.Tensor, q: QWeight, lora_a: Optional[torch.Tensor] = None,
+                   lora_b: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4w_linear_noalloc: fp4w_linear with the library's own per-device scratch
+    array as its workspace; with ``out`` given nothing is allocated."""
+    _need(x, torch.bfloat16, "x")
+    m, k = x.shape
+    if k != q.k:
+        raise ValueError(f"x has k={k}, the weight k={q.k}")
+    r = 0
+    if lora_a is not None or lora_b is not None:
+        _need(lora_a, torch.bfloat16, "lora_a")
+        _need(lora_b, torch.bfloat16, "lora_b")
+        r = lora_a.shape[0]
+        if lora_a.shape != (r, k) or lora_b.shape != (q.n, r):
+            raise ValueError("lora_a must be (r, k) and lora_b (n, r)")
+    y = _out(out, (m, q.n), torch.bfloat16, x.device)
+    _check(_linear_noalloc(q.fmt, _ptr(x), m, k, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.n,
+                           _ptr(lora_a), _ptr(lora_b), r, _ptr(y), _stream(x.device)), "fp4w_linear_noalloc")
     return y
 
 

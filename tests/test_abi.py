@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         assert lib.status_string(code) and lib.status_string(code) != "unknown status"
     assert lib.status_string(-99) == "unknown status"
     assert lib.version() >= 1
@@ -153,3 +153,21 @@ def test_backward_delta_aqn_validation_without_launch(lib):
     assert a(_fake(A), 4, 16, _fake(A), None, 0.01, 1e-6, _fake(A), None) == -1            # noise null
     assert a(_fake(A), 4, 16, _fake(A), _fake(A + 4), 0.01, 1e-6, _fake(A), None) == -3    # noise alignment
     assert a(None, 0, 16, None, None, 0.01, 1e-6, None, None) == 0                          # m = 0
+
+
+def test_noalloc_validation_without_launch(lib):
+    """fp4w_linear_noalloc checks what fp4w_linear checks, and refuses a call whose
+    workspace would exceed its device array before touching the device."""
+    f = lib._linear_noalloc
+    A = 0x10000
+    assert lib.NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert f(7, _fake(A), 2, 64, _fake(A), _fake(A), _fake(A), 16, None, None, 0, _fake(A), None) == -4
+    assert f(0, _fake(A), 2, 48, _fake(A), _fake(A), _fake(A), 16, None, None, 0, _fake(A), None) == -2
+    assert f(0, _fake(A), 2, 64, _fake(A), _fake(A), None, 16, None, None, 0, _fake(A), None) == -1
+    assert f(0, _fake(A + 2), 2, 64, _fake(A), _fake(A), _fake(A), 16, None, None, 0, _fake(A), None) == -3
+    assert f(0, _fake(A), 2, 64, _fake(A), _fake(A), _fake(A), 16, _fake(A), None, 16, _fake(A), None) == -1
+    assert f(0, _fake(A), 0, 64, None, None, None, 16, None, None, 0, None, None) == 0
+    m, n, k, r = 40000, 64, 256, 64
+    assert lib.linear_workspace_bytes(m, n, k, r) > lib.NOALLOC_SCRATCH_BYTES
+    assert f(0, _fake(A), m, k, _fake(A), _fake(A), _fake(A), n, _fake(A), _fake(A), r, _fake(A), None) == -7
+    assert "no-allocation" in lib.status_string(-7)

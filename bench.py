@@ -12,9 +12,11 @@ through the frozen base, its Scale-QLoRA delta gradient and its W4A4 MXFP4
 form, quantize, merge, dequantize, grouped MoE).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-rows]
-       python bench.py --roofline-only   (the decode kernel's launches and a plain
-                                          copy of known size, for profiler runs)
-       python bench.py --gemm-only       (the prefill GEMM rows only, for profiler runs)
+       python bench.py --only TARGET     (one kernel's launches and a plain copy of known
+                                          size, for profiler runs; TARGET is one of
+                                          decode_m1_lora, decode_m1, decode_m8_lora,
+                                          quantize_nvfp4, gemm)
+       --roofline-only = --only decode_m1_lora;  --gemm-only = --only gemm
 Progress goes to stderr; stdout is exactly one JSON line.
 """
 import argparse
@@ -34,6 +36,23 @@ FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 ROTATE_BYTES = 1 << 30         # rotate each weight over at least 1 GiB (4x the 256 MB MALL)
 METRIC = "W4A16 NVFP4 linear: effective HBM GB/s (% peak) at M=1/8; TFLOP/s at M=16K"
+PROFILE_TARGETS = ("decode_m1_lora", "decode_m1", "decode_m8_lora", "quantize_nvfp4", "gemm")
+# kernel sources behind each profiled target: a committed counter summary whose
+# recorded hash differs from these files' hash no longer describes the kernel
+TARGET_SOURCES = {
+    "decode_m1_lora": ("decode.hip", "xenc.hpp", "lora_handover.hpp", "sync.hpp", "fp4w_device.hpp",
+                       "fp4w_internal.hpp"),
+    "decode_m1": ("decode.hip", "xenc.hpp", "sync.hpp", "fp4w_device.hpp", "fp4w_internal.hpp"),
+    "decode_m8_lora": ("decode_xs.hip", "lora_handover.hpp", "sync.hpp", "fp4w_device.hpp", "fp4w_internal.hpp"),
+    "quantize_nvfp4": ("quantize.hip", "codec.hpp", "fp4w_device.hpp", "fp4w_internal.hpp"),
+    "gemm": ("gemm.hip", "gemm_common.hpp", "linear.hip", "fp4w_device.hpp", "fp4w_internal.hpp"),
+}
+PROFILE_FILES = {
+    "decode_m1_lora": "decode_gate_up_m1_nvfp4_lora_pmc.txt",
+    "decode_m1": "decode_gate_up_m1_nvfp4_pmc.txt",
+    "decode_m8_lora": "decode_gate_up_m8_nvfp4_lora_pmc.txt",
+    "quantize_nvfp4": "quantize_gate_up_nvfp4_pmc.txt",
+}
 
 
 def log(*a):
@@ -50,8 +69,15 @@ def parse():
                    help="only the prefill GEMM rows (both formats), for profiler runs")
     p.add_argument("--roofline-only", action="store_true",
                    help="only the roofline launches of the decode kernel and a copy kernel of known size")
-    p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
-    return p.parse_args()
+    p.add_argument("--only", choices=PROFILE_TARGETS, default=None,
+                   help="only one kernel's launches (and a copy of known size), for profiler runs")
+    p.add_argument("--cpu-seconds", type=float, default=8.0, help="budget of the CPU-oracle headline sample")
+    a = p.parse_args()
+    if a.roofline_only:
+        a.only = "decode_m1_lora"
+    if a.gemm_only:
+        a.only = "gemm"
+    return a
 
 
 # ---- algorithmic work ---------------------------------------------------------------
@@ -139,7 +165,7 @@ def main():
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
 
-    if args.gemm_only:
+    if args.only == "gemm":
         rank = W.LORA_RANK
         n, k = W.QWEN7B_SHAPES["gate_up"]
         weights = {}
@@ -156,7 +182,11 @@ def main():
     decode = {}
     t_gen = time.time()
     for fmt in (0, 1):
+        if args.only and fmt == 1:
+            break
         for si, (name, (n, k)) in enumerate(shapes.items()):
+            if args.only and name != "gate_up":
+                continue
             wkind = "outlier" if fmt == 0 else "student_t"
             w, x1, a, b = W.linear_inputs(100 + si, n, k, 1, rank=rank, wkind=wkind)
             x8 = W.normal_bf16(100 + si, W.TID_X + 50, (8, k), 1.0)
@@ -174,57 +204,84 @@ def main():
     sync()
     log(f"[bench] inputs ready in {time.time() - t_gen:.1f}s")
 
-    # ---- headline step: NVFP4, M = 1, three shapes, LoRA r = 16 ------------------------
     ys = {name: torch.empty((8, d["n"]), dtype=torch.bfloat16, device=dev)
           for (fmt, name), d in decode.items() if fmt == 0}
     ws_bytes = max(fp4w.linear_workspace_bytes(m, n, k, rank) for (n, k) in shapes.values() for m in (1, 8))
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)      # zero-filled once, reused by every call
 
+    # ---- the decode kernel on W (18944, 3584): with the LoRA (the headline's kernel) and without
+    dg = decode[(0, "gate_up")]
+    n, k = dg["n"], dg["k"]
+
+    def gemv(m, lora):
+        x = dg["x1"] if m == 1 else dg["x8"]
+
+        def f(i):
+            q, a, b = dg["qs"][i % len(dg["qs"])]
+            if lora:
+                fp4w.linear(x, q, a, b, out=ys["gate_up"][:m], workspace=ws)
+            else:
+                fp4w.linear(x, q, out=ys["gate_up"][:m], workspace=ws)
+        return f
+
+    launches = max(args.steps, 100)
+    if args.only:
+        copy_bytes = calibration_copy(torch, dev, sync)
+        if args.only == "quantize_nvfp4":
+            w = bf16(dg["host"][0])
+            outs = [fp4w.empty_qweight(0, n, k, dev) for _ in range(4)]
+            for i in range(launches):
+                fp4w.quantize(w, 0, out=outs[i % 4])
+            sync()
+            per, what = float("nan"), "quantize"
+        else:
+            m, lora = {"decode_m1_lora": (1, True), "decode_m1": (1, False), "decode_m8_lora": (8, True)}[args.only]
+            per, _ = time_graph(gemv(m, lora), launches, args.warmup)
+            what = "linear"
+        print(json.dumps({"target": args.only, "launches": launches, "per_launch_us": round(per * 1e3, 3),
+                          "calls": what, "copy_kernel_bytes": copy_bytes,
+                          "kernel_sources_sha256": kernel_sources_sha256(args.only)}), flush=True)
+        return
+
+    # ---- headline step: NVFP4, M = 1, three shapes, LoRA r = 16 ------------------------
     def step(i):
         for name in shapes:
             d = decode[(0, name)]
             q, a, b = d["qs"][i % len(d["qs"])]
             fp4w.linear(d["x1"], q, a, b, out=ys[name][:1], workspace=ws)
 
-    step_bytes = sum(linear_bytes(0, 1, n, k, rank) for n, k in shapes.values())
-    if args.roofline_only:
-        ms_step, wall, ms_eager = float("nan"), 0.0, float("nan")
-    else:
-        ms_step, wall = time_graph(step, args.steps, args.warmup)
+    step_bytes = sum(linear_bytes(0, 1, n_, k_, rank) for n_, k_ in shapes.values())
+    ms_step, wall = time_graph(step, args.steps, args.warmup)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    if not args.roofline_only:
-        log(f"[bench] step (graph replay): {ms_step * 1e3:.2f} us, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of peak)")
-        ms_eager, _ = time_loop(step, args.steps, args.warmup)
-        log(f"[bench] step (eager launches): {ms_eager * 1e3:.2f} us")
+    log(f"[bench] step (graph replay): {ms_step * 1e3:.2f} us, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of peak)")
+    ms_eager, _ = time_loop(step, args.steps, args.warmup)
+    log(f"[bench] step (eager launches): {ms_eager * 1e3:.2f} us")
 
-    # ---- roofline: the decode kernel alone (gate/up, M = 1, no LoRA: one launch per call) -
-    dg = decode[(0, "gate_up")]
-    n, k = dg["n"], dg["k"]
-
-    def gemv_only(i):
-        q, _, _ = dg["qs"][i % len(dg["qs"])]
-        fp4w.linear(dg["x1"], q, out=ys["gate_up"][:1], workspace=ws)
-
-    launches = max(args.steps, 100)
-    per_launch_ms, _ = time_graph(gemv_only, launches, args.warmup)
-    gemv_bytes = linear_bytes(0, 1, n, k, 0)
-    achieved = gemv_bytes / (per_launch_ms * 1e-3) / 1e9
-    roofline = {"kernel": "decode_f8f4_kernel<NVFP4, 1 row, 4 waves, ring 8, no LoRA> on W (18944, 3584), M=1",
+    # ---- roofline: the headline's dominant kernel, one launch per call -------------------
+    per_lora, _ = time_graph(gemv(1, True), launches, args.warmup)
+    per_plain, _ = time_graph(gemv(1, False), launches, args.warmup)
+    clock = sclk_mhz(torch, dev, sync)
+    bytes_lora = linear_bytes(0, 1, n, k, rank)
+    bytes_plain = linear_bytes(0, 1, n, k, 0)
+    achieved = bytes_lora / (per_lora * 1e-3) / 1e9
+    ach_plain = bytes_plain / (per_plain * 1e-3) / 1e9
+    ceiling = read_ceiling(torch, dev, sync, time_graph, bytes_lora, launches, args.warmup)
+    roofline = {"kernel": "decode_f8f4_kernel<NVFP4, 1 row, LoRA r=16 formed inside the launch> on W (18944, 3584), M=1",
                 "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(),
-                "avg_launch_us": round(per_launch_ms * 1e3, 3), "launches_timed": launches,
-                "timing": "HIP events around a graph of back-to-back launches (weights rotated over >1 GiB)",
-                "algorithmic_bytes_per_launch": gemv_bytes}
-    log(f"[bench] decode kernel alone: {per_launch_ms * 1e3:.2f} us/launch, {achieved:.1f} GB/s")
-    if args.roofline_only:
-        # a plain copy of known size: the scale of the profiler's FETCH_SIZE / WRITE_SIZE
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        sync()
-        print(json.dumps({"roofline": roofline, "copy_kernel_bytes": src.numel()}), flush=True)
-        return
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic("decode_m1_lora"),
+                "avg_launch_us": round(per_lora * 1e3, 3), "launches_timed": launches,
+                "timing": "HIP events around a graph of back-to-back launches on their stream "
+                          "(weights rotated over >1 GiB)",
+                "algorithmic_bytes_per_launch": bytes_lora,
+                "variants": {"no_lora": {"achieved": round(ach_plain, 1), "frac": round(ach_plain / HBM_PEAK_GBS, 4),
+                                         "avg_launch_us": round(per_plain * 1e3, 3),
+                                         "algorithmic_bytes_per_launch": bytes_plain,
+                                         "traffic": pmc_traffic("decode_m1")}},
+                "ceiling": dict(ceiling, sclk_mhz=clock,
+                                frac_of_ceiling=round(achieved / ceiling["read_gbs"], 4) if ceiling["read_gbs"] else None)}
+    log(f"[bench] decode kernel with LoRA {per_lora * 1e3:.2f} us ({achieved:.1f} GB/s), without "
+        f"{per_plain * 1e3:.2f} us ({ach_plain:.1f} GB/s); plain read of the same bytes {ceiling['read_us']} us "
+        f"({ceiling['read_gbs']} GB/s); sclk {clock} MHz")
 
     rows = {}
     if not args.skip_rows:
@@ -247,10 +304,10 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def pmc_traffic():
-    """HBM bytes per launch of the decode kernel from the committed rocprofv3 --pmc
-    summary, if it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "decode_gate_up_m1_nvfp4_pmc.txt")
+def pmc_traffic(target):
+    """HBM bytes per launch of a profiled kernel from its committed rocprofv3 --pmc
+    summary, if that was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", PROFILE_FILES[target])
     if not os.path.exists(path):
         return None
     kv = {}
@@ -258,7 +315,7 @@ def pmc_traffic():
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
-    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha256(target):
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
@@ -266,14 +323,81 @@ def pmc_traffic():
         return None
 
 
-KERNEL_SOURCES = ("decode.hip", "xenc.hpp", "sync.hpp", "fp4w_device.hpp", "fp4w_internal.hpp")
-
-
-def kernel_sources_sha256():
+def kernel_sources_sha256(target):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in TARGET_SOURCES[target]:
         h.update(open(os.path.join(ROOT, "mxfp4_bit_weight_amd", "csrc", f), "rb").read())
     return h.hexdigest()
+
+
+def calibration_copy(torch, dev, sync):
+    """A plain 256 MiB device copy: the profiler's FETCH_SIZE / WRITE_SIZE for a
+    launch of known size, which scales the counters of the profiled kernel."""
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    sync()
+    return src.numel()
+
+
+def _membench():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "mxfp4_bit_weight_amd", "libfp4w_membench.so"))
+    lib.fp4w_membench_read.restype = ctypes.c_int
+    lib.fp4w_membench_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.fp4w_membench_clock.restype = ctypes.c_int
+    lib.fp4w_membench_clock.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def sclk_mhz(torch, dev, sync):
+    """The shader clock right after the decode launches: cycle counter against the
+    100 MHz counter over 50 us on one wave (median of 5)."""
+    import ctypes
+    lib = _membench()
+    out = torch.zeros(2, dtype=torch.int64, device=dev)
+    vals = []
+    for _ in range(5):
+        st = lib.fp4w_membench_clock(5000, ctypes.c_void_p(out.data_ptr()),
+                                     ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+        if st != 0:
+            return None
+        sync()
+        cyc, ticks = (int(v) for v in out.cpu().tolist())
+        if ticks > 0:
+            vals.append(100.0 * cyc / ticks)
+    return round(sorted(vals)[len(vals) // 2], 1) if vals else None
+
+
+def read_ceiling(torch, dev, sync, time_graph, nbytes, launches, warmup):
+    """What a memory-bound launch of `nbytes` can reach here: a plain streaming
+    read of the same byte count from buffers rotated over more than 1 GiB, timed
+    like the decode kernel (graph of back-to-back launches, HIP events); the best
+    of a few grid sizes."""
+    import ctypes
+    lib = _membench()
+    nb = (nbytes + 15) // 16 * 16
+    copies = max(2, -(-ROTATE_BYTES // nb))
+    bufs = [torch.ones(nb, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        def f(i, blocks=blocks):
+            st = lib.fp4w_membench_read(ctypes.c_void_p(bufs[i % copies].data_ptr()), nb, blocks,
+                                        ctypes.c_void_p(sink.data_ptr()),
+                                        ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"fp4w_membench_read: status {st}")
+        per, _ = time_graph(f, launches, warmup)
+        if best is None or per < best[0]:
+            best = (per, blocks)
+    del bufs
+    per, blocks = best
+    return {"read_us": round(per * 1e3, 3), "read_gbs": round(nbytes / (per * 1e-3) / 1e9, 1),
+            "read_frac_of_peak": round(nbytes / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "read_blocks": blocks,
+            "what": "plain 16-byte streaming read of the kernel's algorithmic bytes, same rotation and timing"}
 
 
 def gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights):
@@ -498,8 +622,10 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
 
 
 def cpu_baseline(args, W, decode, rank, step_bytes):
-    """The CPU oracle (test infrastructure, binary64) on the same decode step, on
-    all host cores it is given, repeated for about --cpu-seconds."""
+    """The CPU oracle (test infrastructure, binary64, OpenMP) on the host cores it
+    is given: the headline decode step for about --cpu-seconds, then a bounded
+    sample of each other row (a few seconds each), in the same units as the GPU
+    rows.  The oracle is used as it stands, never tuned for this."""
     import oracle as O
     host = {name: decode[(0, name)]["host"] for name in W.QWEN7B_SHAPES}
     prepared = {}
@@ -515,10 +641,71 @@ def cpu_baseline(args, W, decode, rank, step_bytes):
         if time.perf_counter() - t0 >= args.cpu_seconds:
             break
     dt = time.perf_counter() - t0
+    total = dt
+
+    def timed(fn, budget=2.0):
+        n_, t_ = 0, time.perf_counter()
+        while True:
+            fn()
+            n_ += 1
+            if time.perf_counter() - t_ >= budget:
+                return n_, time.perf_counter() - t_
+
+    rows = {}
+    w, x1, a, b = host["gate_up"]
+    n, k = w.shape
+    for fmt, tag in ((O.NVFP4, "nvfp4"), (O.MXFP4, "mxfp4")):
+        cnt, sec = timed(lambda: O.quantize(fmt, w))
+        total += sec
+        rate = cnt * w.size / sec
+        rows[f"quantize_{tag}"] = {"weights_per_s": round(rate, 1),
+                                   "GB/s": round(rate * quant_bytes(fmt, w.size) / w.size / 1e9, 3),
+                                   "sample": f"{cnt} quantizations of W (18944, 3584), {sec:.1f} s"}
+    x1n, c, sc, st, an, bn = prepared["gate_up"]
+    g = np.random.default_rng(401)
+    deltas = (0.01 * g.standard_normal(sc.size)).astype(np.float32)
+    cnt, sec = timed(lambda: O.merge_scales(O.NVFP4, sc, deltas))
+    total += sec
+    rows["merge_scales_nvfp4"] = {"us": round(1e6 * sec / cnt, 1), "GB/s": round(cnt * sc.size * 6 / sec / 1e9, 4),
+                                  "sample": f"{cnt} in-place merges of 4,243,456 blocks, {sec:.1f} s"}
+    x8 = W.normal_bf16(100, W.TID_X + 50, (8, k), 1.0)
+    cnt, sec = timed(lambda: O.linear(O.NVFP4, x8, c, sc, st, an, bn))
+    total += sec
+    rows["decode_nvfp4_gate_up_M8"] = {"us": round(1e6 * sec / cnt, 1),
+                                       "GB/s": round(cnt * linear_bytes(0, 8, n, k, rank) / sec / 1e9, 4),
+                                       "sample": f"{cnt} linears x (8, 3584) W (18944, 3584) LoRA r=16, {sec:.1f} s"}
+    slice_rows = 32
+    xs = W.normal_bf16(300, W.TID_X, (slice_rows, k), 1.0)
+    cnt, sec = timed(lambda: O.linear(O.NVFP4, xs, c, sc, st, an, bn), budget=3.0)
+    total += sec
+    per_row = sec / cnt / slice_rows
+    full_s = per_row * W.PREFILL_M
+    rows["prefill_gemm_nvfp4"] = {
+        "TFLOP/s": round(linear_flops(W.PREFILL_M, n, k, rank) / full_s / 1e12, 6),
+        "extrapolated_ms": round(1e3 * full_s, 1),
+        "sample": f"{cnt} x a {slice_rows}-row slice of x (16384, 3584) against W (18944, 3584), LoRA r=16, "
+                  f"{sec:.1f} s; extrapolated per row to 16384 rows (labelled: not a full run)"}
+    cfg = W.MOE
+    row_index, offsets = W.moe_routing(500)
+    xm = W.normal_bf16(500, W.TID_X, (cfg["tokens"], cfg["d_model"]), 1.0)
+    ex = W.moe_expert_weights(600, cfg["experts"], cfg["d_ff"], cfg["d_model"])
+    qe = [O.quantize(O.NVFP4, ex[e]) for e in range(cfg["experts"])]
+    ce = np.stack([q[0] for q in qe])
+    se = np.stack([q[1] for q in qe])
+    te = np.array([q[2] for q in qe], np.float32)
+    active = int((np.diff(offsets) > 0).sum())
+    cnt, sec = timed(lambda: O.grouped_linear(O.NVFP4, xm, row_index, offsets, ce, se, te))
+    total += sec
+    nbm = active * (cfg["d_ff"] * cfg["d_model"] * 9 // 16 + 4) + 2 * (cfg["tokens"] * cfg["d_model"]
+                                                                      + row_index.size * cfg["d_ff"])
+    rows["grouped_moe_gate_nvfp4"] = {"us": round(1e6 * sec / cnt, 1), "GB/s": round(cnt * nbm / sec / 1e9, 4),
+                                      "sample": f"{cnt} grouped gate projections (128 experts (768, 2048), "
+                                                f"64 tokens top-8), {sec:.1f} s"}
     return {"value": round(step_bytes * reps / dt / 1e9, 3), "unit": "GB/s", "cores": O.num_threads(),
             "kind": "oracle",
             "sample": f"{reps} decode steps (the three Qwen-2.5-7B shapes at M=1, NVFP4, LoRA r=16), binary64 "
-                      f"oracle with OpenMP, {dt:.1f} s"}
+                      f"oracle with OpenMP, {dt:.1f} s",
+            "affinity_cpus": len(os.sched_getaffinity(0)), "total_cpu_seconds": round(total, 1), "rows": rows}
 
 
 if __name__ == "__main__":

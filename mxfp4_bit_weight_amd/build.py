@@ -14,6 +14,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp4w.so")
+# measurement references for the benchmark (plain streaming read, clock probe); not the path
+MEMBENCH_LIB = os.path.join(HERE, "libfp4w_membench.so")
 SOURCES = ["api.hip", "quantize.hip", "dequantize.hip", "merge.hip", "linear.hip", "decode.hip", "decode_xs.hip", "grouped.hip", "gemm.hip", "a4w4.hip", "backward.hip", "delta_grad.hip", "aqn.hip"]
 ARCH = "gfx950"
 
@@ -58,6 +60,10 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    obj = compile_one("membench.hip")
+    tmp = MEMBENCH_LIB + ".tmp"
+    subprocess.run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj], check=True)
+    os.replace(tmp, MEMBENCH_LIB)
     return LIB
 
 

@@ -80,6 +80,14 @@ def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
 
 
+def _check_scales(fmt, scales, n, k):
+    """The C code reads (n, k / blk) scale bytes: refuse any other shape."""
+    if fmt not in BLOCK:
+        raise ValueError(f"unknown format {fmt}")
+    if scales.shape != (n, k // BLOCK[fmt]):
+        raise ValueError(f"scales must be {(n, k // BLOCK[fmt])} for format {fmt}, got {scales.shape}")
+
+
 # ---- scalar codecs ---------------------------------------------------------
 
 def e2m1_decode(code: int) -> float:
@@ -173,6 +181,7 @@ def dequantize(fmt: int, codes, scales, tensor_scale=1.0, out: str = "f64"):
     codes = _c(codes, np.uint8)
     scales = _c(scales, np.uint8)
     n, k = codes.shape[0], codes.shape[1] * 2
+    _check_scales(fmt, scales, n, k)
     if out == "f64":
         y = np.empty((n, k), np.float64)
         _lib.orc_dequantize_f64(fmt, _ptr(codes), _ptr(scales), float(tensor_scale), n, k, _ptr(y))
@@ -210,6 +219,7 @@ def linear(fmt: int, x, codes, scales, tensor_scale, lora_a=None, lora_b=None):
     m, k = x.shape
     n = codes.shape[0]
     assert codes.shape[1] * 2 == k
+    _check_scales(fmt, scales, n, k)
     r = 0
     if lora_a is not None:
         lora_a = _c(lora_a, np.uint16)
@@ -231,6 +241,8 @@ def linear_sampled(fmt: int, x, codes, scales, tensor_scale, rows, cols, lora_a=
     cols = _c(cols, np.int64)
     m, k = x.shape
     n = codes.shape[0]
+    assert codes.shape[1] * 2 == k
+    _check_scales(fmt, scales, n, k)
     assert rows.shape == cols.shape
     assert rows.size == 0 or (rows.min() >= 0 and rows.max() < m and cols.min() >= 0 and cols.max() < n)
     r = 0
@@ -238,6 +250,7 @@ def linear_sampled(fmt: int, x, codes, scales, tensor_scale, rows, cols, lora_a=
         lora_a = _c(lora_a, np.uint16)
         lora_b = _c(lora_b, np.uint16)
         r = lora_a.shape[0]
+        assert lora_a.shape == (r, k) and lora_b.shape == (n, r)
     y = np.empty(rows.size, np.float64)
     _lib.orc_linear_sampled(fmt, _ptr(x), m, k, _ptr(codes), _ptr(scales), float(tensor_scale), n,
                             _ptr(lora_a), _ptr(lora_b), r, _ptr(rows), _ptr(cols), rows.size, _ptr(y))
@@ -329,6 +342,8 @@ def grouped_linear(fmt: int, x, row_index, offsets, codes, scales, tensor_scales
     e, n, kh = codes.shape
     k = kh * 2
     assert x.shape[1] == k and offsets.size == e + 1
+    if scales.shape != (e, n, k // BLOCK[fmt]) or ts.size < e:
+        raise ValueError("scales must be (experts, n, k / blk) with one tensor scale per expert")
     assert row_index.size == 0 or (row_index.min() >= 0 and row_index.max() < x.shape[0])
     total = int(offsets[-1])
     y = np.zeros((total, n), np.float64)

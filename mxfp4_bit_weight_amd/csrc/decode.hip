@@ -51,6 +51,7 @@
 #include "xenc.hpp"
 
 #include <atomic>
+#include <type_traits>
 
 namespace fp4w {
 
@@ -286,6 +287,10 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
 #pragma unroll
       for (int i = 0; i < 4; i++) acc[q][i] = 0.f;
     }
+    // A part that fits the ring was issued whole by the prologue: no refill loads
+    // (a load past the part still costs an instruction in the unit's in-order
+    // return queue).  The two cases are separate loops, so each gets exact wait counts.
+    auto run = [&](auto refill) {
     for (int jb = 0; jb < j1 - j0; jb += DEPTH) {
 #pragma unroll
       for (int u = 0; u < DEPTH; u++) {
@@ -315,10 +320,13 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
           s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4, 1.0f, false);   // E4M3 -> fp32, exact
           s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4, 1.0f, true);
         }
-        ring[u] = buffer_load16(crs, code_off(j0 + jb + u + DEPTH));
+        if constexpr (decltype(refill)::value) ring[u] = buffer_load16(crs, code_off(j0 + jb + u + DEPTH));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    };
+    if (j1 - j0 > DEPTH) run(std::true_type{});
+    else run(std::false_type{});
 #pragma unroll
     for (int q = 0; q < NQ; q++) {
       acc[q][0] = __builtin_fmaf(s01.x, dprev[q][0], acc[q][0]);
@@ -347,6 +355,10 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
     f32x4_t acc[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; q++) acc[q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    // A part that fits the ring was issued whole by the prologue: no refill loads
+    // (a load past the part still costs an instruction in the unit's in-order
+    // return queue).  The two cases are separate loops, so each gets exact wait counts.
+    auto run = [&](auto refill) {
     for (int jb = 0; jb < j1 - j0; jb += DEPTH) {
 #pragma unroll
       for (int u = 0; u < DEPTH; u++) {
@@ -364,10 +376,13 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
             acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[q], 0, 4, 0, sa, 0, sbw);
           }
         }
-        ring[u] = buffer_load16(crs, code_off(j0 + jb + u + DEPTH));
+        if constexpr (decltype(refill)::value) ring[u] = buffer_load16(crs, code_off(j0 + jb + u + DEPTH));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    };
+    if (j1 - j0 > DEPTH) run(std::true_type{});
+    else run(std::false_type{});
     // lane (n, g): rows 4 g + i = high (g < 2) / low (g >= 2) terms of m = 8 q + 4 (g & 1) + i
 #pragma unroll
     for (int q = 0; q < NQ; q++)
@@ -458,12 +473,11 @@ size_t decode_f8f4_lds_bytes(int fmt, int64_t m, int kslice, int nw, int r) {
   return (size_t)dq_layout(fmt, (int)m, kslice, nw, r).bytes;
 }
 
-// Waves per tile (the workgroup) and K slices.  Aim: about 16 waves per CU
-// (4 per SIMD), each with a handful of steps, so that every code load of the
-// launch is issued up front; wide workgroups before K slices (slices cost an
-// arrival atomic and a second pass over the partials), slices when the x slice
-// does not fit the LDS budget or the tiles are too few to fill the chip.
-constexpr int64_t kDqTargetWaves = 3072;
+// Waves per tile (the workgroup) and K slices.  Aim: every code load of the
+// launch issued up front, by as few waves as can hold them (a ring of at most 16
+// loads each); K slices (an arrival atomic and a second pass over the partials)
+// only when the x slice does not fit the LDS budget or the waves are very few.
+constexpr int64_t kDqTargetWaves = 768;
 
 static int dq_budget(int nw) { return nw == 4 ? 40 * 1024 : 64 * 1024; }
 
@@ -471,7 +485,14 @@ DecodeConfig plan_decode_f8f4(int fmt, int64_t m, int64_t n, int64_t k, int r) {
   DecodeConfig c{};
   const int64_t ntiles = (n + DQ_ROWS - 1) / DQ_ROWS;
   const int64_t nsteps = (k + DQ_STEP - 1) / DQ_STEP;
-  c.nw = ntiles * 4 >= kDqTargetWaves ? 4 : ntiles * 8 >= kDqTargetWaves ? 8 : 16;
+  // the fewest waves per tile whose parts (of the whole K) fit a ring of 16 loads,
+  // so every code load of the launch is issued up front by as few waves as can
+  // hold them (measured on MI355X at m = 1: 3584 x 3584 takes 4.7 us with 4
+  // waves against 6.3 us with 16; 18944 x 3584 is best with 4, 3584 x 18944 with 16)
+  c.nw = nsteps <= 4 * 16 ? 4 : nsteps <= 8 * 16 ? 8 : 16;
+  // several rows of x (one MFMA chain each per step): more waves when the tiles
+  // are few (3584 x 3584 at m = 2: 5.4 us with 8 waves, 6.4 with 4)
+  if (m >= 2 && c.nw == 4 && ntiles * 4 < 1536) c.nw = 8;
   if (m >= 2 && c.nw > 8) c.nw = 8;     // several MFMA chains per wave: 1024-thread groups would spill
   auto sps_for = [&](int64_t s) {
     int64_t sps = (nsteps + s - 1) / s;

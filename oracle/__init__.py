@@ -267,6 +267,29 @@ def linear_backward_dx(fmt: int, dy, codes, scales, tensor_scale):
     return dyf @ dequantize(fmt, codes, scales, tensor_scale, "f64")
 
 
+def lora_backward(dy, x, lora_a, lora_b):
+    """Gradients of the LoRA branch y_lora = (x A^T) B^T of the linear (Telegram
+    post, "Metod": an adapter trained in parallel to the frozen base), in
+    binary64, from the output gradient dY (m, n) and the input x (m, k), both
+    bf16, A (r, k) and B (n, r) bf16:
+        t  = x A^T          (m, r)
+        u  = dY B           (m, r)
+        dB = dY^T t         (n, r)
+        dA = u^T x          (r, k)
+        dX_lora = u A       (m, k)   (added to dY deq(W) for the whole input gradient)
+    Returns (t, u, dA, dB, dX_lora); each is one binary64 matrix product of
+    exact inputs, in the order the chain rule gives them."""
+    f = lambda a: (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    dyf, xf = f(np.atleast_2d(dy)), f(np.atleast_2d(x))
+    af, bf = f(lora_a), f(lora_b)
+    t = xf @ af.T
+    u = dyf @ bf
+    db = dyf.T @ t
+    da = u.T @ xf
+    dx = u @ af
+    return t, u, da, db, dx
+
+
 def scale_delta_grad(fmt: int, dy, x, codes, tensor_scale):
     """Scale-QLoRA delta gradient (Scale-QLoRA page: block-scale corrections in
     the decoded scale domain, rounded to the grid in every forward, the rounding

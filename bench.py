@@ -427,6 +427,35 @@ def gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights):
         rows[f"backward_dx_{name}"] = {"m": mrows, "n": n, "k": k, "ms": round(bms, 3), "TFLOP/s": round(btf, 1),
                                        "pct_bf16_peak": round(100 * btf / BF16_PEAK_TFLOPS, 1), "algorithmic_flop": bfl}
         log(f"[bench] backward dX {name} {bms:.3f} ms, {btf:.1f} TFLOP/s")
+        # the adapter's gradients (u = dY B, dA = u^T x, dB = dY^T (x A^T)) and the
+        # input gradient with the adapter's term u A, same layer and tokens
+        if fmt == 0:
+            ga = torch.empty((rank, k), dtype=torch.float32, device=dev)
+            gb = torch.empty((n, rank), dtype=torch.float32, device=dev)
+            uu = torch.empty((mrows, rank), dtype=torch.float32, device=dev)
+            wsl = torch.empty(fp4w.lora_backward_workspace_bytes(mrows, n, k, rank), dtype=torch.uint8, device=dev)
+
+            def lgrad(i):
+                fp4w._check(fp4w._lora_bwd(fp4w._ptr(y), mrows, n, fp4w._ptr(x), k, fp4w._ptr(a), fp4w._ptr(b), rank,
+                                           fp4w._ptr(uu), fp4w._ptr(ga), fp4w._ptr(gb), fp4w._ptr(wsl), wsl.numel(),
+                                           fp4w._stream(dev)), "fp4w_lora_backward")
+            lms, _ = time_loop(lgrad, 10, 5)
+            lfl = 2 * mrows * rank * (2 * n + 2 * k)
+            lbytes = 2 * (2 * mrows * n + 2 * mrows * k)            # dY and x, each read twice
+            rows["lora_backward"] = {"m": mrows, "n": n, "k": k, "r": rank, "ms": round(lms, 3),
+                                     "GB/s": round(lbytes / (lms * 1e-3) / 1e9, 1),
+                                     "pct_hbm_peak": round(100 * lbytes / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                                     "algorithmic_bytes": lbytes, "algorithmic_flop": lfl,
+                                     "bound": "hbm (dY and x streamed twice: products over their rows and columns)"}
+            log(f"[bench] LoRA backward {lms:.3f} ms")
+            xms, _ = time_loop(lambda i: fp4w.linear_backward_dx(y, q, out=dx, lora_u=uu, lora_a=a), 10, 5)
+            xfl = bfl + 2 * mrows * rank * k
+            rows["backward_dx_with_lora_nvfp4"] = {"m": mrows, "n": n, "k": k, "r": rank, "ms": round(xms, 3),
+                                                   "TFLOP/s": round(xfl / (xms * 1e-3) / 1e12, 1),
+                                                   "pct_bf16_peak": round(100 * xfl / (xms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 1),
+                                                   "algorithmic_flop": xfl}
+            log(f"[bench] backward dX + u A {xms:.3f} ms")
+            del ga, gb, uu, wsl
         # the Scale-QLoRA delta gradient of the same layer: dY = y, X = x
         gout = torch.empty((n, k // (16 if fmt == 0 else 32)), dtype=torch.float32, device=dev)
         dms, _ = time_loop(lambda i: fp4w.scale_delta_grad(y, x, q, out=gout), 10, 10)

@@ -214,23 +214,47 @@ int fp4w_linear_w4a4(int fmt, const uint8_t *x_codes, const uint8_t *x_scales,
                      int64_t n, void *y_bf16, void *stream);
 
 /*
- * fp4w_linear_backward_dx -- the input gradient through the frozen 4-bit base:
- * dx (m, k) bf16 = dy (m, n) deq(W) (n, k), fp32 accumulation, rounded once to
- * bf16 (training with the quantized base frozen back-propagates through it;
- * Telegram post, "Metod").  The weight is decoded exactly (as fp4w_dequantize
- * to bf16), the NVFP4 tensor scale multiplies the fp32 sums.  The LoRA branch's
- * own gradients are not formed here.
+ * fp4w_linear_backward_dx -- the input gradient through the frozen 4-bit base
+ * and, with a LoRA, through the adapter (training with the quantized base frozen
+ * back-propagates through it; Telegram post, "Metod"):
+ *   dx (m, k) bf16 = dy (m, n) deq(W) (n, k) + u A,   u = dy B (see fp4w_lora_backward)
+ * fp32 accumulation, rounded once to bf16.  The weight is decoded exactly (as
+ * fp4w_dequantize to bf16), the NVFP4 tensor scale multiplies its fp32 sums; u
+ * enters the bf16 matrix core as two bf16 parts (hi + lo, 2^-16 relative).
  *   dy_bf16    (m, n) bf16, 16-byte aligned;  n % 8 == 0 (else FP4W_ERR_SHAPE)
  *   codes, scales, tensor_scale   a quantized W (n, k), as fp4w_quantize writes it
+ *   lora_u     (m, r) fp32, 4-byte aligned, and lora_a (r, k) bf16, 2-byte aligned;
+ *              or both NULL / r == 0 (no LoRA term); r <= 64
  *   dx_bf16    (m, k) bf16, 8-byte aligned
- * m at most 65535 * 128.  n == 0 writes zeros; m == 0 or k == 0 does nothing.
- * A NaN block scale makes the outputs of its block's k columns NaN in every
- * row.  One launch on `stream`; no workspace.
+ * m at most 65535 * 128.  n == 0 writes u A (zeros without a LoRA); m == 0 or
+ * k == 0 does nothing.  A NaN block scale makes the outputs of its block's k
+ * columns NaN in every row.  One launch on `stream`; no workspace.
  */
 int fp4w_linear_backward_dx(int fmt, const void *dy_bf16, int64_t m, int64_t n,
                             const uint8_t *codes, const uint8_t *scales,
-                            const float *tensor_scale, int64_t k, void *dx_bf16,
-                            void *stream);
+                            const float *tensor_scale, int64_t k, const float *lora_u,
+                            const void *lora_a, int r, void *dx_bf16, void *stream);
+
+/*
+ * fp4w_lora_backward -- the gradients of the LoRA branch y_lora = (x A^T) B^T of
+ * fp4w_linear (the adapter trained in parallel to the frozen base; Telegram post,
+ * "Metod"), from the output gradient dy and the input x:
+ *   t = x A^T (m, r);   u = dy B (m, r);   dB = dy^T t (n, r);   dA = u^T x (r, k)
+ * all accumulated in fp32 on the bf16 matrix core (t and u enter the products
+ * over m as two bf16 parts, hi + lo); every sum in a fixed order.  u is what
+ * fp4w_linear_backward_dx takes for the adapter's share of dx.
+ *   dy_bf16 (m, n), x_bf16 (m, k): bf16, 16-byte aligned; n % 8 == 0, k % 32 == 0
+ *   lora_a (r, k) bf16 16-byte aligned; lora_b (n, r) bf16 2-byte aligned; 1 <= r <= 64
+ *   u (m, r), grad_a (r, k), grad_b (n, r): fp32 outputs, 4-byte aligned, each may
+ *     be NULL (not written); m == 0 writes zero gradients
+ *   workspace >= fp4w_lora_backward_workspace_bytes(m, n, k, r) bytes, 256-byte
+ *     aligned, no initial contents required
+ * Nine launches on `stream`.
+ */
+size_t fp4w_lora_backward_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
+int fp4w_lora_backward(const void *dy_bf16, int64_t m, int64_t n, const void *x_bf16, int64_t k,
+                       const void *lora_a, const void *lora_b, int r, float *u, float *grad_a,
+                       float *grad_b, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * fp4w_scale_delta_grad -- the Scale-QLoRA training gradient of the block-scale

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp4w.so")
 # measurement references for the benchmark (plain streaming read, clock probe); not the path
 MEMBENCH_LIB = os.path.join(HERE, "libfp4w_membench.so")
-SOURCES = ["api.hip", "quantize.hip", "dequantize.hip", "merge.hip", "linear.hip", "decode.hip", "decode_xs.hip", "grouped.hip", "gemm.hip", "a4w4.hip", "backward.hip", "delta_grad.hip", "aqn.hip"]
+SOURCES = ["api.hip", "quantize.hip", "dequantize.hip", "merge.hip", "linear.hip", "decode.hip", "decode_xs.hip", "grouped.hip", "gemm.hip", "a4w4.hip", "backward.hip", "lora_grad.hip", "delta_grad.hip", "aqn.hip"]
 ARCH = "gfx950"
 
 

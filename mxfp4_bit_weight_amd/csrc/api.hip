@@ -35,7 +35,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP4W_OK : FP4W_ERR_HIP; 
 
 extern "C" {
 
-int fp4w_version(void) { return 8; }
+int fp4w_version(void) { return 9; }
 
 const char* fp4w_status_string(int status) {
   switch (status) {
@@ -168,20 +168,52 @@ int fp4w_linear_w4a4(int fmt, const uint8_t* x_codes, const uint8_t* x_scales, i
 }
 
 int fp4w_linear_backward_dx(int fmt, const void* dy_bf16, int64_t m, int64_t n, const uint8_t* codes,
-                            const uint8_t* scales, const float* tensor_scale, int64_t k, void* dx_bf16, void* stream) {
+                            const uint8_t* scales, const float* tensor_scale, int64_t k, const float* lora_u,
+                            const void* lora_a, int r, void* dx_bf16, void* stream) {
   if (!valid_fmt(fmt)) return FP4W_ERR_FORMAT;
-  if (m < 0 || n < 0 || k < 0) return FP4W_ERR_ARG;
+  if (m < 0 || n < 0 || k < 0 || r < 0) return FP4W_ERR_ARG;
   int st = check_nk(n, k);
   if (st) return st;
   if (n % 8 != 0 || m > ((int64_t)65535 * 128) || n > 0x7FFFFFFF || k > 0x7FFFFFFF) return FP4W_ERR_SHAPE;
+  if (r > FP4W_MAX_LORA_RANK) return FP4W_ERR_SHAPE;
   if (m > 0 && n > kMaxElems / (m > 0 ? m : 1)) return FP4W_ERR_SHAPE;
   if (m == 0 || k == 0) return FP4W_OK;
   if (!dx_bf16 || (n > 0 && (!dy_bf16 || !codes || !scales))) return FP4W_ERR_ARG;
   if (fmt == FP4W_NVFP4 && !tensor_scale) return FP4W_ERR_ARG;
+  const bool lora = r > 0 && (lora_u || lora_a);
+  if (lora && (!lora_u || !lora_a)) return FP4W_ERR_ARG;
   if (!aligned16(dy_bf16) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(dx_bf16) & 7u) != 0)
     return FP4W_ERR_ALIGN;
+  if (lora && (((reinterpret_cast<uintptr_t>(lora_u) & 3u) != 0) || !aligned2(lora_a))) return FP4W_ERR_ALIGN;
   return hip_status(fp4w::launch_backward_dx(fmt, dy_bf16, m, n, codes, scales, tensor_scale, k, dx_bf16,
+                                             lora ? lora_u : nullptr, lora ? lora_a : nullptr, lora ? r : 0,
                                              as_stream(stream)));
+}
+
+size_t fp4w_lora_backward_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
+  if (m < 0 || n < 0 || k < 0 || r < 1 || r > FP4W_MAX_LORA_RANK) return 0;
+  if ((m > 0 && (n > kMaxElems / m || k > kMaxElems / m))) return 0;
+  return fp4w::lora_backward_workspace_bytes(m, n, k, r);
+}
+
+int fp4w_lora_backward(const void* dy_bf16, int64_t m, int64_t n, const void* x_bf16, int64_t k,
+                       const void* lora_a, const void* lora_b, int r, float* u, float* grad_a, float* grad_b,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (m < 0 || n < 0 || k < 0 || r < 0) return FP4W_ERR_ARG;
+  if (r < 1 || r > FP4W_MAX_LORA_RANK || k % 32 != 0 || n % 8 != 0) return FP4W_ERR_SHAPE;
+  if (m > 0 && (n > kMaxElems / m || k > kMaxElems / m)) return FP4W_ERR_SHAPE;
+  if (n > kMaxElems / r || k > kMaxElems / r) return FP4W_ERR_SHAPE;
+  if ((m > 0 && ((n > 0 && !dy_bf16) || (k > 0 && !x_bf16))) || (k > 0 && !lora_a) || (n > 0 && !lora_b))
+    return FP4W_ERR_ARG;
+  if (!aligned16(dy_bf16) || !aligned16(x_bf16) || !aligned16(lora_a) || !aligned2(lora_b)) return FP4W_ERR_ALIGN;
+  if (((reinterpret_cast<uintptr_t>(u) | reinterpret_cast<uintptr_t>(grad_a) | reinterpret_cast<uintptr_t>(grad_b)) &
+       3u) != 0)
+    return FP4W_ERR_ALIGN;
+  const size_t need = fp4w::lora_backward_workspace_bytes(m, n, k, r);
+  if (!workspace || workspace_bytes < need) return FP4W_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP4W_ERR_ALIGN;
+  return hip_status(fp4w::launch_lora_backward(dy_bf16, m, n, x_bf16, k, lora_a, lora_b, r, u, grad_a, grad_b,
+                                               workspace, as_stream(stream)));
 }
 
 int fp4w_scale_delta_grad(int fmt, const void* dy_bf16, const void* x_bf16, int64_t m, int64_t n, int64_t k,

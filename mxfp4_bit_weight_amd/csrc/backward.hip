@@ -48,7 +48,8 @@ __device__ __forceinline__ void bw_decode_byte(uint32_t c0, uint32_t c1, float s
 template <int FMT>
 __global__ __launch_bounds__(BW_THREADS, 2) void backward_dx_kernel(
     const uint16_t* __restrict__ dy, int M, int N, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int K, uint16_t* __restrict__ dx) {
+    const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int K, uint16_t* __restrict__ dx,
+    const float* __restrict__ lu, const uint16_t* __restrict__ la, int lr) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[BW_LDS];
   constexpr int BLK = FMT == FMT_NVFP4 ? 16 : 32;
   const int k0 = blockIdx.x * BW_BK, m0 = blockIdx.y * BW_BM;
@@ -142,9 +143,62 @@ __global__ __launch_bounds__(BW_THREADS, 2) void backward_dx_kernel(
     __syncthreads();
   }
 
-  // dX = s_t * acc, rounded once to bf16: lane (l32, hh), register 4 qq + e of
-  // tile (jk, im) is k = 32 jk + 8 qq + 4 hh + e, m = 32 im + l32 of the wave's block
+  // dX = s_t * acc (+ u A), rounded once to bf16: lane (l32, hh), register 4 qq + e
+  // of tile (jk, im) is k = 32 jk + 8 qq + 4 hh + e, m = 32 im + l32 of the wave's block
   const float st = FMT == FMT_NVFP4 ? *tensor_scale : 1.0f;
+#pragma unroll
+  for (int j = 0; j < 2; j++)
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int q = 0; q < 16; q++) acc[j][i][q] *= st;
+  if (lr > 0) {
+    // the LoRA term u A (u = dY B, fp32 (M, lr); A (lr, K) bf16) on the same
+    // matrix core: A^T of the block's 128 k staged in LDS ([k][j], 16-byte rows of
+    // 8 j), u split into two bf16 parts (hi + lo, 2^-16 relative) in registers
+    const int RB = (lr + 15) / 16;
+    constexpr int AS = 72;                          // bf16 per staged row: 64 j + 8 (bank spread)
+    uint16_t* at = reinterpret_cast<uint16_t*>(smem);
+    for (int e = tid; e < BW_BK * 16 * RB; e += BW_THREADS) {
+      const int jj = e / BW_BK, kk = e - jj * BW_BK;   // consecutive threads: consecutive k of one row of A
+      const int k = k0 + kk;
+      at[kk * AS + jj] = (jj < lr && k < K) ? la[(int64_t)jj * K + k] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int b = 0; b < RB; b++) {
+      bf16x8_t af[2], uh[2], ul[2];
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+        af[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(at + (64 * wk + 32 * j + l32) * AS + 16 * b + 8 * hh));
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        const int m = m0 + 64 * wm + 32 * i + l32;
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          float v[2];
+#pragma unroll
+          for (int d = 0; d < 2; d++) {
+            const int jj = 16 * b + 8 * hh + 2 * e + d;
+            v[d] = (m < M && jj < lr) ? lu[(int64_t)m * lr + jj] : 0.f;
+          }
+          const uint32_t h0 = f32_to_bf16_rne(v[0]), h1 = f32_to_bf16_rne(v[1]);
+          h[e] = h0 | (h1 << 16);
+          l[e] = f32_to_bf16_rne(v[0] - __uint_as_float(h0 << 16)) |
+                 (f32_to_bf16_rne(v[1] - __uint_as_float(h1 << 16)) << 16);
+        }
+        uh[i] = as_bf16x8((u32x4_t){h[0], h[1], h[2], h[3]});
+        ul[i] = as_bf16x8((u32x4_t){l[0], l[1], l[2], l[3]});
+      }
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j], uh[i], acc[j][i], 0, 0, 0);
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j], ul[i], acc[j][i], 0, 0, 0);
+        }
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 2; j++)
 #pragma unroll
@@ -156,7 +210,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void backward_dx_kernel(
         if (m < M && k < K) {
           uint32_t o[4];
 #pragma unroll
-          for (int e = 0; e < 4; e++) o[e] = f32_to_bf16_rne(acc[j][i][4 * qq + e] * st);
+          for (int e = 0; e < 4; e++) o[e] = f32_to_bf16_rne(acc[j][i][4 * qq + e]);
           *reinterpret_cast<uint2*>(dx + (int64_t)m * K + k) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
         }
       }
@@ -164,18 +218,18 @@ __global__ __launch_bounds__(BW_THREADS, 2) void backward_dx_kernel(
 }
 
 hipError_t launch_backward_dx(int fmt, const void* dy, int64_t m, int64_t n, const uint8_t* codes,
-                              const uint8_t* scales, const float* tensor_scale, int64_t k, void* dx,
-                              hipStream_t stream) {
+                              const uint8_t* scales, const float* tensor_scale, int64_t k, void* dx, const float* lu,
+                              const void* la, int lr, hipStream_t stream) {
   if (m == 0 || k == 0) return hipSuccess;
   const dim3 grid((unsigned)((k + BW_BK - 1) / BW_BK), (unsigned)((m + BW_BM - 1) / BW_BM));
   const uint16_t* y = reinterpret_cast<const uint16_t*>(dy);
   uint16_t* o = reinterpret_cast<uint16_t*>(dx);
   if (fmt == FMT_NVFP4)
     hipLaunchKernelGGL(backward_dx_kernel<FMT_NVFP4>, grid, dim3(BW_THREADS), 0, stream, y, (int)m, (int)n, codes,
-                       scales, tensor_scale, (int)k, o);
+                       scales, tensor_scale, (int)k, o, lu, reinterpret_cast<const uint16_t*>(la), lr);
   else
     hipLaunchKernelGGL(backward_dx_kernel<FMT_MXFP4>, grid, dim3(BW_THREADS), 0, stream, y, (int)m, (int)n, codes,
-                       scales, tensor_scale, (int)k, o);
+                       scales, tensor_scale, (int)k, o, lu, reinterpret_cast<const uint16_t*>(la), lr);
   return hipGetLastError();
 }
 

@@ -113,10 +113,18 @@ bool gemm_a4w4_supports(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_a4w4(const uint8_t* xc, const uint8_t* xs, int64_t m, int64_t k, const uint8_t* wc,
                             const uint8_t* ws, int64_t n, void* y, hipStream_t stream);
 
-// dX = dY deq(W) through the frozen base (backward.hip): n % 8 == 0, k % 32 == 0.
+// dX = dY deq(W) (+ u A) through the frozen base (backward.hip): n % 8 == 0, k % 32 == 0;
+// lu (m, lr) fp32 and la (lr, k) bf16, or lr == 0.
 hipError_t launch_backward_dx(int fmt, const void* dy, int64_t m, int64_t n, const uint8_t* codes,
-                              const uint8_t* scales, const float* tensor_scale, int64_t k, void* dx,
-                              hipStream_t stream);
+                              const uint8_t* scales, const float* tensor_scale, int64_t k, void* dx, const float* lu,
+                              const void* la, int lr, hipStream_t stream);
+
+// LoRA gradients (lora_grad.hip): u = dY B (m, r), dA = u^T x (r, k), dB = dY^T t
+// (n, r) with t = x A^T, all fp32; n % 8 == 0, k % 32 == 0, 1 <= r <= 64.
+size_t lora_backward_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
+hipError_t launch_lora_backward(const void* dy, int64_t m, int64_t n, const void* x, int64_t k, const void* la,
+                                const void* lb, int r, float* u_out, float* grad_a, float* grad_b, void* workspace,
+                                hipStream_t stream);
 
 // Scale-QLoRA delta gradient (delta_grad.hip): n % 8 == 0, k % 32 == 0.
 hipError_t launch_delta_grad(int fmt, const void* dy, const void* x, int64_t m, int64_t n, int64_t k,

@@ -47,7 +47,9 @@ _ws_bytes = _sig("fp4w_linear_workspace_bytes", _sz, _i64, _i64, _i64, _int)
 _linear = _sig("fp4w_linear", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _int, _p, _p, _sz, _p)
 _linear_noalloc = _sig("fp4w_linear_noalloc", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _int, _p, _p)
 _w4a4 = _sig("fp4w_linear_w4a4", _int, _int, _p, _p, _i64, _i64, _p, _p, _i64, _p, _p)
-_bwd_dx = _sig("fp4w_linear_backward_dx", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p)
+_bwd_dx = _sig("fp4w_linear_backward_dx", _int, _int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _int, _p, _p)
+_lora_bwd_ws = _sig("fp4w_lora_backward_workspace_bytes", _sz, _i64, _i64, _i64, _int)
+_lora_bwd = _sig("fp4w_lora_backward", _int, _p, _i64, _i64, _p, _i64, _p, _p, _int, _p, _p, _p, _p, _sz, _p)
 _delta_grad = _sig("fp4w_scale_delta_grad", _int, _int, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p)
 _aqn = _sig("fp4w_aqn_rmsnorm", _int, _p, _i64, _i64, _p, _p, ctypes.c_float, ctypes.c_float, _p, _p)
 _aqn_sigma = _sig("fp4w_aqn_sigma", ctypes.c_double, _i64, _i64, ctypes.c_double, ctypes.c_double)
@@ -60,7 +62,8 @@ _debug_lora_wait = _sig("fp4w_debug_lora_wait", _i64, _i64)
 EXPORTED = ["fp4w_quantize", "fp4w_dequantize", "fp4w_linear_workspace_bytes", "fp4w_linear",
             "fp4w_grouped_linear", "fp4w_merge_scales", "fp4w_status_string", "fp4w_version",
             "fp4w_debug_lora_wait", "fp4w_fake_quant", "fp4w_linear_w4a4", "fp4w_linear_backward_dx",
-            "fp4w_scale_delta_grad", "fp4w_aqn_rmsnorm", "fp4w_aqn_sigma", "fp4w_linear_noalloc"]
+            "fp4w_scale_delta_grad", "fp4w_aqn_rmsnorm", "fp4w_aqn_sigma", "fp4w_linear_noalloc",
+            "fp4w_lora_backward", "fp4w_lora_backward_workspace_bytes"]
 
 
 class Fp4wError(RuntimeError):
@@ -291,17 +294,54 @@ def linear_a4(x: torch.Tensor, q: QWeight, out: Optional[torch.Tensor] = None) -
     return linear_w4a4(quantize(x, MXFP4), q, out)
 
 
-def linear_backward_dx(dy: torch.Tensor, q: QWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """fp4w_linear_backward_dx: dx = dy deq(W) (the input gradient through the
-    frozen base), bf16 in and out, fp32 accumulation."""
+def linear_backward_dx(dy: torch.Tensor, q: QWeight, out: Optional[torch.Tensor] = None,
+                       lora_u: Optional[torch.Tensor] = None, lora_a: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4w_linear_backward_dx: dx = dy deq(W) (+ u A with the adapter's u = dy B
+    from ``lora_backward`` and its A), bf16 in and out, fp32 accumulation."""
     _need(dy, torch.bfloat16, "dy")
     m, n = dy.shape
     if n != q.n:
         raise ValueError(f"dy has n={n}, the weight n={q.n}")
+    r = 0
+    if lora_u is not None or lora_a is not None:
+        _need(lora_u, torch.float32, "lora_u")
+        _need(lora_a, torch.bfloat16, "lora_a")
+        r = lora_a.shape[0]
+        if lora_a.shape != (r, q.k) or lora_u.shape != (m, r):
+            raise ValueError("lora_a must be (r, k) and lora_u (m, r)")
     dx = _out(out, (m, q.k), torch.bfloat16, dy.device)
-    _check(_bwd_dx(q.fmt, _ptr(dy), m, n, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.k, _ptr(dx),
-                   _stream(dy.device)), "fp4w_linear_backward_dx")
+    _check(_bwd_dx(q.fmt, _ptr(dy), m, n, _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.k, _ptr(lora_u),
+                   _ptr(lora_a), r, _ptr(dx), _stream(dy.device)), "fp4w_linear_backward_dx")
     return dx
+
+
+def lora_backward_workspace_bytes(m: int, n: int, k: int, r: int) -> int:
+    return int(_lora_bwd_ws(m, n, k, r))
+
+
+def lora_backward(dy: torch.Tensor, x: torch.Tensor, lora_a: torch.Tensor, lora_b: torch.Tensor,
+                  workspace: Optional[torch.Tensor] = None):
+    """fp4w_lora_backward: (u, grad_a, grad_b) for the adapter y_lora = (x A^T) B^T,
+    u = dy B (m, r), dA = u^T x (r, k), dB = dy^T (x A^T) (n, r), all fp32."""
+    _need(dy, torch.bfloat16, "dy")
+    _need(x, torch.bfloat16, "x")
+    _need(lora_a, torch.bfloat16, "lora_a")
+    _need(lora_b, torch.bfloat16, "lora_b")
+    m, n = dy.shape
+    r, k = lora_a.shape
+    if x.shape != (m, k) or lora_b.shape != (n, r):
+        raise ValueError("dy (m, n), x (m, k), lora_a (r, k) and lora_b (n, r) must agree")
+    dev = dy.device
+    u = torch.empty((m, r), dtype=torch.float32, device=dev)
+    ga = torch.empty((r, k), dtype=torch.float32, device=dev)
+    gb = torch.empty((n, r), dtype=torch.float32, device=dev)
+    nbytes = lora_backward_workspace_bytes(m, n, k, r)
+    if nbytes == 0:
+        raise ValueError("invalid lora_backward shape")
+    ws = workspace if workspace is not None else torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(_lora_bwd(_ptr(dy), m, n, _ptr(x), k, _ptr(lora_a), _ptr(lora_b), r, _ptr(u), _ptr(ga), _ptr(gb),
+                     _ptr(ws), ws.numel(), _stream(dev)), "fp4w_lora_backward")
+    return u, ga, gb
 
 
 def scale_delta_grad(dy: torch.Tensor, x: torch.Tensor, q: QWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -132,14 +132,19 @@ def test_w4a4_validation_without_launch(lib):
 def test_backward_delta_aqn_validation_without_launch(lib):
     A = 0x10000
     f = lib._bwd_dx
-    assert f(7, _fake(A), 4, 8, _fake(A), _fake(A), _fake(A), 32, _fake(A), None) == -4     # format
-    assert f(0, _fake(A), -1, 8, _fake(A), _fake(A), _fake(A), 32, _fake(A), None) == -1    # negative
-    assert f(0, _fake(A), 4, 12, _fake(A), _fake(A), _fake(A), 32, _fake(A), None) == -2    # n % 8
-    assert f(0, _fake(A), 4, 8, _fake(A), _fake(A), _fake(A), 48, _fake(A), None) == -2    # k % 32
-    assert f(0, _fake(A), 4, 8, _fake(A), _fake(A), None, 32, _fake(A), None) == -1        # NVFP4 tensor scale
-    assert f(1, _fake(A + 8), 4, 8, _fake(A), _fake(A), None, 32, _fake(A), None) == -3    # dy alignment
-    assert f(1, _fake(A), 4, 8, _fake(A), _fake(A), None, 32, _fake(A + 4), None) == -3    # dx alignment
-    assert f(1, None, 0, 8, None, None, None, 32, None, None) == 0                          # m = 0
+    assert f(7, _fake(A), 4, 8, _fake(A), _fake(A), _fake(A), 32, None, None, 0, _fake(A), None) == -4     # format
+    assert f(0, _fake(A), -1, 8, _fake(A), _fake(A), _fake(A), 32, None, None, 0, _fake(A), None) == -1    # negative
+    assert f(0, _fake(A), 4, 12, _fake(A), _fake(A), _fake(A), 32, None, None, 0, _fake(A), None) == -2    # n % 8
+    assert f(0, _fake(A), 4, 8, _fake(A), _fake(A), _fake(A), 48, None, None, 0, _fake(A), None) == -2    # k % 32
+    assert f(0, _fake(A), 4, 8, _fake(A), _fake(A), None, 32, None, None, 0, _fake(A), None) == -1        # NVFP4 tensor scale
+    assert f(1, _fake(A + 8), 4, 8, _fake(A), _fake(A), None, 32, None, None, 0, _fake(A), None) == -3    # dy alignment
+    assert f(1, _fake(A), 4, 8, _fake(A), _fake(A), None, 32, None, None, 0, _fake(A + 4), None) == -3    # dx alignment
+    assert f(1, None, 0, 8, None, None, None, 32, None, None, 0, None, None) == 0                          # m = 0
+    # the LoRA term: both operands or neither, rank <= 64, alignment
+    assert f(0, _fake(A), 4, 8, _fake(A), _fake(A), _fake(A), 32, _fake(A), None, 16, _fake(A), None) == -1
+    assert f(0, _fake(A), 4, 8, _fake(A), _fake(A), _fake(A), 32, _fake(A), _fake(A), 65, _fake(A), None) == -2
+    assert f(0, _fake(A), 4, 8, _fake(A), _fake(A), _fake(A), 32, _fake(A + 2), _fake(A), 16, _fake(A), None) == -3
+    assert f(0, _fake(A), 4, 8, _fake(A), _fake(A), _fake(A), 32, _fake(A), _fake(A + 1), 16, _fake(A), None) == -3
     g = lib._delta_grad
     assert g(7, _fake(A), _fake(A), 4, 8, 32, _fake(A), _fake(A), _fake(A), None) == -4
     assert g(0, _fake(A), _fake(A), 4, 12, 32, _fake(A), _fake(A), _fake(A), None) == -2   # n % 8
@@ -171,3 +176,25 @@ def test_noalloc_validation_without_launch(lib):
     assert lib.linear_workspace_bytes(m, n, k, r) > lib.NOALLOC_SCRATCH_BYTES
     assert f(0, _fake(A), m, k, _fake(A), _fake(A), _fake(A), n, _fake(A), _fake(A), r, _fake(A), None) == -7
     assert "no-allocation" in lib.status_string(-7)
+
+
+def test_lora_backward_validation_without_launch(lib):
+    f = lib._lora_bwd
+    A = 0x10000
+    ws = lib.lora_backward_workspace_bytes(64, 48, 96, 16)
+    assert ws > 0 and lib.lora_backward_workspace_bytes(64, 48, 96, 0) == 0 and lib.lora_backward_workspace_bytes(4, 8, 32, 65) == 0
+
+    def call(**kw):
+        v = dict(dy=_fake(A), m=64, n=48, x=_fake(A), k=96, a=_fake(A), b=_fake(A), r=16, u=_fake(A), ga=_fake(A),
+                 gb=_fake(A), ws=_fake(A), wsb=ws)
+        v.update(kw)
+        return f(v["dy"], v["m"], v["n"], v["x"], v["k"], v["a"], v["b"], v["r"], v["u"], v["ga"], v["gb"], v["ws"],
+                 v["wsb"], None)
+    assert call(m=-1) == -1
+    assert call(r=0) == -2 and call(r=65) == -2
+    assert call(k=80) == -2 and call(n=44) == -2
+    assert call(dy=None) == -1 and call(a=None) == -1 and call(b=None) == -1
+    assert call(x=_fake(A + 8)) == -3 and call(a=_fake(A + 2)) == -3 and call(b=_fake(A + 1)) == -3
+    assert call(gb=_fake(A + 2)) == -3
+    assert call(wsb=ws - 1) == -6 and call(ws=None) == -6
+    assert call(ws=_fake(A + 16)) == -3

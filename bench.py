@@ -519,10 +519,18 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
         fp4w.aqn_rmsnorm(d["x1"], gam, noise, sig, 1e-6, out=xn)
         fp4w.linear(xn, q, a, b, out=yn, workspace=ws)
     nms, _ = time_graph(norm_linear, reps, 5)
+    aws = torch.zeros(fp4w.linear_aqn_workspace_bytes(1, d["n"], d["k"], rank), dtype=torch.uint8, device=dev)
+
+    def fused(i):
+        q, a, b = d["qs"][i % len(d["qs"])]
+        fp4w.linear_aqn(d["x1"], gam, noise, sig, q, a, b, eps=1e-6, out=yn, workspace=aws)
+    fms, _ = time_graph(fused, reps, 5)
     rows["aqn_rmsnorm_m1_k3584"] = {"us": round(ams * 1e3, 2),
                                     "us_with_gate_up_linear_nvfp4": round(nms * 1e3, 2),
+                                    "us_fused_into_gate_up_linear_nvfp4": round(fms * 1e3, 2),
                                     "linear_alone_us": dec["nvfp4/gate_up/M1"]["us"]}
-    log(f"[bench] noisy RMSNorm {ams * 1e3:.2f} us, with the gate/up linear {nms * 1e3:.2f} us")
+    log(f"[bench] noisy RMSNorm {ams * 1e3:.2f} us, then the gate/up linear {nms * 1e3:.2f} us, "
+        f"fused {fms * 1e3:.2f} us")
 
     weights = {fmt: (*decode[(fmt, "gate_up")]["qs"][0], decode[(fmt, "gate_up")]["n"], decode[(fmt, "gate_up")]["k"])
                for fmt in (0, 1)}

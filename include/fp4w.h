@@ -302,6 +302,37 @@ int fp4w_aqn_rmsnorm(const void *x_bf16, int64_t m, int64_t k, const void *gamma
 double fp4w_aqn_sigma(int64_t step, int64_t total_steps, double sigma_max, double sigma_min);
 
 /*
+ * Workspace for fp4w_linear_aqn, in bytes: fp4w_linear_workspace_bytes(m, n, k,
+ * r) rounded up to 256, plus m * k * 2 (the normalized x where the norm runs as
+ * a launch of its own) rounded up to 256; 0 for invalid arguments.  Its first
+ * bytes are fp4w_linear's counter area, with the same zero-fill rule.
+ */
+size_t fp4w_linear_aqn_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
+
+/*
+ * fp4w_linear_aqn -- the linear of the noisy RMSNorm of x: y = fp4w_linear of
+ * x~ (m, k), x~ = x / sqrt(mean(x^2) + eps) * gamma * (1 + sigma * noise) per row
+ * (the norm of fp4w_aqn_rmsnorm, the projection that follows it; Telegram post,
+ * "Metod": noise in the RMS norm before the projections).  Arguments are
+ * fp4w_aqn_rmsnorm's (gamma_bf16, noise, sigma, eps) followed by fp4w_linear's;
+ * gamma and noise 16-byte aligned, workspace 256-byte aligned and at least
+ * fp4w_linear_aqn_workspace_bytes(m, n, k, r).
+ * Where the linear runs as one decode launch over the whole K (m <= 2 and no K
+ * split, as for k = 3584 at any n of the Qwen-2.5-7B projections) the norm runs
+ * inside it: each workgroup forms bf16(x * gamma * (1 + sigma * noise)) while
+ * staging x, sums x^2 of its rows in fp32, and multiplies its fp32 outputs (with
+ * the LoRA term) by 1 / sqrt(mean(x^2) + eps) before the one rounding to bf16.
+ * Elsewhere fp4w_aqn_rmsnorm writes x~ into the workspace and fp4w_linear reads
+ * it.  Both round x~ (or x~ without the row factor) to bf16 once: the outputs
+ * are within the linear's bound of x~ plus 2^-8 of sum_k |x~_k w_k|.
+ */
+int fp4w_linear_aqn(int fmt, const void *x_bf16, int64_t m, int64_t k, const void *gamma_bf16,
+                    const float *noise, float sigma, float eps, const uint8_t *codes,
+                    const uint8_t *scales, const float *tensor_scale, int64_t n,
+                    const void *lora_a, const void *lora_b, int r, void *y_bf16,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * fp4w_grouped_linear -- the W4A16 linear over the experts of a mixture of
  * experts (QATFactory page: dense and MoE models; Nemotron page: 30B-A3B base).
  * For every expert e and every row q in [expert_offsets[e], expert_offsets[e+1]):

@@ -35,7 +35,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP4W_OK : FP4W_ERR_HIP; 
 
 extern "C" {
 
-int fp4w_version(void) { return 9; }
+int fp4w_version(void) { return 10; }
 
 const char* fp4w_status_string(int status) {
   switch (status) {
@@ -152,6 +152,30 @@ int fp4w_linear(int fmt, const void* x_bf16, int64_t m, int64_t k, const uint8_t
   return hip_status(fp4w::launch_linear(fmt, x_bf16, m, k, codes, scales, tensor_scale, n, lora ? lora_a : nullptr,
                                         lora ? lora_b : nullptr, lora ? r : 0, y_bf16, workspace, plan,
                                         as_stream(stream)));
+}
+
+size_t fp4w_linear_aqn_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
+  if (m < 0 || n < 0 || k < 0 || r < 0 || r > FP4W_MAX_LORA_RANK) return 0;
+  if (m > 0 && k > 0 && m > kMaxElems / k) return 0;
+  return fp4w::linear_aqn_workspace_bytes(fp4w::plan_linear(m, n, k, r), m, k);
+}
+
+int fp4w_linear_aqn(int fmt, const void* x_bf16, int64_t m, int64_t k, const void* gamma_bf16, const float* noise,
+                    float sigma, float eps, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                    int64_t n, const void* lora_a, const void* lora_b, int r, void* y_bf16, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  bool nothing = false, lora = false;
+  fp4w::LinearPlan plan{};
+  int st = linear_check(fmt, x_bf16, m, k, codes, scales, tensor_scale, n, lora_a, lora_b, r, y_bf16, &nothing,
+                        &lora, &plan);
+  if (st || nothing) return st;
+  if (k > 0 && (!gamma_bf16 || !noise)) return FP4W_ERR_ARG;
+  if (k > 0 && (!aligned16(gamma_bf16) || !aligned16(noise))) return FP4W_ERR_ALIGN;
+  if (!workspace || workspace_bytes < fp4w::linear_aqn_workspace_bytes(plan, m, k)) return FP4W_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP4W_ERR_ALIGN;
+  return hip_status(fp4w::launch_linear_aqn(fmt, x_bf16, m, k, gamma_bf16, noise, sigma, eps, codes, scales,
+                                            tensor_scale, n, lora ? lora_a : nullptr, lora ? lora_b : nullptr,
+                                            lora ? r : 0, y_bf16, workspace, plan, as_stream(stream)));
 }
 
 int fp4w_linear_w4a4(int fmt, const uint8_t* x_codes, const uint8_t* x_scales, int64_t m, int64_t k,

@@ -98,16 +98,23 @@ __host__ __device__ inline DqLayout dq_layout(int fmt, int m, int kslice, int nw
   return L;
 }
 
-template <int FMT, int NQ, int NW, int DEPTH, bool LORA>
-__global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
+template <int FMT, int NQ, int NW, int DEPTH, bool LORA, bool AQN>
+// The fused norm's gain staging takes ~20 more VGPRs: held to 5 waves per SIMD at
+// ring depth 8 (else a few AGPRs push the LoRA variant to 4, and a 4-wave grid of
+// 1191 groups no longer fits the chip in one round)
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(AQN && DEPTH <= 8 ? 5 : 1)))
+void decode_f8f4_kernel(
     const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t N,
     const uint16_t* __restrict__ lora_a, const uint16_t* __restrict__ lora_b, int r,
     int lparts, int lsw, uint32_t* __restrict__ lsync, uint16_t* __restrict__ y, float* __restrict__ part,
     uint32_t* __restrict__ cnt, int S, int sps, int nsteps_total, int ntiles, int scales16,
-    uint64_t wait_ticks) {
+    uint64_t wait_ticks, const uint16_t* __restrict__ gam, const float* __restrict__ noise, float sigma,
+    float eps) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int flag;
+  __shared__ float aqn_ss[AQN ? NW : 1][2];                       // AQN: per-wave sums of x^2, rows 0 and 1
+  const XGain xg = AQN ? XGain{gam, noise, sigma} : XGain{nullptr, nullptr, 0.f};
   __shared__ int lfin, have_t;                                    // LoRA: waves done streaming; t published
   constexpr int NT = 64 * NW;
   constexpr int BLK = FMT == FMT_NVFP4 ? 16 : 32;
@@ -127,7 +134,7 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
   float* lr = reinterpret_cast<float*>(lds + L.lr_off);            // [wave][m][j]: a LoRA chunk
   if (LORA && bid < 0) {
     // ---- 0. a chunk workgroup: its partial of t, complemented, then its arrival --
-    lora_chunk_publish(lr, x, M, K, lora_a, rr, (int)blockIdx.x, NW, lsw, lsync, nread, lparts);
+    lora_chunk_publish(lr, x, M, K, lora_a, rr, (int)blockIdx.x, NW, lsw, lsync, nread, lparts, xg);
     return;
   }
 
@@ -149,6 +156,19 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
     const bool ok = u < xunits && k0 + kk < K;
     xv[c] = load16(x + (ok ? (int64_t)m * K + k0 + kk : 0));
     if (!ok) xv[c] = (u32x4_t){0u, 0u, 0u, 0u};
+  }
+  // AQN: the gain's gamma and noise at the same k (one K slice: k0 = 0)
+  u32x4_t gv[DQ_XPRE], nv0[DQ_XPRE], nv1[DQ_XPRE];
+  if (AQN) {
+#pragma unroll
+    for (int c = 0; c < DQ_XPRE; c++) {
+      const int u = tid + c * NT;
+      const int m = u / xunits_row, kk = 8 * (u - m * xunits_row);
+      const int64_t ko = u < xunits && k0 + kk < K ? k0 + kk : 0;
+      gv[c] = load16(gam + ko);
+      nv0[c] = load16(noise + ko);
+      nv1[c] = load16(noise + ko + 4);
+    }
   }
   const int64_t krem = K - k0;
   const int svalid = (int)((krem < kslice ? krem : kslice) / BLK);   // scale bytes of a row in this slice
@@ -192,6 +212,7 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 3. encode x into LDS; zeros; scale bytes; LoRA operands ------------------
+  float ssq[2] = {0.f, 0.f};                         // AQN: this thread's sums of x^2, rows 0 and 1
   auto put_x = [&](int u, u32x4_t v) {
     const XEnc8 e = encode_x8(v);
     if (u < xunits) {
@@ -207,17 +228,43 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
     }
   };
   // quads of lanes hold one 32-element block: all four take the same branch
+  // AQN: x enters as bf16(x g), g = gamma (1 + sigma noise); the row factor
+  // 1 / sqrt(mean x^2 + eps) multiplies the fp32 sums at the end
+  auto gain = [&](int u, u32x4_t v, u32x4_t g_, u32x4_t n0, u32x4_t n1) -> u32x4_t {
+    if (!AQN) return v;
+    const int m = u / xunits_row;
+    float s2 = 0.f;
+    const u32x4_t o = xgain_bf16(v, g_, n0, n1, sigma, &s2);
+    if (u < xunits) {
+      if (m == 0) ssq[0] += s2;
+      else ssq[1] += s2;
+    }
+    return o;
+  };
 #pragma unroll
   for (int c = 0; c < DQ_XPRE; c++) {
     const int u = tid + c * NT;
-    if (u - (u & 3) < xunits) put_x(u, xv[c]);
+    if (u - (u & 3) < xunits) put_x(u, AQN ? gain(u, xv[c], gv[c], nv0[c], nv1[c]) : xv[c]);
   }
   for (int u = tid + DQ_XPRE * NT; u - (u & 3) < xunits; u += NT) {
     const int m = u / xunits_row, kk = 8 * (u - m * xunits_row);
     const bool ok = u < xunits && k0 + kk < K;
     u32x4_t v = load16(x + (ok ? (int64_t)m * K + k0 + kk : 0));
     if (!ok) v = (u32x4_t){0u, 0u, 0u, 0u};
+    if (AQN) {
+      const int64_t ko = ok ? k0 + kk : 0;
+      v = gain(u, v, load16(gam + ko), load16(noise + ko), load16(noise + ko + 4));
+    }
     put_x(u, v);
+  }
+  if (AQN) {                                         // per-wave sums, in lane order
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      float v = ssq[q];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      if (lane == 0) aqn_ss[wave][q] = v;
+    }
   }
   for (int u = tid; u < DQ_STEP * (L.spw + 1) / 16; u += NT)
     *reinterpret_cast<u32x4_t*>(lds + L.zero_off + 16 * u) = (u32x4_t){0u, 0u, 0u, 0u};
@@ -442,7 +489,7 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
   if (LORA && __builtin_expect(!have_t, 0)) {
     // ---- 6. the wait for t ran out: the chunks formed here, by the same steps in
     //      the same order -----------------------------------------------------------
-    lora_form_all(lr, reinterpret_cast<float*>(lds + L.lt_off), x, M, K, lora_a, rr, NW, lsw, lparts);
+    lora_form_all(lr, reinterpret_cast<float*>(lds + L.lt_off), x, M, K, lora_a, rr, NW, lsw, lparts, xg);
   }
   if (e < nout) {
     const int m = e / DQ_ROWS, nn = e - m * DQ_ROWS;
@@ -456,6 +503,11 @@ __global__ __launch_bounds__(64 * NW) void decode_f8f4_kernel(
         float l = 0.f;
         for (int j = 0; j < rr; j++) l = __builtin_fmaf(lt[m * rr + j], __uint_as_float((uint32_t)lb[nn * rr + j] << 16), l);
         out += l;
+      }
+      if (AQN) {                                     // the row factor of the norm, waves in order
+        float ss = 0.f;
+        for (int w = 0; w < NW; w++) ss += aqn_ss[w][m];
+        out *= 1.0f / __builtin_sqrtf(ss / (float)K + eps);
       }
       y[(int64_t)m * N + row] = (uint16_t)f32_to_bf16_rne(out);
     }
@@ -516,36 +568,45 @@ int64_t lora_wait_ticks() { return g_lora_wait.load(std::memory_order_relaxed); 
 int64_t set_lora_wait_ticks(int64_t ticks) { return g_lora_wait.exchange(ticks, std::memory_order_relaxed); }
 
 
-template <int FMT, int NQ>
+template <int FMT, int NQ, bool AQN>
 static void launch_nq(const DecodeConfig& c, dim3 grid, size_t lds, hipStream_t stream, const uint16_t* x, int m,
                       int64_t k, const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t n,
-                      const uint16_t* la, const uint16_t* lb, int r, int lparts, int lsw, uint32_t* lsync, uint16_t* y, float* part, uint32_t* cnt, int nsteps, int ntiles,
-                      int scales16) {
+                      const uint16_t* la, const uint16_t* lb, int r, int lparts, int lsw, uint32_t* lsync, uint16_t* y,
+                      float* part, uint32_t* cnt, int nsteps, int ntiles, int scales16, const uint16_t* gam,
+                      const float* noise, float sigma, float eps) {
 #define FP4W_DQ(W, D)                                                                                        \
   do {                                                                                                       \
     if (r > 0)                                                                                               \
-      hipLaunchKernelGGL((decode_f8f4_kernel<FMT, NQ, W, D, true>), grid, dim3(64 * W), lds, stream, x, m, k,  \
-                         codes, scales, ts, n, la, lb, r, lparts, lsw, lsync, y, part, cnt, c.splits, c.sps, nsteps, \
-                         ntiles, scales16, (uint64_t)lora_wait_ticks());                                     \
+      hipLaunchKernelGGL((decode_f8f4_kernel<FMT, NQ, W, D, true, AQN>), grid, dim3(64 * W), lds, stream, x, m, \
+                         k, codes, scales, ts, n, la, lb, r, lparts, lsw, lsync, y, part, cnt, c.splits, c.sps,      \
+                         nsteps, ntiles, scales16, (uint64_t)lora_wait_ticks(), gam, noise, sigma, eps);         \
     else                                                                                                     \
-      hipLaunchKernelGGL((decode_f8f4_kernel<FMT, NQ, W, D, false>), grid, dim3(64 * W), lds, stream, x, m, k, \
-                         codes, scales, ts, n, la, lb, r, lparts, lsw, lsync, y, part, cnt, c.splits, c.sps, nsteps, \
-                         ntiles, scales16, (uint64_t)0);                                                     \
+      hipLaunchKernelGGL((decode_f8f4_kernel<FMT, NQ, W, D, false, AQN>), grid, dim3(64 * W), lds, stream, x, m, \
+                         k, codes, scales, ts, n, la, lb, r, lparts, lsw, lsync, y, part, cnt, c.splits, c.sps,      \
+                         nsteps, ntiles, scales16, (uint64_t)0, gam, noise, sigma, eps);                        \
   } while (0)
   if (c.nw == 4) {
     if (c.depth <= 8) FP4W_DQ(4, 8); else FP4W_DQ(4, 16);
   } else if (c.nw == 8 || (FMT == FMT_NVFP4 && NQ > 1)) {
     if (c.depth <= 8) FP4W_DQ(8, 8); else FP4W_DQ(8, 16);
-  } else if constexpr (FMT == FMT_MXFP4 || NQ == 1) {
+  } else if constexpr (!AQN && (FMT == FMT_MXFP4 || NQ == 1)) {
     if (c.depth <= 8) FP4W_DQ(16, 8); else FP4W_DQ(16, 16);
   }
 #undef FP4W_DQ
 }
 
+// The fused norm: one K slice (the row's sum of squares in one workgroup), m <= 2
+// (two per-thread sums), at most 8 waves (16-wave groups would spill the gain's
+// prefetched gamma and noise).
+bool decode_f8f4_fuses_aqn(const DecodeConfig& c, int64_t m) {
+  return m >= 1 && m <= 2 && c.splits == 1 && c.nw <= 8;
+}
+
 hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c0, const void* x, int64_t m, int64_t k,
                               const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t n,
                               const void* la, const void* lb, int r, uint32_t* lsync, void* y, float* part,
-                              uint32_t* cnt, hipStream_t stream) {
+                              uint32_t* cnt, hipStream_t stream, const void* aqn_gamma, const float* aqn_noise,
+                              float aqn_sigma, float aqn_eps) {
   DecodeConfig c = c0;
   const int nq = fmt == FMT_NVFP4 ? (int)m : (int)((m + 7) / 8);
   if (fmt == FMT_NVFP4 && nq > 1 && c.nw > 8) c.nw = 8;   // 16-wave groups only for one chain (else they spill)
@@ -567,12 +628,26 @@ hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c0, const void* x, in
   const uint16_t* bb = reinterpret_cast<const uint16_t*>(lb);
   uint16_t* yy = reinterpret_cast<uint16_t*>(y);
   const int mm = (int)m;
+  const uint16_t* gam = reinterpret_cast<const uint16_t*>(aqn_gamma);
+  if (gam) {                                       // the fused noisy RMSNorm: one K slice, m <= 2
+    if (!decode_f8f4_fuses_aqn(c, m) || !aqn_noise) return hipErrorInvalidValue;
+    if (fmt == FMT_NVFP4 && mm == 2)
+      launch_nq<FMT_NVFP4, 2, true>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, aa, bb, rr, lparts, lsw,
+                                    lsync, yy, part, cnt, nsteps, ntiles, scales16, gam, aqn_noise, aqn_sigma, aqn_eps);
+    else if (fmt == FMT_NVFP4)
+      launch_nq<FMT_NVFP4, 1, true>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, aa, bb, rr, lparts, lsw,
+                                    lsync, yy, part, cnt, nsteps, ntiles, scales16, gam, aqn_noise, aqn_sigma, aqn_eps);
+    else
+      launch_nq<FMT_MXFP4, 1, true>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, aa, bb, rr, lparts, lsw,
+                                    lsync, yy, part, cnt, nsteps, ntiles, scales16, gam, aqn_noise, aqn_sigma, aqn_eps);
+    return hipSuccess;
+  }
   if (fmt == FMT_NVFP4) {
     switch (mm) {
 #define FP4W_NQ(Q_)                                                                                        \
   case Q_:                                                                                                 \
-    launch_nq<FMT_NVFP4, Q_>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, aa, bb, rr, lparts, lsw, lsync, \
-                             yy, part, cnt, nsteps, ntiles, scales16);                                     \
+    launch_nq<FMT_NVFP4, Q_, false>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, aa, bb, rr, lparts, lsw, \
+                                    lsync, yy, part, cnt, nsteps, ntiles, scales16, nullptr, nullptr, 0.f, 0.f);   \
     break;
       FP4W_NQ(1) FP4W_NQ(2) FP4W_NQ(3) FP4W_NQ(4) FP4W_NQ(5) FP4W_NQ(6) FP4W_NQ(7) FP4W_NQ(8)
 #undef FP4W_NQ
@@ -580,11 +655,11 @@ hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c0, const void* x, in
     }
   } else {
     if (mm <= 8)
-      launch_nq<FMT_MXFP4, 1>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, aa, bb, rr, lparts, lsw, lsync, yy,
-                              part, cnt, nsteps, ntiles, scales16);
+      launch_nq<FMT_MXFP4, 1, false>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, aa, bb, rr, lparts, lsw,
+                                     lsync, yy, part, cnt, nsteps, ntiles, scales16, nullptr, nullptr, 0.f, 0.f);
     else
-      launch_nq<FMT_MXFP4, 2>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, aa, bb, rr, lparts, lsw, lsync, yy,
-                              part, cnt, nsteps, ntiles, scales16);
+      launch_nq<FMT_MXFP4, 2, false>(c, grid, lds, stream, xx, mm, k, codes, scales, ts, n, aa, bb, rr, lparts, lsw,
+                                     lsync, yy, part, cnt, nsteps, ntiles, scales16, nullptr, nullptr, 0.f, 0.f);
   }
   return hipSuccess;
 }

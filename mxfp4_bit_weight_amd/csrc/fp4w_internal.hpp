@@ -59,10 +59,15 @@ int64_t set_lora_wait_ticks(int64_t ticks);      // returns the previous bound
 // la / lb: LoRA A (r x k bf16) and B (n x r bf16), or nullptr (no LoRA); the
 // kernel forms t = x A^T itself (K chunks in workgroups of their own, handed
 // over through lsync: the kLsyncSlots words of the counter area from kLsyncBase)
+// aqn_gamma non-null: the noisy RMSNorm fused into the x staging (one K slice, m <= 2;
+// decode_f8f4_fuses_aqn): x enters as bf16(x gamma (1 + sigma noise)), the row factor
+// 1 / sqrt(mean x^2 + eps) multiplies the fp32 sums.
+bool decode_f8f4_fuses_aqn(const DecodeConfig& c, int64_t m);
 hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c, const void* x, int64_t m, int64_t k,
                               const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t n,
                               const void* la, const void* lb, int r, uint32_t* lsync, void* y, float* part,
-                              uint32_t* cnt, hipStream_t stream);
+                              uint32_t* cnt, hipStream_t stream, const void* aqn_gamma = nullptr,
+                              const float* aqn_noise = nullptr, float aqn_sigma = 0.f, float aqn_eps = 0.f);
 
 // Decode kernel with x held in registers (decode_xs.hip): K in `splits` spans of
 // `qspan` 32-wide groups, `nw` waves per workgroup, weight tiles of 16 rows.
@@ -98,6 +103,15 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
                          const uint8_t* scales, const float* tensor_scale, int64_t n, const void* lora_a,
                          const void* lora_b, int r, void* y, void* workspace, const LinearPlan& plan,
                          hipStream_t stream);
+
+// The linear of the noisy RMSNorm of x (aqn.hip's prologue): fused into the decode
+// kernel where it takes one K slice at m <= 2, else the norm into the workspace
+// after the linear's own bytes (m x k bf16 at align256(plan.bytes)), then the linear.
+size_t linear_aqn_workspace_bytes(const LinearPlan& plan, int64_t m, int64_t k);
+hipError_t launch_linear_aqn(int fmt, const void* x, int64_t m, int64_t k, const void* gamma, const float* noise,
+                             float sigma, float eps, const uint8_t* codes, const uint8_t* scales,
+                             const float* tensor_scale, int64_t n, const void* lora_a, const void* lora_b, int r,
+                             void* y, void* workspace, const LinearPlan& plan, hipStream_t stream);
 
 // The m > 16 GEMM with W decoded in registers (gemm.hip): K a multiple of 128,
 // x and the codes below 2 GiB each, scales 16-byte aligned; t = x A^T (fp32,

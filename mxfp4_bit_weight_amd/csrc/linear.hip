@@ -773,4 +773,33 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
   return hipGetLastError();
 }
 
+size_t linear_aqn_workspace_bytes(const LinearPlan& plan, int64_t m, int64_t k) {
+  return align256(plan.bytes) + align256((size_t)m * (size_t)k * 2);
+}
+
+hipError_t launch_linear_aqn(int fmt, const void* x, int64_t m, int64_t k, const void* gamma, const float* noise,
+                             float sigma, float eps, const uint8_t* codes, const uint8_t* scales,
+                             const float* tensor_scale, int64_t n, const void* lora_a, const void* lora_b, int r,
+                             void* y, void* workspace, const LinearPlan& plan, hipStream_t stream) {
+  if (m == 0 || n == 0) return hipSuccess;
+  const bool has_lora = r > 0 && lora_a && lora_b;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  if (plan.path == 0 && k > 0 && decode_f8f4_fuses_aqn(plan.dq, m)) {
+    uint32_t* cnt_m = reinterpret_cast<uint32_t*>(ws + plan.off_count);
+    hipError_t e = launch_decode_f8f4(fmt, plan.dq, x, m, k, codes, scales, tensor_scale, n,
+                                      has_lora ? lora_a : nullptr, has_lora ? lora_b : nullptr, r,
+                                      cnt_m + kLsyncBase, y, reinterpret_cast<float*>(ws + plan.off_part),
+                                      cnt_m + kLoraSlots, stream, gamma, noise, sigma, eps);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+  }
+  // two launches: the norm into the workspace, then the linear on it
+  void* xn = ws + align256(plan.bytes);
+  if (k > 0) {
+    hipError_t e = launch_aqn_rmsnorm(x, m, k, gamma, noise, sigma, eps, xn, stream);
+    if (e != hipSuccess) return e;
+  }
+  return launch_linear(fmt, xn, m, k, codes, scales, tensor_scale, n, lora_a, lora_b, r, y, workspace, plan, stream);
+}
+
 }  // namespace fp4w

@@ -72,13 +72,39 @@ __device__ __forceinline__ void lsync_reader_arrive(uint32_t* ls, int rd, int nr
   if (old == quota - 1u) lsync_top_arrive(ls, lsync_top_expected(nread, lparts), words, lane);
 }
 
+// With a gain (the fused noisy RMSNorm), x enters as bf16(x * g), g = gamma (1 + sigma
+// noise), exactly as the workgroups that stream the codes form it (xgain_bf16).
+struct XGain {
+  const uint16_t* gamma;    // (K) bf16, or nullptr: no gain
+  const float* noise;       // (K) fp32
+  float sigma;
+};
+
+// bf16(x * gamma (1 + sigma noise)) of the 8 elements of v at k .. k + 7, with
+// gamma's 8 bf16 in gv and noise's 8 fp32 in n0, n1; also adds x^2 to *ss.
+__device__ __forceinline__ u32x4_t xgain_bf16(u32x4_t v, u32x4_t gv, u32x4_t n0, u32x4_t n1, float sigma,
+                                             float* ss) {
+  u32x4_t o;
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    const float x0 = bf16lo_f32(v[d]), x1 = bf16hi_f32(v[d]);
+    const float nz0 = __uint_as_float(d < 2 ? n0[2 * d] : n1[2 * d - 4]);
+    const float nz1 = __uint_as_float(d < 2 ? n0[2 * d + 1] : n1[2 * d - 3]);
+    const float g0 = bf16lo_f32(gv[d]) * __builtin_fmaf(sigma, nz0, 1.0f);
+    const float g1 = bf16hi_f32(gv[d]) * __builtin_fmaf(sigma, nz1, 1.0f);
+    if (ss) *ss = __builtin_fmaf(x1, x1, __builtin_fmaf(x0, x0, *ss));
+    o[d] = f32_to_bf16_rne(x0 * g0) | (f32_to_bf16_rne(x1 * g1) << 16);
+  }
+  return o;
+}
+
 // Wave `wave` of `nw` forms its share of chunk p into lr[wave][m][j] (m < M rows of
 // x (M, K) row-major, j < r rows of A (r, K)): 32-wide steps (p nw + wave) lsw ..
 // + lsw - 1, column block b of 16 rows of A at a time; lane (j, g) of the MFMA
 // result holds rows m = 4 g + i.
 __device__ __forceinline__ void lora_chunk_to_lds(float* lr, const uint16_t* __restrict__ x, int M, int64_t K,
                                                   const uint16_t* __restrict__ lora_a, int r, int p, int nw,
-                                                  int wave, int lane, int lsw) {
+                                                  int wave, int lane, int lsw, XGain xg = XGain{nullptr, nullptr, 0.f}) {
   const int li = lane & 15, lg = lane >> 4;
   const int64_t st0 = ((int64_t)p * nw + wave) * lsw;
   for (int b = 0; b < (r + 15) / 16; b++) {
@@ -92,6 +118,11 @@ __device__ __forceinline__ void lora_chunk_to_lds(float* lr, const uint16_t* __r
         const bool okx = li < M && kk < K, oka = j < r && kk < K;
         xa[i] = load16(x + (okx ? (int64_t)li * K + kk : 0));
         av[i] = load16(lora_a + (oka ? (int64_t)j * K + kk : 0));
+        if (xg.gamma) {
+          const u32x4_t gv = load16(xg.gamma + (okx ? kk : 0));
+          const u32x4_t n0 = load16(xg.noise + (okx ? kk : 0)), n1 = load16(xg.noise + (okx ? kk + 4 : 0));
+          xa[i] = xgain_bf16(xa[i], gv, n0, n1, xg.sigma, nullptr);
+        }
         if (!okx) xa[i] = (u32x4_t){0u, 0u, 0u, 0u};
         if (!oka) av[i] = (u32x4_t){0u, 0u, 0u, 0u};
       }
@@ -118,10 +149,11 @@ __device__ __forceinline__ float lora_chunk_value(const float* lr, int e, int nw
 // A chunk workgroup (all threads): forms chunk p, stores it, arrives.
 __device__ __forceinline__ void lora_chunk_publish(float* lr, const uint16_t* __restrict__ x, int M, int64_t K,
                                                    const uint16_t* __restrict__ lora_a, int r, int p, int nw,
-                                                   int lsw, uint32_t* lsync, int nread, int lparts) {
+                                                   int lsw, uint32_t* lsync, int nread, int lparts,
+                                                   XGain xg = XGain{nullptr, nullptr, 0.f}) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int mr = M * r;
-  lora_chunk_to_lds(lr, x, M, K, lora_a, r, p, nw, wave, lane, lsw);
+  lora_chunk_to_lds(lr, x, M, K, lora_a, r, p, nw, wave, lane, lsw, xg);
   __syncthreads();
   if (wave == 0) {
     for (int e = lane; e < mr; e += 64) lsync_store(&lsync[p * mr + e], ~__float_as_uint(lora_chunk_value(lr, e, nw, mr)));
@@ -164,13 +196,13 @@ __device__ __forceinline__ int lora_poll(const uint32_t* lsync, int lparts, int 
 // steps in their order (the same value bit for bit).
 __device__ __forceinline__ void lora_form_all(float* lr, float* lt, const uint16_t* __restrict__ x, int M,
                                               int64_t K, const uint16_t* __restrict__ lora_a, int r, int nw, int lsw,
-                                              int lparts) {
+                                              int lparts, XGain xg = XGain{nullptr, nullptr, 0.f}) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int mr = M * r;
   if (wave == 0)
     for (int q = lane; q < mr; q += 64) lt[q] = 0.f;
   for (int p = 0; p < lparts; p++) {
-    lora_chunk_to_lds(lr, x, M, K, lora_a, r, p, nw, wave, lane, lsw);
+    lora_chunk_to_lds(lr, x, M, K, lora_a, r, p, nw, wave, lane, lsw, xg);
     __syncthreads();
     if (wave == 0)
       for (int q = lane; q < mr; q += 64) lt[q] += lora_chunk_value(lr, q, nw, mr);

@@ -53,6 +53,9 @@ _lora_bwd = _sig("fp4w_lora_backward", _int, _p, _i64, _i64, _p, _i64, _p, _p, _
 _delta_grad = _sig("fp4w_scale_delta_grad", _int, _int, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p)
 _aqn = _sig("fp4w_aqn_rmsnorm", _int, _p, _i64, _i64, _p, _p, ctypes.c_float, ctypes.c_float, _p, _p)
 _aqn_sigma = _sig("fp4w_aqn_sigma", ctypes.c_double, _i64, _i64, ctypes.c_double, ctypes.c_double)
+_linear_aqn_ws = _sig("fp4w_linear_aqn_workspace_bytes", _sz, _i64, _i64, _i64, _int)
+_linear_aqn = _sig("fp4w_linear_aqn", _int, _int, _p, _i64, _i64, _p, _p, ctypes.c_float, ctypes.c_float, _p, _p, _p,
+                   _i64, _p, _p, _int, _p, _p, _sz, _p)
 _grouped = _sig("fp4w_grouped_linear", _int, _int, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p)
 _merge = _sig("fp4w_merge_scales", _int, _int, _p, _p, _i64, _p, _p, _p, _i64, _p)
 _status = _sig("fp4w_status_string", ctypes.c_char_p, _int)
@@ -63,7 +66,8 @@ EXPORTED = ["fp4w_quantize", "fp4w_dequantize", "fp4w_linear_workspace_bytes", "
             "fp4w_grouped_linear", "fp4w_merge_scales", "fp4w_status_string", "fp4w_version",
             "fp4w_debug_lora_wait", "fp4w_fake_quant", "fp4w_linear_w4a4", "fp4w_linear_backward_dx",
             "fp4w_scale_delta_grad", "fp4w_aqn_rmsnorm", "fp4w_aqn_sigma", "fp4w_linear_noalloc",
-            "fp4w_lora_backward", "fp4w_lora_backward_workspace_bytes"]
+            "fp4w_lora_backward", "fp4w_lora_backward_workspace_bytes", "fp4w_linear_aqn",
+            "fp4w_linear_aqn_workspace_bytes"]
 
 
 class Fp4wError(RuntimeError):
@@ -361,6 +365,39 @@ def scale_delta_grad(dy: torch.Tensor, x: torch.Tensor, q: QWeight, out: Optiona
 def aqn_sigma(step: int, total_steps: int, sigma_max: float = 1e-2, sigma_min: float = 5e-4) -> float:
     """fp4w_aqn_sigma: the exponentially decaying noise scale."""
     return float(_aqn_sigma(step, total_steps, sigma_max, sigma_min))
+
+
+def linear_aqn_workspace_bytes(m: int, n: int, k: int, r: int = 0) -> int:
+    return int(_linear_aqn_ws(m, n, k, r))
+
+
+def linear_aqn(x: torch.Tensor, gamma: torch.Tensor, noise: torch.Tensor, sigma: float, q: QWeight,
+               lora_a: Optional[torch.Tensor] = None, lora_b: Optional[torch.Tensor] = None, eps: float = 1e-6,
+               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4w_linear_aqn: the linear of the noisy RMSNorm of x (the norm fused into
+    the decode kernel where it runs over the whole K at m <= 2)."""
+    _need(x, torch.bfloat16, "x")
+    _need(gamma, torch.bfloat16, "gamma")
+    _need(noise, torch.float32, "noise")
+    m, k = x.shape
+    if k != q.k:
+        raise ValueError(f"x has k={k}, the weight k={q.k}")
+    if gamma.shape != (k,) or noise.shape != (k,):
+        raise ValueError("gamma and noise must be (k,)")
+    r = 0
+    if lora_a is not None or lora_b is not None:
+        _need(lora_a, torch.bfloat16, "lora_a")
+        _need(lora_b, torch.bfloat16, "lora_b")
+        r = lora_a.shape[0]
+        if lora_a.shape != (r, k) or lora_b.shape != (q.n, r):
+            raise ValueError("lora_a must be (r, k) and lora_b (n, r)")
+    y = _out(out, (m, q.n), torch.bfloat16, x.device)
+    nbytes = linear_aqn_workspace_bytes(m, q.n, k, r)
+    ws = workspace if workspace is not None else workspace_for(x.device, nbytes)
+    _check(_linear_aqn(q.fmt, _ptr(x), m, k, _ptr(gamma), _ptr(noise), float(sigma), float(eps), _ptr(q.codes),
+                       _ptr(q.scales), _ptr(q.tensor_scale), q.n, _ptr(lora_a), _ptr(lora_b), r, _ptr(y), _ptr(ws),
+                       ws.numel(), _stream(x.device)), "fp4w_linear_aqn")
+    return y
 
 
 def aqn_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, noise: torch.Tensor, sigma: float, eps: float = 1e-6,

@@ -332,6 +332,22 @@ def aqn_rmsnorm(x, gamma, noise, sigma: float, eps: float):
     return xf * r * gain
 
 
+def linear_aqn(fmt: int, x, gamma, noise, sigma: float, eps: float, codes, scales, tensor_scale,
+               lora_a=None, lora_b=None):
+    """The projection of the noisy RMSNorm's output (Telegram post, "Metod": the
+    noise enters the RMS norm that precedes the projections), in binary64 with
+    no rounding between the two: x~ = aqn_rmsnorm(x, gamma, noise, sigma, eps),
+    y = x~ deq(W)^T + (x~ A^T) B^T, W decoded exactly, LoRA A (r, k) and B (n, r)
+    bf16 bit patterns or None."""
+    xt = aqn_rmsnorm(x, gamma, noise, sigma, eps)
+    w = dequantize(fmt, codes, scales, tensor_scale, "f64")
+    y = xt @ w.T
+    if lora_a is not None:
+        f = lambda a: (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        y = y + (xt @ f(lora_a).T) @ f(lora_b).T
+    return y
+
+
 def linear_w4a4(x_codes, x_scales, codes, scales):
     """W4A4 MXFP4 (QATFactory page, section on the strategies NVFP4 and MXFP4
     need: weights and activations both 4-bit): y (m, n) in binary64 =

@@ -198,3 +198,27 @@ def test_lora_backward_validation_without_launch(lib):
     assert call(gb=_fake(A + 2)) == -3
     assert call(wsb=ws - 1) == -6 and call(ws=None) == -6
     assert call(ws=_fake(A + 16)) == -3
+
+
+def test_linear_aqn_validation_without_launch(lib):
+    """fp4w_linear_aqn checks what fp4w_linear checks, then gamma, noise and the
+    larger workspace, before any launch."""
+    f = lib._linear_aqn
+    A = 0x10000
+    m, n, k = 2, 16, 64
+    ws = lib.linear_aqn_workspace_bytes(m, n, k, 0)
+    assert ws >= lib.linear_workspace_bytes(m, n, k, 0) + m * k * 2
+    assert lib.linear_aqn_workspace_bytes(1, 10, 64, 65) == 0 and lib.linear_aqn_workspace_bytes(-1, 10, 64, 0) == 0
+
+    def call(**kw):
+        v = dict(fmt=0, x=_fake(A), m=m, k=k, g=_fake(A), nz=_fake(A), codes=_fake(A), sc=_fake(A), ts=_fake(A), n=n,
+                 a=None, b=None, r=0, y=_fake(A), ws=_fake(A), wsb=ws)
+        v.update(kw)
+        return f(v["fmt"], v["x"], v["m"], v["k"], v["g"], v["nz"], 1e-2, 1e-6, v["codes"], v["sc"], v["ts"], v["n"],
+                 v["a"], v["b"], v["r"], v["y"], v["ws"], v["wsb"], None)
+    assert call(fmt=7) == -4 and call(m=-1) == -1 and call(k=48) == -2
+    assert call(g=None) == -1 and call(nz=None) == -1
+    assert call(g=_fake(A + 2)) == -3 and call(nz=_fake(A + 4)) == -3
+    assert call(wsb=ws - 1) == -6 and call(ws=None) == -6 and call(ws=_fake(A + 16)) == -3
+    assert call(a=_fake(A), r=16) == -1
+    assert call(m=0, x=None, y=None, g=None, nz=None) == 0

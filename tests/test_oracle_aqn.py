@@ -79,3 +79,29 @@ def test_gain_against_closed_forms():
         assert abs(y[j] - want) <= 1e-14 * abs(want)
         others = np.delete(y, j)
         assert np.all(others == 0.0)
+
+
+@pytest.mark.parametrize("fmt", [O.NVFP4, O.MXFP4])
+def test_linear_of_the_norm_against_the_c_linear(fmt):
+    """The composition (norm, then projection with its LoRA branch) pinned against
+    the C oracle's linear on inputs where the norm's output is exact in bf16:
+    rows of +-c (RMS |c|, eps 0) give x~ = +-gamma (1 + sigma noise), and with
+    sigma = 1, noise in {0, 1, -1/2} and gamma in {1, 2, -1/2} every factor is a
+    power of two.  A norm applied twice, a noise term on the wrong axis, or a
+    LoRA branch fed x instead of x~ fails it."""
+    rng = np.random.default_rng(21)
+    n, k, r = 40, 96, 5
+    w, _, a, b = W.linear_inputs(6, n, k, 2, rank=r)
+    codes, scales, st = O.quantize(fmt, w)
+    gamma_f = rng.choice([1.0, 2.0, -0.5], k)
+    noise = rng.choice([0.0, 1.0, -0.5], k).astype(np.float32)
+    for c in (3.0, 0.375):
+        signs = rng.choice([-1.0, 1.0], (2, k))
+        x = W.to_bf16_bits(c * signs)
+        xt = signs * gamma_f[None, :] * (1.0 + noise.astype(np.float64))[None, :]
+        want = O.linear(fmt, W.to_bf16_bits(xt), codes, scales, st, a, b)
+        got = O.linear_aqn(fmt, x, W.to_bf16_bits(gamma_f), noise, 1.0, 0.0, codes, scales, st, a, b)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+        no_lora = O.linear_aqn(fmt, x, W.to_bf16_bits(gamma_f), noise, 1.0, 0.0, codes, scales, st)
+        assert np.allclose(no_lora, O.linear(fmt, W.to_bf16_bits(xt), codes, scales, st), rtol=1e-12,
+                           atol=1e-12 * np.abs(want).max())

@@ -72,8 +72,8 @@ extern "C" {
  *
  * NVFP4, dynamic ("max") scales: A = max |w| over the whole tensor; the tensor
  *   scale s_t = fl32(A / 2688) (correctly rounded binary32 division, 2688 = 6*448)
- *   is written to *tensor_scale (device, one float; it is also the amax scratch
- *   word during the call); block scale sb = RNE_sat(a_b / (6 s_t)) on the E4M3
+ *   is written to *tensor_scale (device, one float); block scale
+ *   sb = RNE_sat(a_b / (6 s_t)) on the E4M3
  *   grid (0 when s_t == 0); code = sign | RNE_sat(|w| / (dec(sb) s_t)) on the
  *   E2M1 grid, with the quotients taken exactly; a block whose scale decodes to 0
  *   gets signed-zero codes.
@@ -86,6 +86,13 @@ extern "C" {
  *   (E4M3 0x00..0x7E, E8M0 0x00..0xFE) and s_t finite and >= 0.
  * RNE_sat: round to nearest, ties to the even code, saturate at the grid top.
  * -0 encodes as 0x8.
+ * Launches on `stream`: MXFP4 and frozen scales one; NVFP4 dynamic two (per-
+ * workgroup maxima of |w|, then the encode, whose workgroups each reduce those
+ * maxima to s_t; one of them writes *tensor_scale).  The maxima live in a slot of
+ * a small device array the library holds, one slot per calling stream (64 per
+ * device, 2 KiB each; a 65th stream shares a slot): calls on one stream are
+ * ordered, and NVFP4 dynamic calls that overlap in time on up to 64 streams of
+ * one device do not interfere.
  */
 int fp4w_quantize(int fmt, const void *w_bf16, int64_t n, int64_t k,
                   uint8_t *codes, uint8_t *scales, float *tensor_scale,
@@ -113,8 +120,8 @@ int fp4w_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
  * its backward is the plain straight-through estimator (the gradient passes
  * unchanged; page on QAT at low bit widths), which needs no kernel.
  * scales (n, k/16 or k/32) and, for NVFP4, *tensor_scale are written as
- * fp4w_quantize writes them (the tensor scale word is the amax scratch during
- * the call), or read with FP4W_FROZEN_SCALES (frozen-scale training).  Also
+ * fp4w_quantize writes them, or read with FP4W_FROZEN_SCALES (frozen-scale
+ * training).  Also
  * fits activations (rows of x) for W4A4 training.  w_bf16 and out_bf16 must be
  * 16-byte aligned and must not overlap.
  */

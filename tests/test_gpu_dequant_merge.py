@@ -131,3 +131,30 @@ def test_merge_constructed_ties_mxfp4(fp4w):
     scales = c.astype(np.uint8).reshape(-1, 1)
     scales[5] = 0xFF
     _merge_case(fp4w, 1, scales, d, "MXFP4 constructed ties")
+
+
+@pytest.mark.parametrize("offsets", [(0, 0, 0), (1, 4, 3), (4, 16, 0), (0, 8, 4)])
+def test_merge_unaligned_and_tails(fp4w, offsets):
+    """Scale, delta and output pointers at byte offsets that take the merge off its
+    16-byte path (and on it), block counts with ragged tails after the whole
+    1024-block chunks; canary bytes after the output stay untouched."""
+    so, do, oo = offsets
+    for nb in (4096 + 1023, 9000, 70001):
+        rng = np.random.default_rng(nb + so)
+        scales = rng.integers(0, 0x7F, nb, dtype=np.uint8)
+        dec = torch.from_numpy(scales).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+        deltas = (np.float32(0.05) * dec * rng.standard_normal(nb).astype(np.float32)).astype(np.float32)
+        want, _ = O.merge_scales(0, scales, deltas)
+        s_buf = torch.zeros(nb + 64, dtype=torch.uint8, device=DEV)
+        s_buf[so:so + nb] = u8_dev(scales)
+        d_buf = torch.zeros(nb + 64, dtype=torch.float32, device=DEV)
+        d_bytes = d_buf.view(torch.uint8)
+        d_bytes[do:do + 4 * nb] = u8_dev(deltas.view(np.uint8))
+        o_buf = torch.full((nb + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+        st = fp4w._merge(0, s_buf.data_ptr() + so, d_buf.data_ptr() + do, nb, o_buf.data_ptr() + oo, None, None, 0,
+                         fp4w._stream(DEV))
+        assert st == 0
+        torch.cuda.synchronize()
+        out = o_buf.cpu().numpy()
+        assert np.array_equal(out[oo:oo + nb], want.reshape(-1)), f"offsets {offsets} nb={nb}"
+        assert (out[:oo] == 0xA5).all() and (out[oo + nb:] == 0xA5).all(), "bytes outside the output were written"

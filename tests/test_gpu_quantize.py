@@ -182,3 +182,37 @@ def test_tensor_scale_every_bf16_amax(fp4w):
         c2, s2 = O.nvfp4_quantize_with_tensor_scale(w[i:i + 1], want[i])
         bad += int(not (np.array_equal(c2[0], c_got[i]) and np.array_equal(s2[0], s_got[i])))
     assert bad == 0
+
+
+def test_tensor_scale_across_calls_and_streams(fp4w):
+    """The amax is reduced in a slot the library holds per stream and returns to
+    zero after every call: a run of tensors whose maxima fall (a slot that kept a
+    maximum would give every later tensor the first one's scale), tensors big
+    enough for many reducing workgroups, and calls interleaved on two streams
+    without synchronisation, each against the oracle's tensor scale, bit for bit."""
+    say("[quantize] tensor scale across calls and streams")
+    rng = np.random.default_rng(12)
+    shapes = [(64, 256), (512, 1024), (3584, 3584), (40, 96)]
+    ws, wants = [], []
+    for i in range(24):
+        n, k = shapes[i % len(shapes)]
+        w = W.to_bf16_bits(rng.standard_normal((n, k)) * 2.0 ** (-i / 3.0))
+        ws.append(w)
+        wants.append(O.nvfp4_tensor_scale(w))
+    dev_w = [bf16_dev(w) for w in ws]
+    torch.cuda.synchronize()
+    outs = [fp4w.quantize(dw, 0) for dw in dev_w]           # falling maxima on one stream
+    torch.cuda.synchronize()
+    for i, q in enumerate(outs):
+        assert np.float32(q.tensor_scale.item()).view(np.uint32) == np.float32(wants[i]).view(np.uint32), i
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = [None] * len(dev_w)
+    for i, dw in enumerate(dev_w):
+        with torch.cuda.stream(s1 if i % 2 == 0 else s2):
+            outs[i] = fp4w.quantize(dw, 0)
+    torch.cuda.synchronize()
+    for i, q in enumerate(outs):
+        assert np.float32(q.tensor_scale.item()).view(np.uint32) == np.float32(wants[i]).view(np.uint32), i
+    c, s, st = qweight_host(outs[2])
+    c2, s2_, _ = O.quantize(0, ws[2])
+    assert np.array_equal(c, c2) and np.array_equal(s, s2_)

@@ -577,9 +577,14 @@ hipError_t launch_decode_xs(int fmt, const XsConfig& c, const void* x, int64_t m
                             uint32_t* lsync, void* y, float* part, uint32_t* cnt, hipStream_t stream) {
   const int rr = la && lb && k > 0 ? r : 0;      // k = 0: t = x A^T is zero
   if (rr > XS_MAX_R || m * rr > 1024) return hipErrorInvalidValue;
-  // tile runs: about kXsGroupsPerCu workgroups per CU over all spans, at most
+  // chunk workgroups of the LoRA down-projection go first in the grid
+  const int lsw = rr > 0 ? lora_chunk_steps(c.nw, k, (int)m * rr) : kLoraStepsPerLoad;
+  const int lparts = rr > 0 ? lora_chunk_count(c.nw, k, lsw) : 0;
+  // tile runs: about kXsGroupsPerCu workgroups per CU over all spans, the chunk
+  // workgroups included (one more workgroup than the chip holds at once would
+  // start after the first ones finish, adding a whole workgroup's time), at most
   // kXsMaxTilesPerGroup tiles each, never more runs than tiles
-  int64_t G = (int64_t)device_cu_count() * kXsGroupsPerCu / c.splits;
+  int64_t G = ((int64_t)device_cu_count() * kXsGroupsPerCu - lparts) / c.splits;
   if (G > c.ntiles) G = c.ntiles;
   if (G > kTileSlots) G = kTileSlots;
   if (G < 1) G = 1;
@@ -611,9 +616,8 @@ hipError_t launch_decode_xs(int fmt, const XsConfig& c, const void* x, int64_t m
   a.la = rr > 0 ? reinterpret_cast<const uint16_t*>(la) : nullptr;
   a.lb = reinterpret_cast<const uint16_t*>(lb);
   a.r = rr;
-  // chunk workgroups of the LoRA down-projection go first in the grid
-  a.lsw = rr > 0 ? lora_chunk_steps(c.nw, k, (int)m * rr) : kLoraStepsPerLoad;
-  a.lparts = rr > 0 ? lora_chunk_count(c.nw, k, a.lsw) : 0;
+  a.lsw = lsw;
+  a.lparts = lparts;
   a.lsync = lsync;
   a.y = reinterpret_cast<uint16_t*>(y);
   a.part = part;

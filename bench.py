@@ -52,6 +52,15 @@ PROFILE_FILES = {
     "decode_m1": "decode_gate_up_m1_nvfp4_pmc.txt",
     "decode_m8_lora": "decode_gate_up_m8_nvfp4_lora_pmc.txt",
     "quantize_nvfp4": "quantize_gate_up_nvfp4_pmc.txt",
+    "gemm": "prefill_gemm_16384x18944x3584_pmc.txt",
+}
+# the kernels one call of each profiled target launches (name prefixes in the traces)
+TARGET_KERNELS = {
+    "decode_m1_lora": ("decode_f8f4_kernel",),
+    "decode_m1": ("decode_f8f4_kernel",),
+    "decode_m8_lora": ("decode_xs_kernel",),
+    "quantize_nvfp4": ("nvfp4_amax_kernel", "nvfp4_encode_kernel"),
+    "gemm": ("gemm_w4_kernel<0", "lora_down_kernel"),
 }
 
 
@@ -72,6 +81,14 @@ def parse():
     p.add_argument("--only", choices=PROFILE_TARGETS, default=None,
                    help="only one kernel's launches (and a copy of known size), for profiler runs")
     p.add_argument("--cpu-seconds", type=float, default=8.0, help="budget of the CPU-oracle headline sample")
+    p.add_argument("--summarize", choices=PROFILE_TARGETS, default=None,
+                   help="write profiles/<target> from rocprofv3 csv output (no GPU): --trace, --fetch, --write dirs")
+    p.add_argument("--trace", default=None, help="rocprofv3 --kernel-trace --stats output directory")
+    p.add_argument("--fetch", default=None, help="rocprofv3 --pmc FETCH_SIZE output directory")
+    p.add_argument("--write", default=None, help="rocprofv3 --pmc WRITE_SIZE output directory")
+    p.add_argument("--sq", default=None, help="rocprofv3 --pmc output directory with SQ counters (gemm)")
+    p.add_argument("--commands", default=None, help="file holding the commands that made the directories")
+    p.add_argument("--bench-json", default=None, help="the --only run's JSON line (HIP-event timing), for comparison")
     a = p.parse_args()
     if a.roofline_only:
         a.only = "decode_m1_lora"
@@ -101,6 +118,9 @@ def quant_bytes(fmt, count):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize_profile(args)
+        return
     if args.gpus != 1:
         log(f"bench.py measures one GPU only: every box here has a single MI355X, so --gpus {args.gpus} "
             "is not supported (the multi-GPU sharding of this path is described in DESIGN.md).")
@@ -172,8 +192,10 @@ def main():
         for fmt in (0, 1):
             w, _, a, b = W.linear_inputs(100, n, k, 1, rank=rank, wkind="outlier" if fmt == 0 else "student_t")
             weights[fmt] = (fp4w.quantize(bf16(w), fmt), bf16(a), bf16(b), n, k)
-        rows = gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights)
-        print(json.dumps({"rows": rows}), flush=True)
+        calibration_copy(torch, dev, sync)
+        rows = gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights, prefill_only=True)
+        print(json.dumps({"target": "gemm", "rows": rows, "kernel_sources_sha256": kernel_sources_sha256("gemm")}),
+              flush=True)
         return
 
     # ---- decode weights: quantize once on the device, then clone for rotation ----------
@@ -230,10 +252,8 @@ def main():
         if args.only == "quantize_nvfp4":
             w = bf16(dg["host"][0])
             outs = [fp4w.empty_qweight(0, n, k, dev) for _ in range(4)]
-            for i in range(launches):
-                fp4w.quantize(w, 0, out=outs[i % 4])
-            sync()
-            per, what = float("nan"), "quantize"
+            per, _ = time_loop(lambda i: fp4w.quantize(w, 0, out=outs[i % 4]), launches, args.warmup)
+            what = "quantize"
         else:
             m, lora = {"decode_m1_lora": (1, True), "decode_m1": (1, False), "decode_m8_lora": (8, True)}[args.only]
             per, _ = time_graph(gemv(m, lora), launches, args.warmup)
@@ -302,6 +322,174 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "rows": rows,
     }
     print(json.dumps(out), flush=True)
+
+
+# ---- profile summaries (rocprofv3 csv -> profiles/*.txt, no GPU) ---------------------
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _is_target(name, target):
+    base = name.split("(")[0]
+    return any(k in base for k in TARGET_KERNELS[target])
+
+
+def _per_dispatch(rows, counter, reduce="sum"):
+    """{dispatch id: (kernel name, value)} of one counter, its instances (XCDs,
+    shader engines) added, or their maximum (a clock such as GRBM_GUI_ACTIVE)."""
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        d = r["Dispatch_Id"]
+        x = float(r["Counter_Value"])
+        if d in out:
+            name, v = out[d]
+            out[d] = (name, v + x if reduce == "sum" else max(v, x))
+        else:
+            out[d] = (r["Kernel_Name"], x)
+    return out
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if v else float("nan")
+
+
+def _calibration(rows, counter):
+    """The counter of the 256 MiB calibration copies: the copy dispatches within 10%
+    of the largest value of that counter among copy kernels."""
+    vals = [v for n, v in _per_dispatch(rows, counter).values() if "copyBuffer" in n or "copy" in n.lower()]
+    if not vals:
+        return None
+    top = max(vals)
+    return _median([v for v in vals if v >= 0.9 * top])
+
+
+def _algorithmic(target):
+    """(algorithmic bytes per call, flops per call or None, what a call is)."""
+    import importlib
+    W = importlib.import_module("mxfp4_bit_weight_amd.workloads")
+    n, k = W.QWEN7B_SHAPES["gate_up"]
+    r = W.LORA_RANK
+    if target == "decode_m1_lora":
+        return linear_bytes(0, 1, n, k, r), linear_flops(1, n, k, r), "fp4w_linear, m = 1, LoRA r = 16"
+    if target == "decode_m1":
+        return linear_bytes(0, 1, n, k, 0), linear_flops(1, n, k, 0), "fp4w_linear, m = 1, no LoRA"
+    if target == "decode_m8_lora":
+        return linear_bytes(0, 8, n, k, r), linear_flops(8, n, k, r), "fp4w_linear, m = 8, LoRA r = 16"
+    if target == "quantize_nvfp4":
+        return quant_bytes(0, n * k), None, "fp4w_quantize NVFP4 (amax + encode launches)"
+    m = W.PREFILL_M
+    return 2 * m * k + n * k // 2 + n * k // 16 + 2 * m * n, linear_flops(m, n, k, r), \
+        f"fp4w_linear, m = {m}, LoRA r = 16 (GEMM launch; the LoRA down-projection is its own launch)"
+
+
+def summarize_profile(args):
+    t = args.summarize
+    lines = []
+    add = lines.append
+    nbytes, flops, what = _algorithmic(t)
+    shape = "(18944, 3584) Qwen-2.5-7B gate/up"
+    add(f"# {t}: W {shape}, NVFP4 unless stated; {what}")
+    add("# commands (repo root on the GPU box; each counter pass a run of its own):")
+    if args.commands:
+        for c in open(args.commands):
+            if c.strip():
+                add("#   " + c.strip())
+    add("# summarized by: python bench.py --summarize " + t + " --trace <dir> --fetch <dir> --write <dir>"
+        + (" --sq <dir>" if args.sq else "") + " --commands <file> --bench-json <file>")
+    # kernel trace
+    tr = _csv_rows(args.trace, "kernel_trace.csv")
+    durs = {}
+    for r in tr:
+        if _is_target(r["Kernel_Name"], t):
+            key = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            durs.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    add("kernel trace (us per dispatch): kernel, dispatches, median, mean, min")
+    call_us = 0.0
+    for key, v in durs.items():
+        add(f"  {key}: {len(v)} {_median(v):.3f} {sum(v) / len(v):.3f} {min(v):.3f}")
+        call_us += _median(v)
+    add(f"median kernel time per call (us): {call_us:.3f}")
+    if args.bench_json and os.path.exists(args.bench_json):
+        for line in open(args.bench_json):
+            line = line.strip()
+            if line.startswith("{"):
+                j = json.loads(line)
+                if "per_launch_us" in j:
+                    add(f"bench.py HIP-event time per call over the same graph (us, includes launch gaps): "
+                        f"{j['per_launch_us']}")
+                if "rows" in j:
+                    for name, row in j["rows"].items():
+                        add(f"bench.py {name}: {row.get('ms')} ms per call")
+    # HBM traffic
+    fetch_rows = _csv_rows(args.fetch, "counter_collection.csv")
+    write_rows = _csv_rows(args.write, "counter_collection.csv")
+    cf = _calibration(fetch_rows, "FETCH_SIZE")
+    cw = _calibration(write_rows, "WRITE_SIZE")
+    copy_kib = 256 * 1024
+    ff = cf / copy_kib if cf else None
+    fw = cw / copy_kib if cw else None
+    add(f"calibration copy 256 MiB: FETCH_SIZE {cf} KiB (factor {ff}), WRITE_SIZE {cw} KiB (factor {fw})")
+    fv = [v for n, v in _per_dispatch(fetch_rows, "FETCH_SIZE").values() if _is_target(n, t)]
+    wv = [v for n, v in _per_dispatch(write_rows, "WRITE_SIZE").values() if _is_target(n, t)]
+    kernels_per_call = max(1, len(durs))
+    fetch_b = _median(fv) * 1024 / ff * kernels_per_call if fv and ff else float("nan")
+    write_b = _median(wv) * 1024 / fw * kernels_per_call if wv and fw else float("nan")
+    if t == "quantize_nvfp4" or t == "gemm":      # per kernel medians, then the call's sum
+        fetch_b = write_b = 0.0
+        for k in TARGET_KERNELS[t]:
+            fk = [v for n, v in _per_dispatch(fetch_rows, "FETCH_SIZE").values() if k in n.split("(")[0]]
+            wk = [v for n, v in _per_dispatch(write_rows, "WRITE_SIZE").values() if k in n.split("(")[0]]
+            if fk and ff:
+                fetch_b += _median(fk) * 1024 / ff
+            if wk and fw:
+                write_b += _median(wk) * 1024 / fw
+    add(f"dispatches counted: {len(fv)} (FETCH_SIZE run), {len(wv)} (WRITE_SIZE run)")
+    add(f"HBM bytes read per call: {fetch_b:.0f}")
+    add(f"HBM bytes written per call: {write_b:.0f}")
+    add(f"algorithmic bytes per call: {nbytes}")
+    add(f"traffic / algorithmic: {(fetch_b + write_b) / nbytes:.4f}")
+    add(f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}")
+    if call_us > 0:
+        add(f"achieved (algorithmic bytes / median kernel time): {nbytes / (call_us * 1e-6) / 1e9:.1f} GB/s "
+            f"= {100 * nbytes / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f} GB/s")
+        if flops:
+            add(f"achieved: {flops / (call_us * 1e-6) / 1e12:.1f} TFLOP/s "
+                f"= {100 * flops / (call_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS:.1f}% of the dense bf16 peak")
+    if args.sq:
+        sq = _csv_rows(args.sq, "counter_collection.csv")
+        names = sorted({r["Counter_Name"] for r in sq})
+        add("SQ counters (median per dispatch of the target kernel):")
+        med = {}
+        for c in names:
+            red = "max" if c.startswith("GRBM_") else "sum"
+            v = [x for n, x in _per_dispatch(sq, c, red).values() if _is_target(n, t) and "lora_down" not in n]
+            med[c] = _median(v)
+            add(f"  {c} ({red} over instances): {med[c]:.0f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "SQ_BUSY_CU_CYCLES" in med and med["SQ_BUSY_CU_CYCLES"] > 0:
+            # per SIMD against the busy cycles of its CU (4 SIMDs per CU); GRBM_GUI_ACTIVE
+            # as read here runs several times faster than the shader clock, so it is listed only
+            add(f"MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES)): "
+                f"{100 * med['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * med['SQ_BUSY_CU_CYCLES']):.1f}%")
+            add(f"CU busy cycles per CU (SQ_BUSY_CU_CYCLES / 256) over the kernel time: "
+                f"{med['SQ_BUSY_CU_CYCLES'] / 256 / (call_us * 1e3):.3f} GHz")
+        if "SQ_LDS_BANK_CONFLICT" in med and "SQ_LDS_IDX_ACTIVE" in med and med["SQ_LDS_IDX_ACTIVE"] > 0:
+            add(f"LDS bank conflict cycles / LDS active cycles: "
+                f"{med['SQ_LDS_BANK_CONFLICT'] / med['SQ_LDS_IDX_ACTIVE']:.4f}")
+    add(f"kernel_sources_sha256: {kernel_sources_sha256(t)}")
+    out = os.path.join(ROOT, "profiles", PROFILE_FILES[t])
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
 
 
 def pmc_traffic(target):
@@ -400,10 +588,10 @@ def read_ceiling(torch, dev, sync, time_graph, nbytes, launches, warmup):
             "what": "plain 16-byte streaming read of the kernel's algorithmic bytes, same rotation and timing"}
 
 
-def gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights):
+def gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights, prefill_only=False):
     """The prefill GEMM: x 16384 x 3584, W (18944, 3584), LoRA r = 16, both formats
     (weights[fmt] = (qweight, A, B, n, k)); 10 untimed calls first, as the clock
-    ramps up under this load."""
+    ramps up under this load.  prefill_only: that GEMM alone (profiler runs)."""
     rows = {}
     mrows = W.PREFILL_M
     for fmt in (0, 1):
@@ -418,6 +606,9 @@ def gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights):
         rows[f"prefill_gemm_{name}"] = {"m": mrows, "n": n, "k": k, "ms": round(gms, 3), "TFLOP/s": round(tf, 1),
                                         "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 1), "algorithmic_flop": fl}
         log(f"[bench] prefill GEMM {name} {gms:.3f} ms, {tf:.1f} TFLOP/s")
+        if prefill_only:
+            del x, y, wsg
+            continue
         # the input gradient through the frozen base for the same shape: dX = dY deq(W),
         # dY the forward's output (m x n), dX m x k
         dx = torch.empty((mrows, k), dtype=torch.bfloat16, device=dev)

@@ -33,14 +33,25 @@ def flags():
             "-Wall", "-Wno-unused-function", "-I", os.path.join(HERE, "..", "include")]
 
 
-def build(verbose: bool = False, jobs: int = 6) -> str:
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the same
+# library (device code unchanged), for the CPU test run of the host validation;
+# each sanitizer flag applies to the host compilation only.
+SAN_LIB = os.path.join(HERE, "libfp4w_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+
+
+def build(verbose: bool = False, jobs: int = 6, sanitize: bool = False) -> str:
     cc = hipcc()
-    objdir = os.path.join(HERE, "_build")
+    objdir = os.path.join(HERE, "_build_san" if sanitize else "_build")
     os.makedirs(objdir, exist_ok=True)
+    extra = SAN_FLAGS if sanitize else []
+    out_lib = SAN_LIB if sanitize else LIB
 
     def compile_one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,12 +65,15 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    tmp = out_lib + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(["-shared-libsan", *extra] if sanitize else []),
+           "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out_lib)
+    if sanitize:
+        return out_lib
     obj = compile_one("membench.hip")
     tmp = MEMBENCH_LIB + ".tmp"
     subprocess.run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj], check=True)
@@ -68,4 +82,4 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

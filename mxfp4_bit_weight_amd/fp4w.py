@@ -23,7 +23,8 @@ MAX_LORA_RANK = 64
 WORKSPACE_COUNTER_BYTES = 28800
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfp4w.so")
+# FP4W_LIB: another build of the same library (the host-sanitized one of tests/run_sanitized.sh)
+LIB_PATH = os.environ.get("FP4W_LIB") or os.path.join(_HERE, "libfp4w.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
@@ -324,7 +325,7 @@ def lora_backward_workspace_bytes(m: int, n: int, k: int, r: int) -> int:
 
 
 def lora_backward(dy: torch.Tensor, x: torch.Tensor, lora_a: torch.Tensor, lora_b: torch.Tensor,
-                  workspace: Optional[torch.Tensor] = None):
+                  workspace: Optional[torch.Tensor] = None, out=None):
     """fp4w_lora_backward: (u, grad_a, grad_b) for the adapter y_lora = (x A^T) B^T,
     u = dy B (m, r), dA = u^T x (r, k), dB = dy^T (x A^T) (n, r), all fp32."""
     _need(dy, torch.bfloat16, "dy")
@@ -336,9 +337,14 @@ def lora_backward(dy: torch.Tensor, x: torch.Tensor, lora_a: torch.Tensor, lora_
     if x.shape != (m, k) or lora_b.shape != (n, r):
         raise ValueError("dy (m, n), x (m, k), lora_a (r, k) and lora_b (n, r) must agree")
     dev = dy.device
-    u = torch.empty((m, r), dtype=torch.float32, device=dev)
-    ga = torch.empty((r, k), dtype=torch.float32, device=dev)
-    gb = torch.empty((n, r), dtype=torch.float32, device=dev)
+    if out is not None:                                  # (u, grad_a, grad_b), fp32, contiguous
+        u = _out(out[0], (m, r), torch.float32, dev, "u")
+        ga = _out(out[1], (r, k), torch.float32, dev, "grad_a")
+        gb = _out(out[2], (n, r), torch.float32, dev, "grad_b")
+    else:
+        u = torch.empty((m, r), dtype=torch.float32, device=dev)
+        ga = torch.empty((r, k), dtype=torch.float32, device=dev)
+        gb = torch.empty((n, r), dtype=torch.float32, device=dev)
     nbytes = lora_backward_workspace_bytes(m, n, k, r)
     if nbytes == 0:
         raise ValueError("invalid lora_backward shape")

@@ -22,6 +22,9 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 
 def _load():
+    alt = os.environ.get("FP4W_ORACLE_LIB")        # the sanitized build (tests/run_sanitized.sh)
+    if alt:
+        return ctypes.CDLL(alt)
     if not os.path.exists(_LIB_PATH) or (
             os.path.getmtime(_LIB_PATH) < os.path.getmtime(os.path.join(_HERE, "fp4_oracle.c"))):
         from . import build as _b

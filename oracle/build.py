@@ -11,6 +11,11 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "fp4_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build for the sanitized CPU test run:
+# clang (the ROCm toolchain's, whose sanitizer runtime the HIP library's host code
+# uses too), single-threaded (no OpenMP), every UB report fatal
+SAN_LIB = os.path.join(HERE, "liboracle_san.so")
+CLANG = "/opt/rocm/lib/llvm/bin/clang"
 
 
 def build(verbose: bool = False) -> str:
@@ -24,5 +29,19 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(verbose: bool = False) -> str:
+    cmd = [CLANG, "-std=c11", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-shared-libsan",
+           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra", "-o", SAN_LIB + ".tmp", SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(SAN_LIB + ".tmp", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -79,3 +79,39 @@ def check_bound(y_gpu: np.ndarray, y64: np.ndarray, xnorm: np.ndarray, wnorm: np
                              f"err={err.flat[i]:.3e} bound={bound.flat[i]:.3e} gpu={y_gpu.flat[i]!r} "
                              f"ref={y64.flat[i]!r}")
     return float((err / np.maximum(bound, 1e-300)).max()) * REL_TOL
+
+
+# ---- canary bytes around device outputs ------------------------------------------------
+CANARY_BYTES = 256          # on each side; keeps the output 256-byte aligned
+CANARY = 0xA5
+
+
+class Guarded:
+    """A device output of `shape` and `dtype` inside a larger byte buffer whose
+    CANARY_BYTES before and after it hold CANARY; check() asserts that no kernel
+    wrote outside the output.  `fill` (a float, e.g. NaN) pre-fills the output."""
+
+    def __init__(self, shape, dtype, fill=None):
+        nbytes = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        self.buf = torch.full((nbytes + 2 * CANARY_BYTES,), CANARY, dtype=torch.uint8, device=DEV)
+        self.nbytes = nbytes
+        self.t = self.buf[CANARY_BYTES:CANARY_BYTES + nbytes].view(dtype).view(shape)
+        if fill is not None:
+            self.t.fill_(fill)
+
+    def check(self, what=""):
+        torch.cuda.synchronize()
+        head = self.buf[:CANARY_BYTES].cpu().numpy()
+        tail = self.buf[CANARY_BYTES + self.nbytes:].cpu().numpy()
+        assert (head == CANARY).all() and (tail == CANARY).all(), f"{what}: bytes outside the output were written"
+
+
+def guarded_qweight(fp4w, fmt, n, k):
+    """An empty QWeight whose codes, scales and tensor scale are Guarded; returns
+    (qweight, [guards])."""
+    blk = 16 if fmt == 0 else 32
+    gc = Guarded((n, k // 2), torch.uint8)
+    gs = Guarded((n, k // blk), torch.uint8)
+    gt = Guarded((1,), torch.float32) if fmt == 0 else None
+    q = fp4w.QWeight(fmt, gc.t, gs.t, gt.t if gt is not None else None, n, k)
+    return q, [g for g in (gc, gs, gt) if g is not None]

@@ -7,7 +7,7 @@ import torch
 
 import oracle as O
 from mxfp4_bit_weight_amd import workloads as W
-from tests.gpu_util import DEV, bf16_dev, bits_host, f32_dev, f64_of_bf16, say
+from tests.gpu_util import DEV, Guarded, bf16_dev, bits_host, f32_dev, f64_of_bf16, say
 
 pytestmark = pytest.mark.gpu
 
@@ -33,8 +33,9 @@ def test_aqn_rmsnorm(fp4w, m, k):
     noise = rng.standard_normal(k).astype(np.float32)
     for step in (0, 400, 1000):
         sigma = O.aqn_sigma(step, 1000)
-        y = fp4w.aqn_rmsnorm(bf16_dev(x), bf16_dev(gamma), f32_dev(noise), sigma, 1e-6)
-        torch.cuda.synchronize()
+        g = Guarded((m, k), torch.bfloat16, float("nan"))
+        y = fp4w.aqn_rmsnorm(bf16_dev(x), bf16_dev(gamma), f32_dev(noise), sigma, 1e-6, out=g.t)
+        g.check(f"aqn m={m} k={k}")
         _check(f64_of_bf16(bits_host(y)), O.aqn_rmsnorm(x, gamma, noise, sigma, 1e-6), f"m={m} k={k} step={step}")
 
 

@@ -11,7 +11,7 @@ import torch
 
 import oracle as O
 from mxfp4_bit_weight_amd import workloads as W
-from tests.gpu_util import DEV, bf16_dev, bits_host, check_bound, f64_of_bf16, qweight_dev, say
+from tests.gpu_util import DEV, Guarded, bf16_dev, bits_host, check_bound, f64_of_bf16, qweight_dev, say
 
 pytestmark = pytest.mark.gpu
 
@@ -46,8 +46,9 @@ def test_backward_dx_ragged(fp4w, fmt, m, n, k):
     rng = np.random.default_rng(m * 7 + n)
     dy = W.to_bf16_bits(rng.standard_normal((m, n)))
     q = qweight_dev(fp4w, fmt, codes, scales, st)
-    dx = fp4w.linear_backward_dx(bf16_dev(dy), q)
-    torch.cuda.synchronize()
+    g = Guarded((m, k), torch.bfloat16, float("nan"))
+    dx = fp4w.linear_backward_dx(bf16_dev(dy), q, out=g.t)
+    g.check(f"backward dx fmt={fmt} m={m} n={n} k={k}")
     want = O.linear_backward_dx(fmt, dy, codes, scales, st)
     yn = np.sqrt((f64_of_bf16(dy) ** 2).sum(axis=1))[:, None]
     check_bound(f64_of_bf16(bits_host(dx)), want, yn, _col_norms(fmt, codes, scales, st)[None, :],

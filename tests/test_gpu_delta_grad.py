@@ -9,7 +9,7 @@ import torch
 
 import oracle as O
 from mxfp4_bit_weight_amd import workloads as W
-from tests.gpu_util import DEV, bf16_dev, check_bound, f64_of_bf16, qweight_dev, say
+from tests.gpu_util import DEV, Guarded, bf16_dev, check_bound, f64_of_bf16, qweight_dev, say
 
 pytestmark = pytest.mark.gpu
 
@@ -46,10 +46,10 @@ def test_delta_grad_ragged(fp4w, fmt, m, n, k):
     rng = np.random.default_rng(m * 3 + k)
     dy = W.to_bf16_bits(rng.standard_normal((m, n)))
     x = W.to_bf16_bits(rng.standard_normal((m, k)))
-    out = torch.full(scales.shape, float("nan"), dtype=torch.float32, device=DEV)
+    guard = Guarded(scales.shape, torch.float32, float("nan"))
     g = fp4w.scale_delta_grad(bf16_dev(dy).view(m, n), bf16_dev(x).view(m, k),
-                              qweight_dev(fp4w, fmt, codes, scales, st), out=out)
-    torch.cuda.synchronize()
+                              qweight_dev(fp4w, fmt, codes, scales, st), out=guard.t)
+    guard.check(f"delta grad fmt={fmt} m={m} n={n} k={k}")
     want = O.scale_delta_grad(fmt, dy.reshape(m, n), x.reshape(m, k), codes, st)
     yn, ws = _bound_terms(fmt, dy.reshape(m, n), x.reshape(m, k), codes, st)
     check_bound(g.cpu().numpy().astype(np.float64), want, yn, ws, f"fmt={fmt} m={m} n={n} k={k}")

@@ -6,7 +6,7 @@ import torch
 
 import oracle as O
 from mxfp4_bit_weight_amd import workloads as W
-from tests.gpu_util import DEV, bits_host, bf16_dev, f32_dev, qweight_dev, say, u8_dev
+from tests.gpu_util import DEV, Guarded, bits_host, bf16_dev, f32_dev, qweight_dev, say, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -20,9 +20,12 @@ def fp4w():
 def _dequant_both(fp4w, fmt, codes, scales, st, what):
     say(f"[dequantize] {what} fmt={fmt} shape={codes.shape}")
     q = qweight_dev(fp4w, fmt, codes, scales, st)
-    yb = fp4w.dequantize(q, torch.bfloat16)
-    yf = fp4w.dequantize(q, torch.float32)
-    torch.cuda.synchronize()
+    n, k = codes.shape[0], codes.shape[1] * 2
+    gb_, gf_ = Guarded((n, k), torch.bfloat16), Guarded((n, k), torch.float32)
+    yb = fp4w.dequantize(q, torch.bfloat16, out=gb_.t)
+    yf = fp4w.dequantize(q, torch.float32, out=gf_.t)
+    gb_.check(f"dequantize bf16 {what}")
+    gf_.check(f"dequantize fp32 {what}")
     gb, gf = bits_host(yb), yf.cpu().numpy()
     wb = O.dequantize(fmt, codes, scales, st, "bf16")
     wf = O.dequantize(fmt, codes, scales, st, "f32")
@@ -74,6 +77,9 @@ def _merge_case(fp4w, fmt, scales, deltas, what, codes=None):
     q = qweight_dev(fp4w, fmt, codes, scales, np.float32(0.5))
     d = f32_dev(deltas.reshape(scales.shape))
     new = fp4w.merge_scales(q, d)                      # out of place: codes copied
+    gso = Guarded(scales.shape, torch.uint8)
+    fp4w.merge_scales(q, d, scales_out=gso.t)
+    gso.check(f"merge {what}")
     torch.cuda.synchronize()
     want, _ = O.merge_scales(fmt, scales, deltas)
     got = new.scales.cpu().numpy()

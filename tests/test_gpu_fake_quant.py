@@ -8,7 +8,7 @@ import torch
 
 import oracle as O
 from mxfp4_bit_weight_amd import workloads as W
-from tests.gpu_util import DEV, bf16_dev, bits_host, f32_dev, say, u8_dev
+from tests.gpu_util import DEV, Guarded, bf16_dev, bits_host, f32_dev, say, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -21,8 +21,9 @@ def fp4w():
 
 def _compare(fp4w, w_bits, fmt, what):
     say(f"[fake-quant] {what} fmt={fmt} shape={w_bits.shape}")
-    y, scales, ts = fp4w.fake_quant(bf16_dev(w_bits), fmt)
-    torch.cuda.synchronize()
+    g = Guarded(w_bits.shape, torch.bfloat16, float("nan"))
+    y, scales, ts = fp4w.fake_quant(bf16_dev(w_bits), fmt, out=g.t)
+    g.check(f"fake-quant {what}")
     codes, s2, st2 = O.quantize(fmt, w_bits)
     want = O.dequantize(fmt, codes, s2, st2, "bf16")
     got = bits_host(y)

@@ -10,7 +10,7 @@ import torch
 
 import oracle as O
 from mxfp4_bit_weight_amd import workloads as W
-from tests.gpu_util import DEV, bf16_dev, bits_host, check_bound, f32_dev, f64_of_bf16, i32_dev, say, u8_dev
+from tests.gpu_util import DEV, Guarded, bf16_dev, bits_host, check_bound, f32_dev, f64_of_bf16, i32_dev, say, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -30,9 +30,10 @@ def _experts(fmt, seed, e, n, k):
 
 def _case(fp4w, fmt, x, row_index, offsets, codes, scales, ts, what):
     say(f"[grouped] {what} fmt={fmt} experts={codes.shape[0]} n={codes.shape[1]} k={codes.shape[2] * 2} rows={row_index.size}")
+    g = Guarded((row_index.size, codes.shape[1]), torch.bfloat16, float("nan"))
     y = fp4w.grouped_linear(bf16_dev(x), i32_dev(row_index), i32_dev(offsets), fmt, u8_dev(codes), u8_dev(scales),
-                            f32_dev(ts) if fmt == 0 else None)
-    torch.cuda.synchronize()
+                            f32_dev(ts) if fmt == 0 else None, out=g.t)
+    g.check(f"grouped {what}")
     yg = f64_of_bf16(bits_host(y))
     y64 = O.grouped_linear(fmt, x, row_index, offsets, codes, scales, ts)
     xn = np.sqrt((f64_of_bf16(x) ** 2).sum(axis=1))[row_index][:, None]

@@ -10,7 +10,7 @@ import torch
 
 import oracle as O
 from mxfp4_bit_weight_amd import workloads as W
-from tests.gpu_util import (DEV, bf16_dev, bits_host, check_bound, f64_of_bf16, qweight_dev, say,
+from tests.gpu_util import (Guarded, DEV, bf16_dev, bits_host, check_bound, f64_of_bf16, qweight_dev, say,
                             weff_norms)
 
 pytestmark = pytest.mark.gpu
@@ -25,10 +25,10 @@ def fp4w():
 def _run_dev(fp4w, fmt, w, x, a, b, nan_out=False):
     codes, scales, st = O.quantize(fmt, w)
     q = qweight_dev(fp4w, fmt, codes, scales, st)
-    out = torch.full((x.shape[0], q.n), float("nan"), dtype=torch.bfloat16, device=DEV) if nan_out else None
+    g = Guarded((x.shape[0], q.n), torch.bfloat16, float("nan") if nan_out else None)
     y = fp4w.linear(bf16_dev(x), q, bf16_dev(a) if a is not None else None, bf16_dev(b) if b is not None else None,
-                    out=out)
-    torch.cuda.synchronize()
+                    out=g.t)
+    g.check(f"linear fmt={fmt} m={x.shape[0]} n={q.n} k={q.k}")
     return y, codes, scales, st
 
 

@@ -20,7 +20,7 @@ import torch
 
 import oracle as O
 from mxfp4_bit_weight_amd import workloads as W
-from tests.gpu_util import DEV, bf16_dev, bits_host, f32_dev, f64_of_bf16, qweight_dev, say
+from tests.gpu_util import DEV, Guarded, bf16_dev, bits_host, f32_dev, f64_of_bf16, qweight_dev, say
 
 pytestmark = pytest.mark.gpu
 
@@ -61,10 +61,11 @@ def _check(fmt, got, x, gamma, noise, sigma, eps, codes, scales, st, a, b, what)
 def _run(fp4w, fmt, x, gamma, noise, sigma, eps, codes, scales, st, a, b):
     q = qweight_dev(fp4w, fmt, codes, scales, st)
     m, n = x.shape[0], codes.shape[0]
-    out = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    g = Guarded((m, n), torch.bfloat16, float("nan"))
+    out = g.t
     fp4w.linear_aqn(bf16_dev(x), bf16_dev(gamma), f32_dev(noise), sigma, q,
                     bf16_dev(a) if a is not None else None, bf16_dev(b) if b is not None else None, eps=eps, out=out)
-    torch.cuda.synchronize()
+    g.check(f"linear aqn m={m} n={n}")
     return f64_of_bf16(bits_host(out)), q
 
 

@@ -21,7 +21,7 @@ import torch
 
 import oracle as O
 from mxfp4_bit_weight_amd import workloads as W
-from tests.gpu_util import DEV, bf16_dev, bits_host, check_bound, f32_dev, f64_of_bf16, qweight_dev, say
+from tests.gpu_util import DEV, Guarded, bf16_dev, bits_host, check_bound, f32_dev, f64_of_bf16, qweight_dev, say
 
 pytestmark = pytest.mark.gpu
 
@@ -62,8 +62,12 @@ def test_lora_gradients_ragged(fp4w, m, n, k, r):
     what = f"m={m} n={n} k={k} r={r}"
     say(f"[lora grad] {what}")
     dy, x, a, b = _inputs(m + 3 * r, m, n, k, r)
-    u, ga, gb = fp4w.lora_backward(bf16_dev(dy), bf16_dev(x), bf16_dev(a), bf16_dev(b))
-    torch.cuda.synchronize()
+    guards = [Guarded((m, r), torch.float32, float("nan")), Guarded((r, k), torch.float32, float("nan")),
+              Guarded((n, r), torch.float32, float("nan"))]
+    u, ga, gb = fp4w.lora_backward(bf16_dev(dy), bf16_dev(x), bf16_dev(a), bf16_dev(b),
+                                   out=tuple(g.t for g in guards))
+    for g in guards:
+        g.check(f"lora grads {what}")
     _check_grads(what, dy, x, a, b, u.double().cpu().numpy(), ga.double().cpu().numpy(), gb.double().cpu().numpy())
     # the same call again: bit for bit (every sum in a fixed order)
     u2, ga2, gb2 = fp4w.lora_backward(bf16_dev(dy), bf16_dev(x), bf16_dev(a), bf16_dev(b))

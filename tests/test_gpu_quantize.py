@@ -6,7 +6,7 @@ import torch
 
 import oracle as O
 from mxfp4_bit_weight_amd import workloads as W
-from tests.gpu_util import DEV, bf16_dev, f32_dev, qweight_host, say, u8_dev
+from tests.gpu_util import DEV, guarded_qweight, bf16_dev, f32_dev, qweight_host, say, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -18,8 +18,11 @@ def fp4w():
 
 
 def _gpu_quant(fp4w, w_bits, fmt):
-    q = fp4w.quantize(bf16_dev(w_bits), fmt)
-    torch.cuda.synchronize()
+    n, k = w_bits.shape
+    out, guards = guarded_qweight(fp4w, fmt, n, k)
+    q = fp4w.quantize(bf16_dev(w_bits), fmt, out=out)
+    for g in guards:
+        g.check(f"quantize fmt={fmt} shape={w_bits.shape}")
     return qweight_host(q)
 
 

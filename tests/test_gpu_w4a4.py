@@ -11,7 +11,7 @@ import torch
 
 import oracle as O
 from mxfp4_bit_weight_amd import workloads as W
-from tests.gpu_util import DEV, bf16_dev, bits_host, check_bound, f64_of_bf16, say, u8_dev
+from tests.gpu_util import DEV, Guarded, bf16_dev, bits_host, check_bound, f64_of_bf16, say, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -44,8 +44,9 @@ def _inputs(seed, m, n, k):
 
 
 def _full(fp4w, xc, xs, wc, ws, what):
-    y = fp4w.linear_w4a4(_q_dev(fp4w, xc, xs), _q_dev(fp4w, wc, ws))
-    torch.cuda.synchronize()
+    g = Guarded((xc.shape[0], wc.shape[0]), torch.bfloat16, float("nan"))
+    y = fp4w.linear_w4a4(_q_dev(fp4w, xc, xs), _q_dev(fp4w, wc, ws), out=g.t)
+    g.check(f"w4a4 {what}")
     yg = f64_of_bf16(bits_host(y))
     y64 = O.linear_w4a4(xc, xs, wc, ws)
     return check_bound(yg, y64, _norms(xc, xs)[:, None], _norms(wc, ws)[None, :], what)

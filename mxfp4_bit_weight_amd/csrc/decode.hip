@@ -62,7 +62,7 @@ constexpr int DQ_ROWS = 16;        // weight rows per tile
 constexpr int DQ_MAX_R = 64;       // LoRA rank staged in LDS
 
 // LDS layout of one workgroup (byte offsets):
-//   zeros   128 (spw + 1)          A lanes that carry no x read here (spw: steps per wave)
+//   zeros   128 (spw + 1)          A lanes that carry no x read here (spw: the longest part of a wave)
 //   xh, xl  m rows x (kslice + 16) high / low E4M3 terms (rows padded against bank conflicts)
 //   sc      m x 2 x nblkp          E8M0 codes of the terms, byte 4 j + b = block b of step j
 //   ws      16 x srow              the tile rows' weight-scale bytes of the slice
@@ -70,6 +70,21 @@ constexpr int DQ_MAX_R = 64;       // LoRA rank staged in LDS
 //   lt      m x r fp32             t = x A^T
 //   red     nw x m x 16 fp32       wave partials
 //   lr      nw x m x r fp32        wave partials of a LoRA chunk
+// Steps of a slice per wave: wave 0 takes `first`, the others `rest` each.  With
+// LoRA and 4 waves, wave 0 (the one that fetches t and arrives when its part is
+// done) takes kDqLoraLead steps fewer than an even share, so that its wait for t
+// and its arrival overlap the other waves' streaming instead of trailing it
+// (MI355X, m = 1: 18944 x 3584 12.2 -> 11.6 us; with 8 or 16 waves the waves end
+// spread out anyway, and a short part was slower: 3584 x 18944 12.9 -> 13.6 us).
+constexpr int kDqLoraLead = 3;
+struct DqParts { int first, rest; };
+__host__ __device__ inline DqParts dq_parts(int nss, int nw, bool lora) {
+  const int even = (nss + nw - 1) / nw;
+  if (!lora || nw != 4 || even <= kDqLoraLead) return DqParts{even, even};
+  const int first = even - kDqLoraLead;
+  return DqParts{first, (nss - first + nw - 2) / (nw - 1)};
+}
+
 struct DqLayout {
   int kslice, xrow, nblkp, srow, spw;
   int zero_off, xh_off, xl_off, sc_off, ws_off, lb_off, lt_off, red_off, lr_off, bytes;
@@ -82,7 +97,7 @@ __host__ __device__ inline DqLayout dq_layout(int fmt, int m, int kslice, int nw
   L.xrow = kslice + 16;
   L.nblkp = ((kslice / 32) + 3) & ~3;
   L.srow = ((kslice / blk) + 15) & ~15;
-  L.spw = (kslice / DQ_STEP + nw - 1) / nw;
+  L.spw = dq_parts(kslice / DQ_STEP, nw, r > 0).rest;     // the longest part
   int off = 0;
   L.zero_off = off; off += DQ_STEP * (L.spw + 1);
   L.xh_off = off;   off += m * L.xrow;
@@ -193,9 +208,9 @@ void decode_f8f4_kernel(
 
   // ---- 2. the code ring: every load of this wave's part in flight ---------------
   const int n = lane & 15, g = lane >> 4;
-  const int spw = (nss + NW - 1) / NW;
-  const int j0 = wave * spw;
-  const int j1 = min(j0 + spw, nss);
+  const DqParts pp = dq_parts(nss, NW, LORA);
+  const int j0 = wave == 0 ? 0 : pp.first + (wave - 1) * pp.rest;
+  const int j1 = min(j0 + (wave == 0 ? pp.first : pp.rest), nss);
   const int64_t tile_rows = min((int64_t)DQ_ROWS, N - row_base);
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes + row_base * (K / 2), (uint32_t)(tile_rows * (K / 2)));
   const uint32_t lane_off = (uint32_t)(n * (K / 2) + (k0 + 32 * g) / 2);
@@ -558,7 +573,7 @@ DecodeConfig plan_decode_f8f4(int fmt, int64_t m, int64_t n, int64_t k, int r) {
   while (ntiles * c.nw * s < kDqTargetWaves && (sps_for(s + 1) + c.nw - 1) / c.nw >= 4) s++;
   c.sps = (int)sps_for(s);
   c.splits = (int)((nsteps + c.sps - 1) / c.sps);
-  const int spw = (c.sps + c.nw - 1) / c.nw;
+  const int spw = dq_parts(c.sps, c.nw, r > 0).rest;    // the longest part of a wave
   c.depth = spw <= 8 ? 8 : 16;
   return c;
 }

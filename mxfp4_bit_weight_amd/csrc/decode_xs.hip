@@ -212,6 +212,29 @@ __device__ __forceinline__ void xs_body(
   const uint32_t span_blen = SB * (uint32_t)(qs1 - s * qspan);
   u32x4_t scv[XS_SC_UNITS];
 
+  // ---- 5. the tiles' loads, then stream ----------------------------------------------
+  // Issued once every wave of the workgroup has issued its x loads (requests
+  // already in flight delay a later x load by most of the stream: they are not
+  // served first), before x has arrived: x returns first, and the first tiles'
+  // latency overlaps the conversion of x.
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  if (SC) {
+#pragma unroll
+    for (int c = 0; c < XS_SC_UNITS; c++) {
+      const int e = tid + c * nt;
+      const int ti = e / (XS_ROWS * upr), rem = e - ti * XS_ROWS * upr;
+      const int r0 = rem / upr, ch = rem - r0 * upr;
+      const int64_t row = tile_of(ti) * XS_ROWS + r0;
+      const bool ok = (e < sc_units) & (row < N) & (16u * (uint32_t)ch < span_blen);
+      scv[c] = buffer_load16(srs, ok ? (uint32_t)row * sbr + span_b0 + 16u * (uint32_t)ch : kBufferOob);
+    }
+  }
+#pragma unroll
+  for (int ti = 0; ti < RP; ti++) load_tile(ti);
+  __builtin_amdgcn_sched_barrier(0);
+
   // ---- 4. x to the operand format -------------------------------------------------
   // Largest |x| of each row over this wave's K groups, as the 15 magnitude bits
   // of bf16 (integer order = magnitude order, Inf and NaN on top); lanes r,
@@ -257,25 +280,6 @@ __device__ __forceinline__ void xs_body(
     fr[i] = __shfl(fin, 4 * g + i, 64);
   }
 
-  // ---- 5. the tiles' loads, then stream ----------------------------------------------
-  // Issued only once every wave of the workgroup holds its x: requests already in
-  // flight delay a later x load by most of the stream (they are not served first).
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  if (SC) {
-#pragma unroll
-    for (int c = 0; c < XS_SC_UNITS; c++) {
-      const int e = tid + c * nt;
-      const int ti = e / (XS_ROWS * upr), rem = e - ti * XS_ROWS * upr;
-      const int r0 = rem / upr, ch = rem - r0 * upr;
-      const int64_t row = tile_of(ti) * XS_ROWS + r0;
-      const bool ok = (e < sc_units) & (row < N) & (16u * (uint32_t)ch < span_blen);
-      scv[c] = buffer_load16(srs, ok ? (uint32_t)row * sbr + span_b0 + 16u * (uint32_t)ch : kBufferOob);
-    }
-  }
-#pragma unroll
-  for (int ti = 0; ti < RP; ti++) load_tile(ti);
   if (SC) {
     u32x4_t* ssc = reinterpret_cast<u32x4_t*>(lds + L.ssc_off);
 #pragma unroll

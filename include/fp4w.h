@@ -324,9 +324,10 @@ size_t fp4w_linear_aqn_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
  * fp4w_aqn_rmsnorm's (gamma_bf16, noise, sigma, eps) followed by fp4w_linear's;
  * gamma and noise 16-byte aligned, workspace 256-byte aligned and at least
  * fp4w_linear_aqn_workspace_bytes(m, n, k, r).
- * Where the linear runs as one decode launch over the whole K (m <= 2 and no K
- * split, as for k = 3584 at any n of the Qwen-2.5-7B projections) the norm runs
- * inside it: each workgroup forms bf16(x * gamma * (1 + sigma * noise)) while
+ * Where the linear runs as one decode launch whose workgroups each cover the
+ * whole K (m <= 16 with no K split, as for k = 3584 at any n of the Qwen-2.5-7B
+ * projections) the norm runs inside it: each workgroup forms
+ * bf16(x * gamma * (1 + sigma * noise)) while
  * staging x, sums x^2 of its rows in fp32, and multiplies its fp32 outputs (with
  * the LoRA term) by 1 / sqrt(mean(x^2) + eps) before the one rounding to bf16.
  * Elsewhere fp4w_aqn_rmsnorm writes x~ into the workspace and fp4w_linear reads

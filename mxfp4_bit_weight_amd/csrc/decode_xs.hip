@@ -46,6 +46,7 @@
 namespace fp4w {
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int XS_ROWS = 16;          // weight rows per tile (MFMA columns)
@@ -63,20 +64,35 @@ constexpr int XS_RING = 2;           // tiles of code loads in flight per wave
 //   lt    [m][r] fp32            t over the span
 //   ssc   [tg * 16][span_bytes]   block-scale bytes of the tiles' rows over the span
 //                                 (staged mode; span_bytes = scale bytes of qspan groups)
+//   gain  [nw][256] fp32          noisy RMSNorm: gamma (1 + sigma noise) over each wave's K groups
+//   ss    [16][nw4] fp32          noisy RMSNorm: each wave's sums of x^2 of the rows
+//                                 (nw4 = nw rounded up to 4; the slots past nw hold 0)
+// (every region starts 16-byte aligned)
 struct XsLayout {
-  int red_off, tred_off, lb_off, lt_off, ssc_off, bytes;
+  int red_off, tred_off, lb_off, lt_off, ssc_off, gain_off, ss_off, bytes;
 };
-__host__ __device__ inline XsLayout xs_layout(int m, int nw, int tg, int r, int span_bytes) {
+__host__ __device__ inline XsLayout xs_layout(int m, int nw, int tg, int r, int span_bytes, bool aqn = false) {
   XsLayout L;
   int off = 0;
   L.red_off = off;  off += nw * tg * m * XS_ROWS * 4;
-  L.tred_off = off; off += nw * m * r * 4;
+  L.tred_off = off; off += (nw * m * r * 4 + 15) & ~15;
   L.lb_off = off;   off += (tg * XS_ROWS * r * 2 + 15) & ~15;
   L.lt_off = off;   off += (m * r * 4 + 15) & ~15;
   L.ssc_off = off;  off += tg * XS_ROWS * span_bytes;
+  L.gain_off = off; off += aqn ? nw * 128 * XS_CPW * 4 : 0;
+  L.ss_off = off;   off += aqn ? XS_ROWS * ((nw + 3) & ~3) * 4 : 0;
   L.bytes = off;
   return L;
 }
+
+// The noisy RMSNorm ahead of the product (one span of K only): row m of x enters
+// as bf16(x gamma (1 + sigma noise)), and the row's sums are multiplied by
+// 1 / sqrt(mean_k x^2 + eps) at the end.
+struct XsAqn {
+  const uint16_t* gamma;    // (K) bf16
+  const float* noise;       // (K) fp32
+  float sigma, eps;
+};
 
 __device__ __forceinline__ f16x8_t bits_as_f16x8(u32x4_t v) { return __builtin_bit_cast(f16x8_t, v); }
 __device__ __forceinline__ bf16x8_t bits_as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -110,7 +126,9 @@ __device__ __forceinline__ bf16x8_t codes8_to_bf16_pow2(uint32_t dw, float pow2)
 // LORA: t = x A^T comes from the launch's chunk workgroups (lora_handover.hpp):
 // wave 0 waits for it in the epilogue, reader `rd` of `nread`, and span 0 adds
 // t B^T to its outputs.
-template <int FMT, int TG, int SC, bool LORA>
+// AQN (S = 1 only): the noisy RMSNorm of `aq` is applied to x on the way in, its
+// row factor to the sums on the way out (t then comes from gained x as well).
+template <int FMT, int TG, int SC, bool LORA, bool AQN>
 __device__ __forceinline__ void xs_body(
     uint8_t* __restrict__ lds, int* flag, int* have_t, const uint16_t* __restrict__ x,
     const int32_t* __restrict__ xrow, int64_t xrows, int M, int64_t K, const uint8_t* __restrict__ codes,
@@ -118,7 +136,7 @@ __device__ __forceinline__ void xs_body(
     const uint16_t* __restrict__ lora_a, const uint16_t* __restrict__ lora_b, int r, int lparts, int lsw,
     uint32_t* __restrict__ lsync, uint64_t wait_ticks, uint16_t* __restrict__ y, float* __restrict__ part,
     uint32_t* __restrict__ cnt, int S, int qspan, int ntiles, int G, int tg, int lb16, int s, int gi, int rd,
-    int nread) {
+    int nread, XsAqn aq) {
   constexpr int CPW = XS_CPW;
   const int nt = (int)blockDim.x;
   const int nw = nt >> 6;
@@ -135,7 +153,7 @@ __device__ __forceinline__ void xs_body(
   const int rr = LORA ? r : 0;                     // LoRA rank (0: none)
   constexpr uint32_t SB = FMT == FMT_NVFP4 ? 2u : 1u;              // scale bytes per 32-wide group
   const int span_bytes = SC ? (int)SB * qspan : 0;
-  const XsLayout L = xs_layout(M, nw, tg, rr, span_bytes);
+  const XsLayout L = xs_layout(M, nw, tg, rr, span_bytes, AQN);
 
   // lane (n, g) takes the 32-wide K groups q(u) = qw0 + 4 u + g of the span
   bool qok[CPW];
@@ -176,6 +194,21 @@ __device__ __forceinline__ void xs_body(
   int64_t lb0 = -1;
   if (lb16 && tid < lb_units) lb0 = lb_off(tid);
   const u32x4_t lbv = buffer_load16(brs, lb0 >= 0 ? (uint32_t)(lb0 * 2) : kBufferOob);
+  // AQN: gamma and noise of the wave's K groups, 8 elements per lane j < GU
+  // (group qw0 + j / 4, elements 8 (j % 4) .. + 7; groups past the span read
+  // zeros, so their gain is 0)
+  constexpr int GU = 16 * CPW;
+  u32x4_t gmv = {0u, 0u, 0u, 0u}, nz0 = gmv, nz1 = gmv;
+  if (AQN) {
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(aq.gamma, (uint32_t)(K * 2));
+    const __amdgpu_buffer_rsrc_t nrs = make_rsrc(aq.noise, (uint32_t)(K * 4));
+    const int qj = qw0 + (lane >> 2);
+    const uint32_t k8 = (uint32_t)(32 * qj + 8 * (lane & 3));
+    const bool ok = lane < GU && qj < qs1;
+    gmv = buffer_load16(grs, ok ? 2u * k8 : kBufferOob);
+    nz0 = buffer_load16(nrs, ok ? 4u * k8 : kBufferOob);
+    nz1 = buffer_load16(nrs, ok ? 4u * k8 + 16u : kBufferOob);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 2. code and scale loads of a tile (tiles past the run read nothing) -------------
@@ -236,21 +269,83 @@ __device__ __forceinline__ void xs_body(
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 4. x to the operand format -------------------------------------------------
+  if (AQN) {
+    // the gain g = gamma (1 + sigma noise) of the wave's K groups into its LDS
+    // slice, then every lane forms bf16(x g) of its elements and its rows' sums
+    // of x^2 (no other wave reads the slice: no workgroup barrier)
+    float* gl = reinterpret_cast<float*>(lds + L.gain_off) + wave * (8 * GU);
+    if (lane < GU) {
+      f32x4_t g0, g1;
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        const uint32_t gb = gmv[d >> 1];
+        const float gm = (d & 1) ? bf16hi_f32(gb) : bf16lo_f32(gb);
+        g0[d] = gm * __builtin_fmaf(aq.sigma, __uint_as_float(nz0[d]), 1.0f);
+        const uint32_t gb1 = gmv[2 + (d >> 1)];
+        const float gm1 = (d & 1) ? bf16hi_f32(gb1) : bf16lo_f32(gb1);
+        g1[d] = gm1 * __builtin_fmaf(aq.sigma, __uint_as_float(nz1[d]), 1.0f);
+      }
+      *reinterpret_cast<f32x4_t*>(gl + 8 * lane) = g0;
+      *reinterpret_cast<f32x4_t*>(gl + 8 * lane + 4) = g1;
+    }
+    // the rows' sums of x^2 (x as it came in) while the writes land
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < CPW; u++)
+#pragma unroll
+      for (int sub = 0; sub < 4; sub++)
+#pragma unroll
+        for (int d = 0; d < 4; d++) ss = bf16x2_sumsq(xa[u][sub][d], ss);
+    __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0): the slice is written; loads stay in flight
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    // unit i = (u, sub) of the lane: k = 32 (qw0 + 4 u + g) + 8 sub; its gain sits
+    // at 32 (4 u + g) + 8 sub of the slice (groups past the span were staged as
+    // 0, and their x is 0: no select).  The next unit's gain is read while this
+    // one is formed.
+    constexpr int NU = 4 * CPW;
+    auto gain_at = [&](int i, f32x4_t& ga, f32x4_t& gb) {
+      int kl = 32 * (4 * (i >> 2) + g) + 8 * (i & 3);
+      asm volatile("" : "+v"(kl));               // read here, not hoisted
+      ga = *reinterpret_cast<const f32x4_t*>(gl + kl);
+      gb = *reinterpret_cast<const f32x4_t*>(gl + kl + 4);
+    };
+    f32x4_t ga_n, gb_n;
+    gain_at(0, ga_n, gb_n);
+#pragma unroll
+    for (int i = 0; i < NU; i++) {
+      const f32x4_t ga = ga_n, gb = gb_n;
+      if (i + 1 < NU) gain_at(i + 1, ga_n, gb_n);
+      const int u = i >> 2, sub = i & 3;
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        const uint32_t w = xa[u][sub][d];
+        const float g0 = d < 2 ? ga[2 * d] : gb[2 * d - 4];
+        const float g1 = d < 2 ? ga[2 * d + 1] : gb[2 * d - 3];
+        xa[u][sub][d] = f32x2_to_bf16x2_rne(bf16lo_f32(w) * g0, bf16hi_f32(w) * g1);
+        asm volatile("" : "+v"(xa[u][sub][d]));   // formed here, one unit at a time
+      }
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const int nw4 = (nw + 3) & ~3;
+    float* ssw = reinterpret_cast<float*>(lds + L.ss_off);
+    if (g == 0) ssw[n * nw4 + wave] = ss;
+    if (wave == 0 && lane < XS_ROWS * (nw4 - nw))     // the slots past the last wave
+      ssw[(lane / (nw4 - nw)) * nw4 + nw + lane % (nw4 - nw)] = 0.f;
+  }
   // Largest |x| of each row over this wave's K groups, as the 15 magnitude bits
   // of bf16 (integer order = magnitude order, Inf and NaN on top); lanes r,
-  // r + 16, r + 32, r + 48 hold row r.
-  uint32_t mx = 0;
+  // r + 16, r + 32, r + 48 hold row r.  Both halves at once (v_pk_max_u16).
+  u16x2_t mxp = {0, 0};
 #pragma unroll
   for (int u = 0; u < CPW; u++)
 #pragma unroll
     for (int sub = 0; sub < 4; sub++)
 #pragma unroll
-      for (int d = 0; d < 4; d++) {
-        const uint32_t w = xa[u][sub][d];
-        const uint32_t a = w & 0x7FFFu, b = (w >> 16) & 0x7FFFu;
-        const uint32_t m2 = a > b ? a : b;
-        mx = m2 > mx ? m2 : mx;
-      }
+      for (int d = 0; d < 4; d++)
+        mxp = __builtin_elementwise_max(mxp, __builtin_bit_cast(u16x2_t, xa[u][sub][d] & 0x7FFF7FFFu));
+  uint32_t mx = mxp[0] > mxp[1] ? (uint32_t)mxp[0] : (uint32_t)mxp[1];
   if (xrow && n < M && !xr_ok) mx = 0x7F80u;     // a routed row without a valid token: NaN outputs
   {
     uint32_t o = (uint32_t)__shfl_xor((int)mx, 16, 64);
@@ -376,7 +471,8 @@ __device__ __forceinline__ void xs_body(
   }
   __syncthreads();
   if (LORA && __builtin_expect(!*have_t, 0))      // the wait ran out (span 0): the chunks formed here
-    lora_form_all(reinterpret_cast<float*>(lds + L.tred_off), lt, x, M, K, lora_a, rr, nw, lsw, lparts);
+    lora_form_all(reinterpret_cast<float*>(lds + L.tred_off), lt, x, M, K, lora_a, rr, nw, lsw, lparts,
+                  AQN ? XGain{aq.gamma, aq.noise, aq.sigma} : XGain{nullptr, nullptr, 0.f});
 
   // ---- 7. tile sums in wave order (+ the span's LoRA term); spans in span order --------
   const float st = (FMT == FMT_NVFP4) ? *tensor_scale : 1.0f;
@@ -398,6 +494,19 @@ __device__ __forceinline__ void xs_body(
       float l = 0.f;
       for (int j = 0; j < rr; j++) l = __builtin_fmaf(lt[m * rr + j], __uint_as_float((uint32_t)b[j] << 16), l);
       v += l;
+    }
+    if (AQN) {                                   // the row factor of the norm, waves in order
+      const int m = rem / XS_ROWS, nw4 = (nw + 3) & ~3;
+      const f32x4_t* ssv = reinterpret_cast<const f32x4_t*>(lds + L.ss_off) + m * (nw4 / 4);
+      float ss = 0.f;
+      for (int w4 = 0; w4 < nw4 / 4; w4++) {
+        const f32x4_t v = ssv[w4];
+        ss += v[0];
+        ss += v[1];
+        ss += v[2];
+        ss += v[3];
+      }
+      v *= 1.0f / __builtin_sqrtf(ss / (float)K + aq.eps);
     }
     if (S > 1) {
       store_agent(&part[((int64_t)s * ntiles + tile_of(ti)) * per_tile + rem], v);
@@ -426,26 +535,27 @@ __device__ __forceinline__ void xs_body(
 
 // Dense: LORA workgroups below lparts form the chunks of t (and stream no codes);
 // workgroup lparts + bid takes span bid % S of tile run bid / S.
-template <int FMT, int TG, int SC, bool LORA>
+template <int FMT, int TG, int SC, bool LORA, bool AQN>
 __global__ __launch_bounds__(64 * XS_MAX_WAVES) void decode_xs_kernel(
     const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, int64_t N,
     const uint16_t* __restrict__ lora_a, const uint16_t* __restrict__ lora_b, int r, int lparts, int lsw,
     uint32_t* __restrict__ lsync, uint64_t wait_ticks, uint16_t* __restrict__ y, float* __restrict__ part,
-    uint32_t* __restrict__ cnt, int S, int qspan, int ntiles, int G, int tg, int lb16) {
+    uint32_t* __restrict__ cnt, int S, int qspan, int ntiles, int G, int tg, int lb16, XsAqn aq) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int flag, have_t;
   if (LORA && (int)blockIdx.x < lparts) {
     const XsLayout L = xs_layout(M, (int)blockDim.x >> 6, tg, r, 0);
     lora_chunk_publish(reinterpret_cast<float*>(lds + L.tred_off), x, M, K, lora_a, r, (int)blockIdx.x,
-                       (int)blockDim.x >> 6, lsw, lsync, G, lparts);
+                       (int)blockDim.x >> 6, lsw, lsync, G, lparts,
+                       AQN ? XGain{aq.gamma, aq.noise, aq.sigma} : XGain{nullptr, nullptr, 0.f});
     return;
   }
   const int bid = (int)blockIdx.x - (LORA ? lparts : 0);
   const int s = bid % S, gi = bid / S;
-  xs_body<FMT, TG, SC, LORA>(lds, &flag, &have_t, x, nullptr, M, M, K, codes, scales, tensor_scale, N, lora_a,
-                             lora_b, r, lparts, lsw, lsync, wait_ticks, y, part, cnt, S, qspan, ntiles, G, tg, lb16,
-                             s, gi, gi, G);
+  xs_body<FMT, TG, SC, LORA, AQN>(lds, &flag, &have_t, x, nullptr, M, M, K, codes, scales, tensor_scale, N, lora_a,
+                                  lora_b, r, lparts, lsw, lsync, wait_ticks, y, part, cnt, S, qspan, ntiles, G, tg,
+                                  lb16, s, gi, gi, G, aq);
 }
 
 // ---------------------------------------------------------------------------------
@@ -473,9 +583,9 @@ __global__ __launch_bounds__(64 * XS_MAX_WAVES) void grouped_xs_kernel(
   const float* te = FMT == FMT_NVFP4 ? tscales + e : nullptr;
   for (; q0 < q1; q0 += XS_MAX_M) {
     const int mc = (int)(q1 - q0 < XS_MAX_M ? q1 - q0 : XS_MAX_M);
-    xs_body<FMT, TG, SC, false>(lds, &flag, &have_t, x, row_index + q0, num_tokens, mc, K, ce, se, te, N, nullptr,
-                                nullptr, 0, 0, 0, nullptr, 0, y + q0 * N, nullptr, nullptr, 1, qspan, ntiles, G, tg, 0,
-                                0, gi, 0, 0);
+    xs_body<FMT, TG, SC, false, false>(lds, &flag, &have_t, x, row_index + q0, num_tokens, mc, K, ce, se, te, N,
+                                       nullptr, nullptr, 0, 0, 0, nullptr, 0, y + q0 * N, nullptr, nullptr, 1, qspan,
+                                       ntiles, G, tg, 0, 0, gi, 0, 0, XsAqn{nullptr, nullptr, 0.f, 0.f});
     __syncthreads();                             // LDS is reused by the next chunk
   }
 }
@@ -530,26 +640,29 @@ struct XsLaunch {
   float* part;
   uint32_t* cnt;
   int G, tg, lb16;
+  XsAqn aq;
 };
 
-template <int FMT, int TG, int SC, bool LORA>
+template <int FMT, int TG, int SC, bool LORA, bool AQN>
 static hipError_t launch_xs_tg(dim3 grid, dim3 block, size_t lds, hipStream_t stream, const XsLaunch& a,
                                const XsConfig& c) {
   static std::atomic<uint64_t> lds_done{0};
   {
-    hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&decode_xs_kernel<FMT, TG, SC, LORA>), kXsMaxLds, lds_done);
+    hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&decode_xs_kernel<FMT, TG, SC, LORA, AQN>), kXsMaxLds,
+                                    lds_done);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_xs_kernel<FMT, TG, SC, LORA>), grid, block, lds, stream, a.x, a.m, a.k, a.codes, a.scales,
-                     a.ts, a.n, a.la, a.lb, a.r, a.lparts, a.lsw, a.lsync, (uint64_t)(LORA ? lora_wait_ticks() : 0),
-                     a.y, a.part, a.cnt, c.splits, c.qspan, c.ntiles, a.G, a.tg, a.lb16);
+  hipLaunchKernelGGL((decode_xs_kernel<FMT, TG, SC, LORA, AQN>), grid, block, lds, stream, a.x, a.m, a.k, a.codes,
+                     a.scales, a.ts, a.n, a.la, a.lb, a.r, a.lparts, a.lsw, a.lsync,
+                     (uint64_t)(LORA ? lora_wait_ticks() : 0), a.y, a.part, a.cnt, c.splits, c.qspan, c.ntiles, a.G,
+                     a.tg, a.lb16, a.aq);
   return hipGetLastError();
 }
 
-template <int FMT, bool LORA>
+template <int FMT, bool LORA, bool AQN>
 static hipError_t launch_xs_fmt(dim3 grid, dim3 block, size_t lds, hipStream_t stream, const XsLaunch& a,
                                 const XsConfig& c, int sc) {
-#define FP4W_XS(TGv, SCv) launch_xs_tg<FMT, TGv, SCv, LORA>(grid, block, lds, stream, a, c)
+#define FP4W_XS(TGv, SCv) launch_xs_tg<FMT, TGv, SCv, LORA, AQN>(grid, block, lds, stream, a, c)
   const int tg = a.tg;
   if (sc) {
     if (tg <= 1) return FP4W_XS(1, 1);
@@ -576,19 +689,25 @@ static int device_cu_count() {
   return cached[dev];
 }
 
-hipError_t launch_decode_xs(int fmt, const XsConfig& c, const void* x, int64_t m, int64_t k, const uint8_t* codes,
-                            const uint8_t* scales, const float* ts, int64_t n, const void* la, const void* lb, int r,
-                            uint32_t* lsync, void* y, float* part, uint32_t* cnt, hipStream_t stream) {
-  const int rr = la && lb && k > 0 ? r : 0;      // k = 0: t = x A^T is zero
-  if (rr > XS_MAX_R || m * rr > 1024) return hipErrorInvalidValue;
+// The launch shape of one call: LoRA chunks, tile runs, staged scales and LDS.
+struct XsGeometry {
+  int lsw, lparts;
+  int64_t G, tg;
+  int sc;
+  size_t lds;
+  bool ok;
+};
+static XsGeometry xs_geometry(int fmt, const XsConfig& c, int64_t m, int64_t k, int rr, const uint8_t* scales,
+                              bool aqn) {
+  XsGeometry q{};
   // chunk workgroups of the LoRA down-projection go first in the grid
-  const int lsw = rr > 0 ? lora_chunk_steps(c.nw, k, (int)m * rr) : kLoraStepsPerLoad;
-  const int lparts = rr > 0 ? lora_chunk_count(c.nw, k, lsw) : 0;
+  q.lsw = rr > 0 ? lora_chunk_steps(c.nw, k, (int)m * rr) : kLoraStepsPerLoad;
+  q.lparts = rr > 0 ? lora_chunk_count(c.nw, k, q.lsw) : 0;
   // tile runs: about kXsGroupsPerCu workgroups per CU over all spans, the chunk
   // workgroups included (one more workgroup than the chip holds at once would
   // start after the first ones finish, adding a whole workgroup's time), at most
   // kXsMaxTilesPerGroup tiles each, never more runs than tiles
-  int64_t G = ((int64_t)device_cu_count() * kXsGroupsPerCu - lparts) / c.splits;
+  int64_t G = ((int64_t)device_cu_count() * kXsGroupsPerCu - q.lparts) / c.splits;
   if (G > c.ntiles) G = c.ntiles;
   if (G > kTileSlots) G = kTileSlots;
   if (G < 1) G = 1;
@@ -597,18 +716,40 @@ hipError_t launch_decode_xs(int fmt, const XsConfig& c, const void* x, int64_t m
     tg = kXsMaxTilesPerGroup;
     G = (c.ntiles + tg - 1) / tg;
   }
-  if (c.splits > 1 && G > kTileSlots) return hipErrorInvalidValue;     // arrival counters would not fit
+  q.G = G;
+  q.tg = tg;
+  q.ok = !(c.splits > 1 && G > kTileSlots);        // arrival counters must fit
   // staged scales: 16-byte aligned rows and spans, few enough units per thread
   const int sb = fmt == FMT_NVFP4 ? 2 : 1;
   const int64_t span_bytes = (int64_t)sb * c.qspan;
-  int sc = (reinterpret_cast<uintptr_t>(scales) & 15u) == 0 && ((k / 32) * sb) % 16 == 0 && span_bytes % 16 == 0 &&
-           tg * XS_ROWS * (span_bytes / 16) <= (int64_t)XS_SC_UNITS * 64 * c.nw ? 1 : 0;
-  size_t lds = (size_t)xs_layout((int)m, c.nw, (int)tg, rr, sc ? (int)span_bytes : 0).bytes;
-  if (lds > (size_t)kXsMaxLds && sc) {
-    sc = 0;
-    lds = (size_t)xs_layout((int)m, c.nw, (int)tg, rr, 0).bytes;
+  q.sc = (reinterpret_cast<uintptr_t>(scales) & 15u) == 0 && ((k / 32) * sb) % 16 == 0 && span_bytes % 16 == 0 &&
+                 tg * XS_ROWS * (span_bytes / 16) <= (int64_t)XS_SC_UNITS * 64 * c.nw
+             ? 1
+             : 0;
+  q.lds = (size_t)xs_layout((int)m, c.nw, (int)tg, rr, q.sc ? (int)span_bytes : 0, aqn).bytes;
+  if (q.lds > (size_t)kXsMaxLds && q.sc) {
+    q.sc = 0;
+    q.lds = (size_t)xs_layout((int)m, c.nw, (int)tg, rr, 0, aqn).bytes;
   }
-  if (lds > (size_t)kXsMaxLds) return hipErrorInvalidValue;
+  if (q.lds > (size_t)kXsMaxLds) q.ok = false;
+  return q;
+}
+
+bool decode_xs_fuses_aqn(int fmt, const XsConfig& c, int64_t m, int64_t k, int r, const uint8_t* scales) {
+  if (c.splits != 1 || m < 1 || m > XS_MAX_M || k <= 0) return false;
+  return xs_geometry(fmt, c, m, k, r, scales, true).ok;
+}
+
+hipError_t launch_decode_xs(int fmt, const XsConfig& c, const void* x, int64_t m, int64_t k, const uint8_t* codes,
+                            const uint8_t* scales, const float* ts, int64_t n, const void* la, const void* lb, int r,
+                            uint32_t* lsync, void* y, float* part, uint32_t* cnt, hipStream_t stream,
+                            const void* aqn_gamma, const float* aqn_noise, float aqn_sigma, float aqn_eps) {
+  const int rr = la && lb && k > 0 ? r : 0;      // k = 0: t = x A^T is zero
+  if (rr > XS_MAX_R || m * rr > 1024) return hipErrorInvalidValue;
+  const bool aqn = aqn_gamma != nullptr;
+  if (aqn && (c.splits != 1 || !aqn_noise)) return hipErrorInvalidValue;
+  const XsGeometry q = xs_geometry(fmt, c, m, k, rr, scales, aqn);
+  if (!q.ok) return hipErrorInvalidValue;
   XsLaunch a{};
   a.x = reinterpret_cast<const uint16_t*>(x);
   a.m = (int)m;
@@ -620,21 +761,31 @@ hipError_t launch_decode_xs(int fmt, const XsConfig& c, const void* x, int64_t m
   a.la = rr > 0 ? reinterpret_cast<const uint16_t*>(la) : nullptr;
   a.lb = reinterpret_cast<const uint16_t*>(lb);
   a.r = rr;
-  a.lsw = lsw;
-  a.lparts = lparts;
+  a.lsw = q.lsw;
+  a.lparts = q.lparts;
   a.lsync = lsync;
   a.y = reinterpret_cast<uint16_t*>(y);
   a.part = part;
   a.cnt = cnt;
-  a.G = (int)G;
-  a.tg = (int)tg;
+  a.G = (int)q.G;
+  a.tg = (int)q.tg;
   a.lb16 = (reinterpret_cast<uintptr_t>(lb) & 15u) == 0 && rr % 8 == 0 ? 1 : 0;
-  const dim3 grid((unsigned)(a.lparts + G * c.splits)), block((unsigned)(64 * c.nw));
-  if (fmt == FMT_NVFP4)
-    return rr > 0 ? launch_xs_fmt<FMT_NVFP4, true>(grid, block, lds, stream, a, c, sc)
-                  : launch_xs_fmt<FMT_NVFP4, false>(grid, block, lds, stream, a, c, sc);
-  return rr > 0 ? launch_xs_fmt<FMT_MXFP4, true>(grid, block, lds, stream, a, c, sc)
-                : launch_xs_fmt<FMT_MXFP4, false>(grid, block, lds, stream, a, c, sc);
+  a.aq = XsAqn{reinterpret_cast<const uint16_t*>(aqn_gamma), aqn_noise, aqn_sigma, aqn_eps};
+  const dim3 grid((unsigned)(a.lparts + q.G * c.splits)), block((unsigned)(64 * c.nw));
+  const size_t lds = q.lds;
+  const int sc = q.sc;
+  if (fmt == FMT_NVFP4) {
+    if (aqn)
+      return rr > 0 ? launch_xs_fmt<FMT_NVFP4, true, true>(grid, block, lds, stream, a, c, sc)
+                    : launch_xs_fmt<FMT_NVFP4, false, true>(grid, block, lds, stream, a, c, sc);
+    return rr > 0 ? launch_xs_fmt<FMT_NVFP4, true, false>(grid, block, lds, stream, a, c, sc)
+                  : launch_xs_fmt<FMT_NVFP4, false, false>(grid, block, lds, stream, a, c, sc);
+  }
+  if (aqn)
+    return rr > 0 ? launch_xs_fmt<FMT_MXFP4, true, true>(grid, block, lds, stream, a, c, sc)
+                  : launch_xs_fmt<FMT_MXFP4, false, true>(grid, block, lds, stream, a, c, sc);
+  return rr > 0 ? launch_xs_fmt<FMT_MXFP4, true, false>(grid, block, lds, stream, a, c, sc)
+                : launch_xs_fmt<FMT_MXFP4, false, false>(grid, block, lds, stream, a, c, sc);
 }
 
 // ---- grouped ------------------------------------------------------------------------

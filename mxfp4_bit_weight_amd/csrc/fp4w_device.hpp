@@ -81,6 +81,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+// Two fp32 -> two bf16 (lo in bits 15:0) in one v_cvt_pk_bf16_f32: round to
+// nearest even, the same bits as f32_to_bf16_rne for every input but NaN, which
+// stays a NaN (all 2^32 inputs compared on gfx950).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// acc + a.lo^2 + a.hi^2 for the two bf16 of a (v_dot2_f32_bf16).
+__device__ __forceinline__ float bf16x2_sumsq(uint32_t a, float acc) {
+  const bf16x2_t v = __builtin_bit_cast(bf16x2_t, a);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+
 // Round the exact value hi + lo (|lo| <= ulp(hi)/2, lo the exact remainder of
 // the fp32 rounding that produced hi) once, to nearest even, to bf16 bits.
 // Only an exact bf16 tie in hi needs lo: the exact value is above or below it.

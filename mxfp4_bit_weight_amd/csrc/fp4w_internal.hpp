@@ -81,9 +81,14 @@ bool decode_xs_supports(int64_t m, int64_t n, int64_t k, int r);
 XsConfig plan_decode_xs(int64_t m, int64_t n, int64_t k, int r);
 // LoRA operands: la = A (r x k bf16) and lb = B (n x r bf16), or nullptr (no
 // LoRA); the kernel forms t = x A^T itself (lora_handover.hpp, through lsync).
+// aqn_gamma (bf16, K) and aqn_noise (fp32, K), or nullptr: the noisy RMSNorm of x
+// fused ahead of the product (one K span only: decode_xs_fuses_aqn).
 hipError_t launch_decode_xs(int fmt, const XsConfig& c, const void* x, int64_t m, int64_t k, const uint8_t* codes,
                             const uint8_t* scales, const float* ts, int64_t n, const void* la, const void* lb, int r,
-                            uint32_t* lsync, void* y, float* part, uint32_t* cnt, hipStream_t stream);
+                            uint32_t* lsync, void* y, float* part, uint32_t* cnt, hipStream_t stream,
+                            const void* aqn_gamma = nullptr, const float* aqn_noise = nullptr, float aqn_sigma = 0.f,
+                            float aqn_eps = 0.f);
+bool decode_xs_fuses_aqn(int fmt, const XsConfig& c, int64_t m, int64_t k, int r, const uint8_t* scales);
 
 struct LinearPlan {
   int path;            // 0 = decode on the block-scaled MFMA, 2 = decode on bf16 MFMA, 1 = GEMM,

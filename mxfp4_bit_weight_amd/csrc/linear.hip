@@ -793,6 +793,13 @@ hipError_t launch_linear_aqn(int fmt, const void* x, int64_t m, int64_t k, const
     if (e != hipSuccess) return e;
     return hipGetLastError();
   }
+  if (plan.path == 3 && k > 0 && decode_xs_fuses_aqn(fmt, plan.xs, m, k, has_lora ? r : 0, scales)) {
+    uint32_t* cnt_m = reinterpret_cast<uint32_t*>(ws + plan.off_count);
+    return launch_decode_xs(fmt, plan.xs, x, m, k, codes, scales, tensor_scale, n, has_lora ? lora_a : nullptr,
+                            has_lora ? lora_b : nullptr, r, cnt_m + kLsyncBase, y,
+                            reinterpret_cast<float*>(ws + plan.off_part), cnt_m + kLoraSlots, stream, gamma, noise,
+                            sigma, eps);
+  }
   // two launches: the norm into the workspace, then the linear on it
   void* xn = ws + align256(plan.bytes);
   if (k > 0) {

@@ -92,8 +92,8 @@ __device__ __forceinline__ u32x4_t xgain_bf16(u32x4_t v, u32x4_t gv, u32x4_t n0,
     const float nz1 = __uint_as_float(d < 2 ? n0[2 * d + 1] : n1[2 * d - 3]);
     const float g0 = bf16lo_f32(gv[d]) * __builtin_fmaf(sigma, nz0, 1.0f);
     const float g1 = bf16hi_f32(gv[d]) * __builtin_fmaf(sigma, nz1, 1.0f);
-    if (ss) *ss = __builtin_fmaf(x1, x1, __builtin_fmaf(x0, x0, *ss));
-    o[d] = f32_to_bf16_rne(x0 * g0) | (f32_to_bf16_rne(x1 * g1) << 16);
+    if (ss) *ss = bf16x2_sumsq(v[d], *ss);
+    o[d] = f32x2_to_bf16x2_rne(x0 * g0, x1 * g1);
   }
   return o;
 }

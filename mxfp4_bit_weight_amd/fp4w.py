@@ -381,7 +381,7 @@ def linear_aqn(x: torch.Tensor, gamma: torch.Tensor, noise: torch.Tensor, sigma:
                lora_a: Optional[torch.Tensor] = None, lora_b: Optional[torch.Tensor] = None, eps: float = 1e-6,
                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """fp4w_linear_aqn: the linear of the noisy RMSNorm of x (the norm fused into
-    the decode kernel where it runs over the whole K at m <= 2)."""
+    the decode kernels where each workgroup covers the whole K, m <= 16)."""
     _need(x, torch.bfloat16, "x")
     _need(gamma, torch.bfloat16, "gamma")
     _need(noise, torch.float32, "noise")

@@ -10,10 +10,12 @@ the one rounding of x~ to bf16 (2^-9 of each term), which both routes take (the
 fused kernel rounds x gamma (1 + sigma noise) and applies the row factor to the
 fp32 sums; the two-launch route rounds x~ itself), and the fp32 sum of squares
 behind the row factor (under 2^-12 relative for k <= 2^12 positive terms).
-Cases: the fused route (m <= 2, one K slice: the Qwen-2.5-7B 3584-wide inputs,
-both formats, with and without LoRA, ragged n and k), the two-launch route (a K
-split, the 16-wave shape 3584 x 18944, m = 5 and m = 40), outputs pre-filled with
-NaN, and the fused result against the two-launch result on the same inputs."""
+Cases: the fused routes -- the block-scaled decode kernel (m <= 2, one K slice)
+and the x-in-registers decode kernel (m = 5 .. 16, one K span) -- on the
+Qwen-2.5-7B 3584-wide inputs, both formats, with and without LoRA, ragged n, k
+and rank; the two-launch route (K splits: 3584 x 18944 at m = 1 and m = 8, and
+m = 40 on the GEMM); outputs pre-filled with NaN; and the fused result against
+the two-launch result on the same inputs."""
 import numpy as np
 import pytest
 import torch
@@ -70,8 +72,10 @@ def _run(fp4w, fmt, x, gamma, noise, sigma, eps, codes, scales, st, a, b):
 
 
 FUSED = [(1, 3584, 3584, 0), (1, 3584, 3584, 16), (2, 3584, 3584, 16), (1, 18944, 3584, 16), (2, 18944, 3584, 0),
-         (1, 200, 96, 5), (2, 264, 544, 17), (1, 1032, 4128, 64)]
-SPLIT = [(1, 3584, 18944, 16), (1, 64, 8192, 0), (5, 1032, 1056, 16), (40, 264, 544, 8)]
+         (1, 200, 96, 5), (2, 264, 544, 17), (1, 1032, 4128, 64),
+         (8, 3584, 3584, 16), (8, 18944, 3584, 16), (16, 4608, 3584, 0), (5, 264, 544, 17), (5, 1032, 1056, 16),
+         (12, 200, 4096, 64)]
+SPLIT = [(1, 3584, 18944, 16), (1, 64, 8192, 0), (8, 3584, 18944, 16), (40, 264, 544, 8)]
 
 
 @pytest.mark.parametrize("m,n,k,r", FUSED + SPLIT)
@@ -86,11 +90,12 @@ def test_linear_aqn(fp4w, fmt, m, n, k, r):
         _check(fmt, got, x, gamma, noise, sigma, 1e-6, codes, scales, st, a, b, f"{what} sigma={sigma}")
 
 
+@pytest.mark.parametrize("m", [1, 8])
 @pytest.mark.parametrize("fmt", [0, 1])
-def test_fused_against_two_launches(fp4w, fmt):
+def test_fused_against_two_launches(fp4w, fmt, m):
     """The fused kernel and the norm-then-linear pair agree to the two roundings
     of x~ they take at different points (2^-8 of sum |x~ w| between them)."""
-    m, n, k, r = 1, 18944, 3584, 16
+    n, k, r = 18944, 3584, 16
     x, gamma, noise, codes, scales, st, a, b = _case(3, fmt, m, n, k, r)
     sigma, eps = 1e-2, 1e-6
     got, q = _run(fp4w, fmt, x, gamma, noise, sigma, eps, codes, scales, st, a, b)
@@ -100,7 +105,7 @@ def test_fused_against_two_launches(fp4w, fmt):
     two = f64_of_bf16(bits_host(two))
     xt = O.aqn_rmsnorm(x, gamma, noise, sigma, eps)
     weff = O.dequantize(fmt, codes, scales, st, "f64") + f64_of_bf16(b) @ f64_of_bf16(a)
-    lim = 2 * 2e-3 * np.linalg.norm(xt) * np.linalg.norm(weff, axis=1)[None, :] \
+    lim = 2 * 2e-3 * np.linalg.norm(xt, axis=1)[:, None] * np.linalg.norm(weff, axis=1)[None, :] \
         + 2.0 ** -7 * (np.abs(xt) @ np.abs(weff).T)
     assert (np.abs(got - two) <= lim).all()
     # repeated calls give the same bits (sums in a fixed order)

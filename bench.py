@@ -673,7 +673,7 @@ def gemm_rows(torch, fp4w, W, dev, bf16, time_loop, rank, weights, prefill_only=
 
 def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_graph, rank):
     rows = {}
-    reps = max(20, args.steps // 4)
+    reps = max(100, args.steps)          # graph launches per row (fewer would carry the graph's start per call)
     ws_bytes = max(fp4w.linear_workspace_bytes(m, n, k, rank) for (n, k) in W.QWEN7B_SHAPES.values() for m in (1, 8))
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     # decode linears, every shape, M = 1 and 8, both formats

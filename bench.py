@@ -686,7 +686,7 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
             def f(i, d=d, x=x, y=y):
                 q, a, b = d["qs"][i % len(d["qs"])]
                 fp4w.linear(x, q, a, b, out=y, workspace=ws)
-            ms, _ = time_graph(f, reps, 5)
+            ms, _ = time_graph(f, reps, reps)    # as many warm launches: the clock drops while graphs are captured
             nb = linear_bytes(fmt, m, d["n"], d["k"], rank)
             gbs = nb / (ms * 1e-3) / 1e9
             dec[f"{'nvfp4' if fmt == 0 else 'mxfp4'}/{name}/M{m}"] = {
@@ -701,25 +701,34 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
     gam = bf16(W.normal_bf16(301, W.TID_X, (d["k"],), 1.0))
     noise = torch.from_numpy(np.random.default_rng(302).standard_normal(d["k"]).astype(np.float32)).to(dev)
     xn = torch.empty_like(d["x1"])
-    yn = torch.empty((1, d["n"]), dtype=torch.bfloat16, device=dev)
     sig = fp4w.aqn_sigma(100, 1000)
-    ams, _ = time_graph(lambda i: fp4w.aqn_rmsnorm(d["x1"], gam, noise, sig, 1e-6, out=xn), reps, 5)
+    ams, _ = time_graph(lambda i: fp4w.aqn_rmsnorm(d["x1"], gam, noise, sig, 1e-6, out=xn), reps, reps)
+    aqn = {}
+    for m in (1, 8):
+        xm = d["x1"] if m == 1 else d["x8"]
+        xnm = torch.empty_like(xm)
+        ym = torch.empty((m, d["n"]), dtype=torch.bfloat16, device=dev)
 
-    def norm_linear(i):
-        q, a, b = d["qs"][i % len(d["qs"])]
-        fp4w.aqn_rmsnorm(d["x1"], gam, noise, sig, 1e-6, out=xn)
-        fp4w.linear(xn, q, a, b, out=yn, workspace=ws)
-    nms, _ = time_graph(norm_linear, reps, 5)
-    aws = torch.zeros(fp4w.linear_aqn_workspace_bytes(1, d["n"], d["k"], rank), dtype=torch.uint8, device=dev)
+        def norm_linear(i, xm=xm, xnm=xnm, ym=ym):
+            q, a, b = d["qs"][i % len(d["qs"])]
+            fp4w.aqn_rmsnorm(xm, gam, noise, sig, 1e-6, out=xnm)
+            fp4w.linear(xnm, q, a, b, out=ym, workspace=ws)
+        nms, _ = time_graph(norm_linear, reps, reps)
+        aws = torch.zeros(fp4w.linear_aqn_workspace_bytes(m, d["n"], d["k"], rank), dtype=torch.uint8, device=dev)
 
-    def fused(i):
-        q, a, b = d["qs"][i % len(d["qs"])]
-        fp4w.linear_aqn(d["x1"], gam, noise, sig, q, a, b, eps=1e-6, out=yn, workspace=aws)
-    fms, _ = time_graph(fused, reps, 5)
+        def fused(i, xm=xm, ym=ym, aws=aws):
+            q, a, b = d["qs"][i % len(d["qs"])]
+            fp4w.linear_aqn(xm, gam, noise, sig, q, a, b, eps=1e-6, out=ym, workspace=aws)
+        fms, _ = time_graph(fused, reps, reps)
+        aqn[m] = (nms, fms)
+    nms, fms = aqn[1]
     rows["aqn_rmsnorm_m1_k3584"] = {"us": round(ams * 1e3, 2),
                                     "us_with_gate_up_linear_nvfp4": round(nms * 1e3, 2),
                                     "us_fused_into_gate_up_linear_nvfp4": round(fms * 1e3, 2),
-                                    "linear_alone_us": dec["nvfp4/gate_up/M1"]["us"]}
+                                    "linear_alone_us": dec["nvfp4/gate_up/M1"]["us"],
+                                    "m8": {"us_with_gate_up_linear_nvfp4": round(aqn[8][0] * 1e3, 2),
+                                           "us_fused_into_gate_up_linear_nvfp4": round(aqn[8][1] * 1e3, 2),
+                                           "linear_alone_us": dec["nvfp4/gate_up/M8"]["us"]}}
     log(f"[bench] noisy RMSNorm {ams * 1e3:.2f} us, then the gate/up linear {nms * 1e3:.2f} us, "
         f"fused {fms * 1e3:.2f} us")
 

@@ -455,7 +455,7 @@ void decode_f8f4_kernel(
   if (LORA) {
     // ---- 4b. the first wave done with its part fetches the chunk words of t
     //      (bounded wait) and adds them in chunk order while the others stream;
-    //      then it arrives ------------------------------------------------------
+    //      then it arrives (its round trips overlap the others' streaming) ------
     int first = 0;
     if (lane == 0) first = atomicAdd(&lfin, 1) == 0;
     first = __shfl(first, 0, 64);
@@ -463,7 +463,8 @@ void decode_f8f4_kernel(
       float* lt = reinterpret_cast<float*>(lds + L.lt_off);
       const int ok = lora_poll(lsync, lparts, mr, lt, wait_ticks, lane);
       if (lane == 0) have_t = ok;
-      lsync_reader_arrive(lsync, bid, nread, lparts, words, lane);
+      const uint32_t old = lsync_reader_issue(lsync, bid, lane);
+      lsync_reader_complete(lsync, old, bid, nread, lparts, words, lane);
     }
   }
 

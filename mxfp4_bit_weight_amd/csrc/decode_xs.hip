@@ -445,6 +445,7 @@ __device__ __forceinline__ void xs_body(
 
   // ---- 6. LoRA B rows and t to LDS ---------------------------------------------------------
   float* lt = reinterpret_cast<float*>(lds + L.lt_off);
+  uint32_t arr_old = 0;                          // wave 0 of span 0: the arrival's group count
   if (rr > 0) {
     if (lb16) {
       u32x4_t* lb = reinterpret_cast<u32x4_t*>(lds + L.lb_off);
@@ -467,6 +468,7 @@ __device__ __forceinline__ void xs_body(
     if (wave == 0) {
       const int ok = s == 0 ? lora_poll(lsync, lparts, M * rr, lt, wait_ticks, lane) : 1;
       if (lane == 0) *have_t = ok;
+      if (s == 0) arr_old = lsync_reader_issue(lsync, rd, lane);    // the words are read: arrive
     }
   }
   __syncthreads();
@@ -517,8 +519,8 @@ __device__ __forceinline__ void xs_body(
       if (row < N) y[(int64_t)m * N + row] = (uint16_t)f32_to_bf16_rne(v);
     }
   }
-  // the chunk words have been read (span 0): arrive
-  if (LORA && s == 0 && wave == 0) lsync_reader_arrive(lsync, rd, nread, lparts, lparts * M * rr, lane);
+  // the arrival issued after the poll, completed before the workgroup can exit
+  if (LORA && s == 0 && wave == 0) lsync_reader_complete(lsync, arr_old, rd, nread, lparts, lparts * M * rr, lane);
   if (S > 1) {
     if (!arrive_last(&cnt[gi], (uint32_t)S, flag)) return;
     for (int e = tid; e < nout; e += nt) {

@@ -57,17 +57,22 @@ __device__ __forceinline__ uint32_t lsync_top_expected(int nread, int lparts) {
   return (uint32_t)((nread < kLsyncSubs ? nread : kLsyncSubs) + lparts);
 }
 
-// One wave of reader workgroup `rd` of `nread`, after its loads of the chunk
-// words have returned.
-__device__ __forceinline__ void lsync_reader_arrive(uint32_t* ls, int rd, int nread, int lparts, int words,
-                                                    int lane) {
+// The arrival of reader workgroup `rd` of `nread`, in two parts so that the
+// returning atomic's round trip overlaps the reader's remaining work.  Issue: one
+// wave, once its loads of the chunk words have returned; returns the group
+// count before it (in lane 0).  Complete: the same wave, later but before the
+// workgroup can exit; the arrival that completes its group clears the group's
+// counter and arrives on top.
+__device__ __forceinline__ uint32_t lsync_reader_issue(uint32_t* ls, int rd, int lane) {
+  uint32_t old = 0;
+  if (lane == 0) old = lsync_add(&ls[kLsyncSub + 32 * (rd % kLsyncSubs)]);
+  return old;
+}
+__device__ __forceinline__ void lsync_reader_complete(uint32_t* ls, uint32_t old, int rd, int nread, int lparts,
+                                                      int words, int lane) {
   const int c = rd % kLsyncSubs;
   const uint32_t quota = (uint32_t)(nread / kLsyncSubs + (c < nread % kLsyncSubs ? 1 : 0));
-  uint32_t old = 0;
-  if (lane == 0) {
-    old = lsync_add(&ls[kLsyncSub + 32 * c]);
-    if (old == quota - 1u) lsync_store(&ls[kLsyncSub + 32 * c], 0u);
-  }
+  if (lane == 0 && old == quota - 1u) lsync_store(&ls[kLsyncSub + 32 * c], 0u);
   old = (uint32_t)__shfl((int)old, 0, 64);
   if (old == quota - 1u) lsync_top_arrive(ls, lsync_top_expected(nread, lparts), words, lane);
 }

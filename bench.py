@@ -158,9 +158,10 @@ def main():
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
 
-    def time_graph(fn, steps, warmup):
+    def time_graph(fn, steps, warmup, replays=1):
         """Capture `warmup` and `steps` calls of fn into two HIP graphs and time the
-        replay of the second (launch overhead off the critical path)."""
+        replay of the second (launch overhead off the critical path); with
+        replays > 1 the second is replayed that many times and the median kept."""
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -176,14 +177,19 @@ def main():
                 fn(warmup + i)
         gw.replay()
         sync()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
         t0 = time.perf_counter()
-        e0.record()
-        gt.replay()
-        e1.record()
-        sync()
+        for _ in range(replays):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gt.replay()
+            e1.record()
+            sync()
+            times.append(e0.elapsed_time(e1) / steps)
         wall = time.perf_counter() - t0
-        return e0.elapsed_time(e1) / steps, wall
+        if replays > 1:
+            log(f"[bench]   replays (ms per call): {', '.join(f'{t:.5f}' for t in times)}")
+        return sorted(times)[len(times) // 2], wall
 
     if args.only == "gemm":
         rank = W.LORA_RANK
@@ -686,7 +692,7 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
             def f(i, d=d, x=x, y=y):
                 q, a, b = d["qs"][i % len(d["qs"])]
                 fp4w.linear(x, q, a, b, out=y, workspace=ws)
-            ms, _ = time_graph(f, reps, reps)    # as many warm launches: the clock drops while graphs are captured
+            ms, _ = time_graph(f, reps, reps, replays=3)   # the median of three replays
             nb = linear_bytes(fmt, m, d["n"], d["k"], rank)
             gbs = nb / (ms * 1e-3) / 1e9
             dec[f"{'nvfp4' if fmt == 0 else 'mxfp4'}/{name}/M{m}"] = {

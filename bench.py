@@ -488,6 +488,16 @@ def summarize_profile(args):
                 f"{100 * med['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * med['SQ_BUSY_CU_CYCLES']):.1f}%")
             add(f"CU busy cycles per CU (SQ_BUSY_CU_CYCLES / 256) over the kernel time: "
                 f"{med['SQ_BUSY_CU_CYCLES'] / 256 / (call_us * 1e3):.3f} GHz")
+        if "SQ_WAIT_INST_ANY" in med and "SQ_WAVE_CYCLES" in med and med["SQ_WAVE_CYCLES"] > 0:
+            # both in the same (quad-cycle) unit, summed over waves
+            add(f"waves' cycles waiting on an instruction's operands (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES): "
+                f"{100 * med['SQ_WAIT_INST_ANY'] / med['SQ_WAVE_CYCLES']:.1f}%")
+        if "SQ_ACTIVE_INST_VALU" in med and "SQ_WAVE_CYCLES" in med and med["SQ_WAVE_CYCLES"] > 0:
+            add(f"waves' cycles issuing VALU (SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES): "
+                f"{100 * med['SQ_ACTIVE_INST_VALU'] / med['SQ_WAVE_CYCLES']:.1f}%")
+        if "SQ_WAVE_CYCLES" in med and "SQ_WAVES" in med and med["SQ_WAVES"] > 0:
+            add(f"mean wave lifetime (4 x SQ_WAVE_CYCLES / SQ_WAVES, shader cycles): "
+                f"{4 * med['SQ_WAVE_CYCLES'] / med['SQ_WAVES']:.0f}")
         if "SQ_LDS_BANK_CONFLICT" in med and "SQ_LDS_IDX_ACTIVE" in med and med["SQ_LDS_IDX_ACTIVE"] > 0:
             add(f"LDS bank conflict cycles / LDS active cycles: "
                 f"{med['SQ_LDS_BANK_CONFLICT'] / med['SQ_LDS_IDX_ACTIVE']:.4f}")

@@ -75,7 +75,8 @@ FUSED = [(1, 3584, 3584, 0), (1, 3584, 3584, 16), (2, 3584, 3584, 16), (1, 18944
          (1, 200, 96, 5), (2, 264, 544, 17), (1, 1032, 4128, 64),
          (8, 3584, 3584, 16), (8, 18944, 3584, 16), (16, 4608, 3584, 0), (5, 264, 544, 17), (5, 1032, 1056, 16),
          (12, 200, 4096, 64),
-         (16, 18944, 3584, 64)]     # the gain's LDS leaves no room for staged scales: per-lane scale loads
+         (16, 18944, 3584, 64),     # the gain's LDS leaves no room for staged scales: per-lane scale loads
+         (6, 72, 64, 3), (9, 40, 32, 0)]
 SPLIT = [(1, 3584, 18944, 16), (1, 64, 8192, 0), (8, 3584, 18944, 16), (40, 264, 544, 8)]
 
 

@@ -347,10 +347,10 @@ __global__ __launch_bounds__(256) void nvfp4_encode_kernel(const uint4* __restri
 // a block holding inf/NaN (E = 255) gets the NaN scale 0xFF.  The codes come from
 // the scaled conversion, which divides by the power of two exactly and rounds to
 // nearest even with saturation.
-template <bool FROZEN, bool FQ = false>
+template <bool FROZEN>
 __global__ __launch_bounds__(256) void mxfp4_encode_kernel(const uint4* __restrict__ w, int64_t nblocks,
                                                            uint8_t* __restrict__ scales,
-                                                           uint4* __restrict__ codes, uint4* __restrict__ fq = nullptr) {
+                                                           uint4* __restrict__ codes) {
   for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += (int64_t)gridDim.x * 256) {
     uint32_t wd[16];
 #pragma unroll
@@ -383,31 +383,77 @@ __global__ __launch_bounds__(256) void mxfp4_encode_kernel(const uint4* __restri
       c[q] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c[q], as_bf16x2(wd[4 * q + 2]), s, 2);
       c[q] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c[q], as_bf16x2(wd[4 * q + 3]), s, 3);
     }
-    if (!FQ) {
-      codes[b] = make_uint4(c[0], c[1], c[2], c[3]);
-    } else {
-      // the 32 values decoded from the codes as dequantize does (codec.hpp)
-      uint32_t o[16];
-      if (sc < 0xFDu) {
+    codes[b] = make_uint4(c[0], c[1], c[2], c[3]);
+  }
+}
+
+// MXFP4 fake-quant, whose bf16 output is as wide as its input: a wave takes 64
+// blocks (4 KB of w) a round; load q of lane l is the 16 bytes at 1024 q + 16 l,
+// quarter l % 4 of block 16 q + l / 4 (8 elements, one code dword), and its
+// output goes to the same 16 bytes of the output, so every load and store of
+// the wave moves one contiguous piece (one block per thread wrote 64 bytes a
+// lane, each store instruction touching 64 separate half-lines).  The four
+// lanes of a block reduce its maximum together.
+template <bool FROZEN>
+__global__ __launch_bounds__(256) void mxfp4_fake_quant_kernel(const uint4* __restrict__ w, int64_t nblocks,
+                                                               uint8_t* __restrict__ scales,
+                                                               uint4* __restrict__ fq) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 3;
+  for (int64_t b0 = ((int64_t)blockIdx.x * 4 + wave) * 64; b0 < nblocks; b0 += (int64_t)gridDim.x * 256) {
+    uint4 v[4];
+    uint32_t scq[4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          o[4 * j + 0] = fp4x2_to_bf16x2_scaled<0>(c[j], s);
-          o[4 * j + 1] = fp4x2_to_bf16x2_scaled<1>(c[j], s);
-          o[4 * j + 2] = fp4x2_to_bf16x2_scaled<2>(c[j], s);
-          o[4 * j + 3] = fp4x2_to_bf16x2_scaled<3>(c[j], s);
-        }
+    for (int q = 0; q < 4; q++) {
+      const int64_t bq = b0 + 16 * q + (lane >> 2);
+      const bool ok = bq < nblocks;
+      v[q] = ok ? w[4 * bq + j] : make_uint4(0u, 0u, 0u, 0u);
+      if (FROZEN) scq[q] = ok ? scales[bq] : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int64_t bq = b0 + 16 * q + (lane >> 2);
+      const uint32_t wd[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+      uint32_t sc;
+      if (FROZEN) {
+        sc = scq[q];
       } else {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          float v[8];
-          mx_plain8(c[j], sc, v);
-#pragma unroll
-          for (int e = 0; e < 4; e++)
-            o[4 * j + e] = f32_to_bf16_rne(v[2 * e]) | (f32_to_bf16_rne(v[2 * e + 1]) << 16);
-        }
+        const u16x2_t m2 = __builtin_elementwise_max(
+            __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, wd[0] & 0x7FFF7FFFu),
+                                      __builtin_bit_cast(u16x2_t, wd[1] & 0x7FFF7FFFu)),
+            __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, wd[2] & 0x7FFF7FFFu),
+                                      __builtin_bit_cast(u16x2_t, wd[3] & 0x7FFF7FFFu)));
+        uint32_t m = m2.x > m2.y ? (uint32_t)m2.x : (uint32_t)m2.y;
+        uint32_t o = (uint32_t)__shfl_xor((int)m, 1, 64);
+        m = o > m ? o : m;
+        o = (uint32_t)__shfl_xor((int)m, 2, 64);
+        m = o > m ? o : m;
+        const uint32_t E = (m >> 7) & 0xFFu;
+        sc = (E == 0xFFu) ? 0xFFu : (E > 2u ? E - 2u : 0u);
       }
+      const float s = e8m0_scale_operand(sc);
+      uint32_t c = 0u;
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, as_bf16x2(wd[0]), s, 0);
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, as_bf16x2(wd[1]), s, 1);
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, as_bf16x2(wd[2]), s, 2);
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, as_bf16x2(wd[3]), s, 3);
+      if (bq >= nblocks) continue;
+      if (!FROZEN && j == 0) scales[bq] = (uint8_t)sc;
+      {
+        // the 8 values decoded from the codes as dequantize does (codec.hpp)
+        uint32_t o[4];
+        if (sc < 0xFDu) {
+          o[0] = fp4x2_to_bf16x2_scaled<0>(c, s);
+          o[1] = fp4x2_to_bf16x2_scaled<1>(c, s);
+          o[2] = fp4x2_to_bf16x2_scaled<2>(c, s);
+          o[3] = fp4x2_to_bf16x2_scaled<3>(c, s);
+        } else {
+          float vv[8];
+          mx_plain8(c, sc, vv);
 #pragma unroll
-      for (int q = 0; q < 4; q++) fq[4 * b + q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+          for (int e = 0; e < 4; e++) o[e] = f32_to_bf16_rne(vv[2 * e]) | (f32_to_bf16_rne(vv[2 * e + 1]) << 16);
+        }
+        fq[4 * bq + j] = make_uint4(o[0], o[1], o[2], o[3]);
+      }
     }
   }
 }
@@ -505,11 +551,11 @@ hipError_t launch_fake_quant(int fmt, const void* w, int64_t n, int64_t k, void*
   } else {
     const int64_t nblocks = count / 32;
     if (!frozen)
-      hipLaunchKernelGGL((mxfp4_encode_kernel<false, true>), dim3(grid_for(nblocks, 256, 16384)), dim3(256), 0,
-                         stream, wv, nblocks, scales, nullptr, fq);
+      hipLaunchKernelGGL(mxfp4_fake_quant_kernel<false>, dim3(grid_for(nblocks, 256, 16384)), dim3(256), 0, stream,
+                         wv, nblocks, scales, fq);
     else
-      hipLaunchKernelGGL((mxfp4_encode_kernel<true, true>), dim3(grid_for(nblocks, 256, 16384)), dim3(256), 0,
-                         stream, wv, nblocks, scales, nullptr, fq);
+      hipLaunchKernelGGL(mxfp4_fake_quant_kernel<true>, dim3(grid_for(nblocks, 256, 16384)), dim3(256), 0, stream,
+                         wv, nblocks, scales, fq);
   }
   return hipGetLastError();
 }

@@ -171,6 +171,8 @@ size_t fp4w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
  *    On both decode paths a non-finite x element makes every output of its row
  *    NaN, and a NaN block scale every output of its weight row.
  *  - m > 16: the LoRA down-projection, then the LDS-staged bf16 MFMA GEMM.
+ *  - k == 0: y = 0 (every output is an empty sum; one fill launch, no operand
+ *    is read).
  * The LoRA product is added in fp32 (GEMM: t split into two bf16 parts for the
  * matrix cores).
  */

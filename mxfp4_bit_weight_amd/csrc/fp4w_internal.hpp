@@ -92,7 +92,7 @@ bool decode_xs_fuses_aqn(int fmt, const XsConfig& c, int64_t m, int64_t k, int r
 
 struct LinearPlan {
   int path;            // 0 = decode on the block-scaled MFMA, 2 = decode on bf16 MFMA, 1 = GEMM,
-                       // 3 = decode with x in registers
+                       // 3 = decode with x in registers, 4 = k == 0 (y is the empty sum: zeros)
   DecodeConfig dq;     // path 0
   XsConfig xs;         // path 3
   int splits;          // K splits of the decode kernel (1 = none)

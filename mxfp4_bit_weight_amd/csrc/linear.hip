@@ -610,6 +610,13 @@ static bool decode_prefers_f8f4(int64_t m, int64_t n, int64_t k) {
 
 LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
   LinearPlan p{};
+  if (k == 0) {                                  // no products: y = 0, the counter area only
+    p.path = 4;
+    p.splits = 1;
+    p.bytes = sizeof(uint32_t) * kCounterSlots;
+    p.off_t = p.off_part = p.bytes;
+    return p;
+  }
   if (m > 16) p.path = 1;
   else if (m >= 2 && decode_xs_supports(m, n, k, r) && !decode_prefers_f8f4(m, n, k)) p.path = 3;
   else p.path = decode_f8f4_supports(FMT_NVFP4, m) ? 0 : 2;
@@ -651,6 +658,11 @@ LinearPlan plan_linear(int64_t m, int64_t n, int64_t k, int r) {
   if (p.splits > 1) off += align256(sizeof(float) * part_floats);
   p.bytes = off;
   return p;
+}
+
+// y = 0 for k == 0 (every output is an empty sum).
+__global__ __launch_bounds__(256) void zero_bf16_kernel(uint16_t* __restrict__ y, int64_t elems) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < elems; i += (int64_t)gridDim.x * 256) y[i] = 0;
 }
 
 // Waves per workgroup of the decode kernel: 1 while the staged x slice is small
@@ -704,6 +716,13 @@ hipError_t launch_linear(int fmt, const void* x, int64_t m, int64_t k, const uin
                          const void* lora_b, int r, void* y, void* workspace, const LinearPlan& plan,
                          hipStream_t stream) {
   if (m == 0 || n == 0) return hipSuccess;
+  if (plan.path == 4) {
+    const int64_t elems = m * n;
+    const int64_t blocks = (elems + 255) / 256;
+    hipLaunchKernelGGL(zero_bf16_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream,
+                       reinterpret_cast<uint16_t*>(y), elems);
+    return hipGetLastError();
+  }
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   const bool has_lora = r > 0 && lora_a && lora_b;
   float* t = has_lora ? reinterpret_cast<float*>(ws + plan.off_t) : nullptr;

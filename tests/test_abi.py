@@ -52,6 +52,15 @@ def test_workspace_bytes(lib):
     assert lib.linear_workspace_bytes(-1, 10, 64, 0) == 0
 
 
+def test_workspace_bytes_for_empty_k(lib):
+    # k == 0 has no products (y is zeros): every m plans the counter area alone,
+    # also where the decode planners would split an empty K
+    for m in (1, 2, 4, 8, 16, 17, 4096):
+        for r in (0, 16):
+            assert lib.linear_workspace_bytes(m, 64, 0, r) == lib.WORKSPACE_COUNTER_BYTES, (m, r)
+            assert lib.linear_aqn_workspace_bytes(m, 64, 0, r) >= lib.WORKSPACE_COUNTER_BYTES, (m, r)
+
+
 def test_workspace_covers_the_counter_area(lib):
     # arrival counters and the LoRA hand-over words sit in the first 28800 bytes
     assert lib.WORKSPACE_COUNTER_BYTES == 28800

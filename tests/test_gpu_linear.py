@@ -176,6 +176,29 @@ def test_workspace_reuse_across_shapes(fp4w):
         assert int(ws[:fp4w.WORKSPACE_COUNTER_BYTES].view(torch.int32).abs().sum().item()) == 0
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_empty_k_writes_zeros(fp4w, fmt):
+    """k == 0: every output is an empty sum, so y = 0 whatever the path m picks
+    (the operands are never read; non-null stand-ins satisfy the argument checks)."""
+    n = 40
+    stand = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+    p = fp4w._ptr(stand)
+    ts = torch.ones(1, dtype=torch.float32, device=DEV)
+    for m in (1, 2, 8, 16, 17):
+        for r in (0, 16):
+            say(f"empty k: fmt={fmt} m={m} r={r}")
+            g = Guarded((m, n), torch.bfloat16, float("nan"))
+            nb = fp4w.linear_workspace_bytes(m, n, 0, r)
+            ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+            rc = fp4w._linear(fmt, p, m, 0, p, p, fp4w._ptr(ts) if fmt == 0 else None, n, p if r else None,
+                              p if r else None, r, fp4w._ptr(g.t), fp4w._ptr(ws), nb, fp4w._stream(DEV))
+            assert rc == 0, rc
+            torch.cuda.synchronize()
+            g.check(f"empty k fmt={fmt} m={m} r={r}")
+            assert int((g.t.view(torch.int16) != 0).sum().item()) == 0
+            assert int(ws.to(torch.int32).sum().item()) == 0
+
+
 def test_empty_and_tiny(fp4w):
     w, x, a, b = W.linear_inputs(1, 32, 64, 1, rank=16)
     codes, scales, st = O.quantize(0, w)

@@ -609,10 +609,12 @@ XsConfig plan_decode_xs(int64_t m, int64_t n, int64_t k, int r) {
   const int64_t per_wave = 4 * XS_CPW;
   int64_t S = (nq + per_wave * XS_MAX_WAVES - 1) / (per_wave * XS_MAX_WAVES);
   if (S < 1) S = 1;
-  // spans of a multiple of 16 groups: their scale bytes start 16-byte aligned
+  // spans of a multiple of 16 groups: their scale bytes start 16-byte aligned;
+  // a single span is K itself (no wave left without groups)
   int64_t qspan = (nq + S - 1) / S;
   qspan = (qspan + 15) & ~(int64_t)15;
   S = (nq + qspan - 1) / qspan;
+  if (S == 1) qspan = nq > 0 ? nq : 1;
   c.splits = (int)S;
   c.qspan = (int)qspan;
   c.nw = (int)((qspan + per_wave - 1) / per_wave);

@@ -807,19 +807,24 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
         log(f"[bench] fake-quant fmt={fmt}: {ms_f:.2f} ms, {nbf / (ms_f * 1e-3) / 1e9:.1f} GB/s")
         del fq, fq_s
         if fmt == 0:
-            # scale-only merge of the (18944, 3584) weight, in place; ratio to re-quantizing it
+            # scale-only merge of the (18944, 3584) weight (new scales, codes kept); ratio to re-quantizing it
             o = outs[0]
             s_t = o.scales.reshape(-1).cpu()
             dec_s = s_t.view(torch.float8_e4m3fn).to(torch.float32).numpy()
             z = W.merge_noise(401, o.scales.numel())
             deltas = torch.from_numpy((np.float32(0.05) * dec_s * z).astype(np.float32)).to(dev).reshape(o.scales.shape)
-            merged = torch.empty_like(o.scales)
+            # rotated over copies of more than 1 GiB together, so each call reads HBM
+            nbm = o.scales.numel() * (1 + 4 + 1)
+            mcopies = max(2, -(-(1 << 30) // nbm))
+            msets = [(fp4w.QWeight(0, o.codes, o.scales.clone(), o.tensor_scale, o.n, o.k), deltas.clone(),
+                      torch.empty_like(o.scales)) for _ in range(mcopies)]
 
             def mpass(i):
-                fp4w.merge_scales(o, deltas, scales_out=merged)
-            ms_m, _ = time_loop(mpass, 50, 5)
-            ms_q, _ = time_loop(lambda i: fp4w.quantize(tensors[0], 0, out=outs[0]), 20, 3)
-            nbm = o.scales.numel() * (1 + 4 + 1)
+                qm, dm, om = msets[i % mcopies]
+                fp4w.merge_scales(qm, dm, scales_out=om)
+            ms_m, _ = time_graph(mpass, 200, 20, replays=3)
+            ms_q, _ = time_graph(lambda i: fp4w.quantize(tensors[0], 0, out=outs[0]), 20, 3)
+            del msets
             rows["merge_scales_nvfp4"] = {"blocks": o.scales.numel(), "us": round(ms_m * 1e3, 2),
                                           "GB/s": round(nbm / (ms_m * 1e-3) / 1e9, 1), "algorithmic_bytes": nbm,
                                           "requantize_same_tensor_us": round(ms_q * 1e3, 2),
@@ -860,7 +865,7 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
             fp4w.grouped_linear(x, ri, off, 0, c, s, t, out=yg)
         c, s, t, n, k = e["down"]
         fp4w.grouped_linear(xd, rid, off, 0, c, s, t, out=yd)
-    ms, _ = time_loop(moe_pass, 30, 5)
+    ms, _ = time_graph(moe_pass, 40, 8, replays=3)
     nb = 0
     for tag, (c, s, t, n, k) in experts.items():
         nb += active * (n * k // 2 + n * k // 16 + 4)

@@ -73,15 +73,17 @@ __device__ uint32_t merge_exact(int fmt, uint32_t code, float delta) {
 // (|delta| in [2^-60, 2^60] or 0, dec(S) and the sum normal numbers away from
 // the ends); every grid value and midpoint is a binary32 number, so hi lies on
 // the same side of each midpoint as the exact sum unless hi is the midpoint,
-// where the sign of lo decides (0: ties to the even code).  `slow` marks the
-// blocks outside that range, which merge_exact decides.
+// where the sign of lo decides (0: ties to the even code; E8M0 here, E4M3 on the
+// exact path).  `slow` marks the blocks outside that range, which merge_exact
+// decides.
 template <int FMT>
 __device__ __forceinline__ uint32_t merge_fast(uint32_t code, float delta, bool& slow) {
   const float base = (FMT == FMT_NVFP4) ? e4m3_to_f32(code) : e8m0_to_f32(code);
   const bool nan_in = base != base || delta != delta;
   const float ad = __builtin_fabsf(delta);
   const bool ok_d = ad == 0.0f || (ad >= 0x1p-60f && ad <= 0x1p60f);
-  const bool ok_b = base == 0.0f || (base >= 0x1p-100f && base < 0x1p100f);
+  // an E4M3 base is 0 or within [2^-9, 448] in magnitude: always in range
+  const bool ok_b = FMT == FMT_NVFP4 || base == 0.0f || (base >= 0x1p-100f && base < 0x1p100f);
   const float hi = base + delta;
   const float bb = hi - base;
   const float lo = (base - (hi - bb)) + (delta - bb);
@@ -91,19 +93,17 @@ __device__ __forceinline__ uint32_t merge_fast(uint32_t code, float delta, bool&
   uint32_t c;
   bool in_range;
   if (FMT == FMT_NVFP4) {
-    const float t = hi * 512.0f;                   // subnormal step 2^-9 (exact scaling)
-    const float fl = __builtin_floorf(t);
-    const float f = t - fl;
-    const uint32_t low_s = (uint32_t)fl;
-    const bool up_s = f > 0.5f || (f == 0.5f && (lo_up || (lo_zero && (low_s & 1u))));
-    const uint32_t rest = bh & 0xFFFFFu;
-    const uint32_t low_n = ((((bh >> 23) & 0xFFu) - 120u) << 3) | ((bh >> 20) & 7u);
-    const bool up_n = rest > 0x80000u || (rest == 0x80000u && (lo_up || (lo_zero && (low_n & 1u))));
-    const uint32_t cn = low_n + (up_n ? 1u : 0u);
-    c = hi < 0x1p-6f ? low_s + (up_s ? 1u : 0u) : (cn > 0x7Eu ? 0x7Eu : cn);
+    // hi to the E4M3 grid, nearest with ties to even: v_cvt_pk_fp8_f32 (the same
+    // code as a bit-level rounding for every fp32 in [0, 448)).  That is the code of
+    // the exact sum unless hi sits exactly on a midpoint (subnormal step 2^-9: hi 2^9
+    // has fraction 1/2; normal: the 20 bits below E4M3's 3 are 1000...0) and lo is
+    // not zero; those take the exact path.
+    const uint32_t hw = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(hi, hi, 0, false) & 0xFFu;
     const bool sat = hi >= 448.0f;
-    c = sat ? 0x7Eu : c;
-    in_range = sat || hi >= 0x1p-60f;
+    c = sat ? 0x7Eu : hw;
+    const bool mid = hi < 0x1p-6f ? __builtin_amdgcn_fractf(hi * 512.0f) == 0.5f : (bh & 0xFFFFFu) == 0x80000u;
+    const bool tie = !lo_zero && mid;
+    in_range = sat || (hi >= 0x1p-60f && !tie);
   } else {
     const uint32_t mant = bh & 0x7FFFFFu;          // 1.5 * 2^e is mantissa 0x400000
     const uint32_t low = (bh >> 23) & 0xFFu;       // e + 127

@@ -124,6 +124,30 @@ def test_merge_constructed_ties_nvfp4(fp4w):
     _merge_case(fp4w, 0, scales, d.reshape(-1), "NVFP4 constructed ties")
 
 
+def test_merge_every_e4m3_midpoint(fp4w):
+    """Every midpoint of the E4M3 grid (subnormal and normal), reached from the
+    codes on both sides and from 0 with deltas nudged by 0, +-1 and +-2 units in
+    the last place: the binary32 sum lands on the midpoint with a nonzero
+    remainder (the exact path decides), on it exactly (ties to even), or beside it."""
+    e4 = torch.arange(0x7F, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    c_list, d_list = [], []
+    for j in range(0x7E):
+        target = 0.5 * (e4[j] + e4[j + 1])
+        for c in (j, j + 1, 0):
+            d0 = np.float32(target - e4[c])
+            for nudge in (0, 1, -1, 2, -2):
+                d = d0
+                for _ in range(abs(nudge)):
+                    d = np.nextafter(d, np.float32(np.inf) if nudge > 0 else -np.float32(np.inf))
+                c_list.append(c)
+                d_list.append(d)
+    pad = (-len(c_list)) % 2
+    c_list += [0] * pad
+    d_list += [np.float32(0)] * pad
+    scales = np.array(c_list, dtype=np.uint8).reshape(-1, 2)
+    _merge_case(fp4w, 0, scales, np.array(d_list, dtype=np.float32), "NVFP4 every midpoint")
+
+
 def test_merge_constructed_ties_mxfp4(fp4w):
     rng = np.random.default_rng(7)
     n = 20000

@@ -768,7 +768,7 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
         def qpass(i):
             for t, o in zip(tensors, outs):
                 fp4w.quantize(t, fmt, out=o)
-        ms, _ = time_loop(qpass, 3, 1)
+        ms, _ = time_graph(qpass, 3, 1)
         nb = sum(quant_bytes(fmt, t.numel()) for t in tensors)
         gbs = nb / (ms * 1e-3) / 1e9
         rows[f"quantize_7b_set_{'nvfp4' if fmt == 0 else 'mxfp4'}"] = {
@@ -782,7 +782,7 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
         def dpass(i):
             for j, o in enumerate(outs):
                 fp4w.dequantize(o, out=deq[j % 7])
-        ms_d, _ = time_loop(dpass, 3, 1)
+        ms_d, _ = time_graph(dpass, 3, 1)
         nbd = sum(o.n * o.k * 2 + o.n * o.k // 2 + o.n * o.k // (16 if fmt == 0 else 32) for o in outs)
         rows[f"dequantize_7b_set_{'nvfp4' if fmt == 0 else 'mxfp4'}"] = {
             "ms": round(ms_d, 3), "GB/s": round(nbd / (ms_d * 1e-3) / 1e9, 1), "algorithmic_bytes": nbd}
@@ -799,7 +799,7 @@ def other_rows(args, torch, fp4w, W, decode, dev, bf16, sync, time_loop, time_gr
                 fp4w._check(fp4w._fake_quant(fmt, fp4w._ptr(t), t.shape[0], t.shape[1], fp4w._ptr(y),
                                              fp4w._ptr(fq_s[j % 7]), fp4w._ptr(ts), 0, fp4w._stream(dev)),
                             "fp4w_fake_quant")
-        ms_f, _ = time_loop(fpass, 3, 1)
+        ms_f, _ = time_graph(fpass, 3, 1)
         nbf = sum(t.numel() * 4 + t.numel() // (16 if fmt == 0 else 32) for t in tensors)
         rows[f"fake_quant_7b_set_{'nvfp4' if fmt == 0 else 'mxfp4'}"] = {
             "ms": round(ms_f, 3), "GB/s": round(nbf / (ms_f * 1e-3) / 1e9, 1),

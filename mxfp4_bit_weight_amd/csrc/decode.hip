@@ -553,10 +553,9 @@ DecodeConfig plan_decode_f8f4(int fmt, int64_t m, int64_t n, int64_t k, int r) {
   DecodeConfig c{};
   const int64_t ntiles = (n + DQ_ROWS - 1) / DQ_ROWS;
   const int64_t nsteps = (k + DQ_STEP - 1) / DQ_STEP;
-  // the fewest waves per tile whose parts (of the whole K) fit a ring of 16 loads,
-  // so every code load of the launch is issued up front by as few waves as can
-  // hold them (measured on MI355X at m = 1: 3584 x 3584 takes 4.7 us with 4
-  // waves against 6.3 us with 16; 18944 x 3584 is best with 4, 3584 x 18944 with 16)
+  // the fewest waves per tile whose parts (of the whole K) are at most 16 steps
+  // (measured on MI355X at m = 1: 3584 x 3584 takes 4.7 us with 4 waves against
+  // 6.3 us with 16; 18944 x 3584 is best with 4, 3584 x 18944 with 16)
   c.nw = nsteps <= 4 * 16 ? 4 : nsteps <= 8 * 16 ? 8 : 16;
   // several rows of x (one MFMA chain each per step): more waves when the tiles
   // are few (3584 x 3584 at m = 2: 5.4 us with 8 waves, 6.4 with 4)
@@ -575,7 +574,13 @@ DecodeConfig plan_decode_f8f4(int fmt, int64_t m, int64_t n, int64_t k, int r) {
   c.sps = (int)sps_for(s);
   c.splits = (int)((nsteps + c.sps - 1) / c.sps);
   const int spw = dq_parts(c.sps, c.nw, r > 0).rest;    // the longest part of a wave
-  c.depth = spw <= 8 ? 8 : 16;
+  // Ring of code loads per wave: a part of at most 8 steps is issued whole up
+  // front (at most 4: a ring of 4, so no load past the part is issued); longer
+  // parts go through a ring of 4 refilled as steps are consumed, which spreads a
+  // workgroup's arrivals, and its decode, over the stream (MI355X, m = 1, no
+  // LoRA, 3584 x 18944: 11.7 -> 10.8 us against a ring of 16 issued whole).
+  // launch_decode_f8f4 takes the ring of 4 also with LoRA and for NVFP4 at m >= 2.
+  c.depth = spw <= 4 || spw > 8 ? 4 : 8;
   return c;
 }
 
@@ -602,11 +607,11 @@ static void launch_nq(const DecodeConfig& c, dim3 grid, size_t lds, hipStream_t 
                          nsteps, ntiles, scales16, (uint64_t)0, gam, noise, sigma, eps);                        \
   } while (0)
   if (c.nw == 4) {
-    if (c.depth <= 8) FP4W_DQ(4, 8); else FP4W_DQ(4, 16);
+    if (c.depth <= 4) FP4W_DQ(4, 4); else FP4W_DQ(4, 8);
   } else if (c.nw == 8 || (FMT == FMT_NVFP4 && NQ > 1)) {
-    if (c.depth <= 8) FP4W_DQ(8, 8); else FP4W_DQ(8, 16);
+    if (c.depth <= 4) FP4W_DQ(8, 4); else FP4W_DQ(8, 8);
   } else if constexpr (!AQN && (FMT == FMT_MXFP4 || NQ == 1)) {
-    if (c.depth <= 8) FP4W_DQ(16, 8); else FP4W_DQ(16, 16);
+    if (c.depth <= 4) FP4W_DQ(16, 4); else FP4W_DQ(16, 8);
   }
 #undef FP4W_DQ
 }
@@ -631,6 +636,12 @@ hipError_t launch_decode_f8f4(int fmt, const DecodeConfig& c0, const void* x, in
   const int nsteps = (int)((k + DQ_STEP - 1) / DQ_STEP);
   const int kslice = c.sps * DQ_STEP;
   const int rr = la && lb && k > 0 ? r : 0;        // k = 0: t = x A^T is zero
+  // With LoRA (wave 0's part is cut short so its wait for t overlaps the others'
+  // streaming) and for NVFP4's several MFMA chains per step, the ring of 4 also
+  // wins where the parts fit a ring of 8 (MI355X, m = 1, with LoRA r = 16, NVFP4:
+  // 18944 x 3584 11.45 -> 11.11 us, 3584 x 3584 6.41 -> 6.23 us; m = 2: 18944 x
+  // 3584 15.91 -> 13.31 us; the same outputs bit for bit)
+  if (rr > 0 || (fmt == FMT_NVFP4 && m >= 2)) c.depth = 4;
   const size_t lds = decode_f8f4_lds_bytes(fmt, m, kslice, c.nw, rr);
   if (lds > 64 * 1024 || rr > DQ_MAX_R || m * rr > 1024) return hipErrorInvalidValue;
   // chunk workgroups of the LoRA down-projection go first in the grid

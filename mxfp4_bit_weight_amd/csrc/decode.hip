@@ -558,9 +558,10 @@ DecodeConfig plan_decode_f8f4(int fmt, int64_t m, int64_t n, int64_t k, int r) {
   // 6.3 us with 16; 18944 x 3584 is best with 4, 3584 x 18944 with 16)
   c.nw = nsteps <= 4 * 16 ? 4 : nsteps <= 8 * 16 ? 8 : 16;
   // more waves when the tiles are few (3584 x 3584 at m = 2: 5.4 us with 8
-  // waves, 6.4 with 4; at m = 1 with LoRA r = 16 6.26 -> 6.02 us, without
-  // 4.56 -> 4.43 us; 18944 x 3584 at m = 1 is 2.2 us slower with 8)
-  if (c.nw == 4 && ntiles * 4 < 1536) c.nw = 8;
+  // waves, 6.4 with 4; at m = 1 without LoRA 4.56 -> 4.47 us).  Not at m = 1 with
+  // LoRA: 8-wave chunk workgroups take twice the K each, and with A read cold
+  // (its own A per weight, as in a model) t comes later: 6.28 -> 6.92 us.
+  if (c.nw == 4 && ntiles * 4 < 1536 && (m >= 2 || r == 0)) c.nw = 8;
   if (m >= 2 && c.nw > 8) c.nw = 8;     // several MFMA chains per wave: 1024-thread groups would spill
   auto sps_for = [&](int64_t s) {
     int64_t sps = (nsteps + s - 1) / s;

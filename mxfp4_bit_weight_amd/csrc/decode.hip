@@ -382,7 +382,14 @@ void decode_f8f4_kernel(
           s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4, 1.0f, false);   // E4M3 -> fp32, exact
           s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4, 1.0f, true);
         }
-        if constexpr (decltype(refill)::value) ring[u] = buffer_load16(crs, code_off(j0 + jb + u + DEPTH));
+        if constexpr (decltype(refill)::value) {
+          // 16-wave single-chain groups with LoRA skip the loads past their part
+          // (a uniform branch: its wait counts turn conservative, which costs the
+          // 4- and 8-wave groups more than the loads; 3584 x 18944, m = 1, LoRA
+          // r = 16: 12.51 -> 11.63 us NVFP4, 12.13 -> 11.26 us MXFP4)
+          if (!(NQ == 1 && NW == 16 && LORA) || jb + u + DEPTH < j1 - j0)
+            ring[u] = buffer_load16(crs, code_off(j0 + jb + u + DEPTH));
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -438,7 +445,14 @@ void decode_f8f4_kernel(
             acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[q], 0, 4, 0, sa, 0, sbw);
           }
         }
-        if constexpr (decltype(refill)::value) ring[u] = buffer_load16(crs, code_off(j0 + jb + u + DEPTH));
+        if constexpr (decltype(refill)::value) {
+          // 16-wave single-chain groups with LoRA skip the loads past their part
+          // (a uniform branch: its wait counts turn conservative, which costs the
+          // 4- and 8-wave groups more than the loads; 3584 x 18944, m = 1, LoRA
+          // r = 16: 12.51 -> 11.63 us NVFP4, 12.13 -> 11.26 us MXFP4)
+          if (!(NQ == 1 && NW == 16 && LORA) || jb + u + DEPTH < j1 - j0)
+            ring[u] = buffer_load16(crs, code_off(j0 + jb + u + DEPTH));
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -32,15 +32,15 @@ def _run_dev(fp4w, fmt, w, x, a, b, nan_out=False):
     return y, codes, scales, st
 
 
-def _run(fp4w, fmt, w, x, a, b):
-    y, codes, scales, st = _run_dev(fp4w, fmt, w, x, a, b)
+def _run(fp4w, fmt, w, x, a, b, nan_out=False):
+    y, codes, scales, st = _run_dev(fp4w, fmt, w, x, a, b, nan_out=nan_out)
     return f64_of_bf16(bits_host(y)), codes, scales, st
 
 
-def _full_case(fp4w, fmt, m, n, k, r, seed=0, wkind="normal"):
+def _full_case(fp4w, fmt, m, n, k, r, seed=0, wkind="normal", nan_out=False):
     say(f"[linear] fmt={fmt} m={m} n={n} k={k} r={r} seed={seed}")
     w, x, a, b = W.linear_inputs(seed, n, k, m, rank=r, wkind=wkind)
-    yg, codes, scales, st = _run(fp4w, fmt, w, x, a, b)
+    yg, codes, scales, st = _run(fp4w, fmt, w, x, a, b, nan_out=nan_out)
     y64 = O.linear(fmt, x, codes, scales, st, a, b)
     xn = np.sqrt((f64_of_bf16(x) ** 2).sum(axis=1))[:, None]
     wn = weff_norms(fmt, codes, scales, st, a, b)[None, :]
@@ -62,6 +62,20 @@ SKINNY = [(1, 200, 544, 16), (2, 45, 96, 5), (3, 1000, 1056, 64), (4, 17, 32, 0)
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_skinny_ragged(fp4w, fmt, m, n, k, r):
     _full_case(fp4w, fmt, m, n, k, r, seed=m * 7 + r, wkind="outlier")
+
+
+# The 2-16-row kernel gives each workgroup a run of 1 to 6 weight tiles of 16
+# rows, about one workgroup per compute unit (256 on MI355X, fewer the LoRA's
+# chunk workgroups): n of 5000, 9000, 13000 and 22000 rows take runs of 2, 3, 4
+# and 6 tiles, with and without LoRA, a ragged last tile each.  Outputs are
+# NaN-filled first, so an output no run writes fails the bound.
+TILE_RUNS = [(8, 5000, 512, 0), (8, 9000, 512, 16), (8, 13000, 512, 16), (16, 22000, 512, 0), (3, 22000, 256, 16)]
+
+
+@pytest.mark.parametrize("m,n,k,r", TILE_RUNS)
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_skinny_tile_runs(fp4w, fmt, m, n, k, r):
+    _full_case(fp4w, fmt, m, n, k, r, seed=n + r, wkind="outlier", nan_out=True)
 
 
 GEMM = [(17, 300, 256, 16), (100, 520, 1056, 16), (300, 257, 544, 0), (64, 64, 64, 5), (513, 700, 2048, 64)]

@@ -71,6 +71,21 @@ def test_uneven_routing(fp4w, fmt):
     _case(fp4w, fmt, x, row_index, offsets, codes, scales, ts, "uneven routing")
 
 
+# Each expert's rows go through runs of up to 6 weight tiles of 16 rows: fewer
+# than 96 rows take runs of 1 to 5 (n = 9, 20, 40, 64: 1, 2, 3 and 4 tiles, the
+# last one ragged where n is not a multiple of 16), K with and without staged
+# scales (512: 16-byte scale rows; 544: not).
+@pytest.mark.parametrize("n,k", [(9, 512), (20, 544), (40, 512), (64, 544)])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_few_tiles_per_expert(fp4w, fmt, n, k):
+    offsets = np.array([0, 17, 17, 20], np.int32)
+    rng = np.random.default_rng(n)
+    row_index = rng.integers(0, 12, offsets[-1]).astype(np.int32)
+    x = W.normal_bf16(5, W.TID_X, (12, k), 1.0)
+    codes, scales, ts = _experts(fmt, 5, 3, n, k)
+    _case(fp4w, fmt, x, row_index, offsets, codes, scales, ts, f"{n} rows per expert")
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_long_k_uses_the_per_tile_kernel(fp4w, fmt):
     # K = 4160: 130 groups of 32, more than one span of the x-in-registers kernel holds
